@@ -1,0 +1,14 @@
+"""NSA selection-attention forward for AMD MI355X (gfx950).
+
+The compute path is the C-ABI library ``libnsa_sel.so`` built from
+``csrc/``; ``nsa_sel_fwd`` here marshals torch tensors into it.
+"""
+
+__all__ = ["nsa_sel_fwd", "nsa_sel_fwd_raw", "load_library"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,107 @@
+"""fp64 CPU oracle for NSA selection-attention forward.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by the
+bench's CPU-baseline leg, never by the GPU library or its binding.  It shares
+no code with the GPU path; both only consume arrays made by the seeded input
+generator.
+
+The arithmetic lives in ``nsa_oracle.c`` (plain C, fp64, exact two-pass
+softmax over the union of selected, causally visible keys); this module only
+loads it and marshals numpy arrays.  Its header lists the page sections it
+follows and the readings taken where the page is silent.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nsa_oracle.c")
+_LIB = os.path.join(_HERE, "libnsa_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (fp64, no fast-math, -O2)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-fno-fast-math",
+               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        lib.nsa_oracle_half_to_double.restype = ctypes.c_double
+        lib.nsa_oracle_half_to_double.argtypes = [ctypes.c_uint16]
+        p = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        lib.nsa_oracle_units.restype = ctypes.c_int
+        lib.nsa_oracle_units.argtypes = [p, p, p, p] + [i64] * 8 + [p, i64, p, p, p, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def half_to_double(bits: int) -> float:
+    return _load().nsa_oracle_half_to_double(bits)
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def _check_inputs(q, k, v, idx):
+    for name, a, dt in (("Q", q, np.float16), ("K", k, np.float16), ("V", v, np.float16),
+                        ("block_indices", idx, np.int32)):
+        if a.dtype != dt or not a.flags.c_contiguous or a.ndim != 4:
+            raise ValueError(f"{name} must be a C-contiguous 4-d {np.dtype(dt).name} array")
+    B, M, H, D = q.shape
+    Bk, N, G, Dk = k.shape
+    if v.shape != k.shape or Bk != B or Dk != D or idx.shape[:3] != (B, M, G) or H % G:
+        raise ValueError("inconsistent shapes")
+    return B, M, N, H, G, D, idx.shape[3]
+
+
+def oracle_units(q, k, v, idx, block_size: int, units: np.ndarray, threads: int = 0):
+    """O (fp64 [U, H/G, D]) and LSE (fp64 [U, H/G]) for units (b, m, g)."""
+    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx)
+    units = np.ascontiguousarray(units, dtype=np.int64).reshape(-1, 3)
+    U = units.shape[0]
+    gs = H // G
+    O = np.empty((U, gs, D), dtype=np.float64)
+    L = np.empty((U, gs), dtype=np.float64)
+    ndup = ctypes.c_int64(0)
+    rc = _load().nsa_oracle_units(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, M, N, H, G, D,
+                                  block_size, T, _ptr(units), U, _ptr(O), _ptr(L),
+                                  ctypes.byref(ndup), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    oracle_units.last_dup_units = ndup.value
+    return O, L
+
+
+oracle_units.last_dup_units = 0
+
+
+def all_units(B: int, M: int, G: int) -> np.ndarray:
+    b, m, g = np.meshgrid(np.arange(B), np.arange(M), np.arange(G), indexing="ij")
+    return np.stack([b.ravel(), m.ravel(), g.ravel()], axis=1).astype(np.int64)
+
+
+def oracle_full(q, k, v, idx, block_size: int, threads: int = 0):
+    """Whole-tensor oracle: O fp64 [B, M, H, D] and LSE fp64 [B, H, M]."""
+    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx)
+    O, L = oracle_units(q, k, v, idx, block_size, all_units(B, M, G), threads)
+    O = O.reshape(B, M, H, D)
+    L = L.reshape(B, M, H).transpose(0, 2, 1).copy()
+    return O, L

@@ -1,0 +1,210 @@
+/*
+ * CPU oracle for NSA selection-attention forward, in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or calls
+ * this file; only the tests, the smoke check and the bench's CPU-baseline leg
+ * do.  It shares no code, header or constant with the GPU library.
+ *
+ * What it computes is the plain definition of the operation described in the
+ * wave issue "[wave] NSA: selection attention forward kernel":
+ *   - section Operation: Q [B,M,H,D], K [B,N,G,D], V [B,N,G,D],
+ *     block_indices [B,M,G,T]  ->  O_slc [B,M,H,D], LSE_slc [B,H,M];
+ *   - section Algorithm: for a query m, each selected block t contributes the
+ *     tokens [t*bs, (t+1)*bs); scores are q.k, causally masked, and one
+ *     softmax runs over all selected blocks (section Requirements: "online
+ *     softmax across all T blocks" is, in exact arithmetic, the softmax over
+ *     the union of the selected keys);
+ *   - section Requirements: heads of one GQA group share the group's index row;
+ *     causal masking inside the gathered blocks; LSE is returned.
+ *
+ * Readings taken where the page is silent (each is listed with its reason in
+ * the design notes of the repository):
+ *   - head h belongs to group g = h / (H/G) (contiguous groups);
+ *   - key n is visible to query m iff n <= m, and n < N;
+ *   - an index entry t counts iff t >= 0 and t*bs < N; negative entries are
+ *     padding; repeated entries select the same block once (set union);
+ *   - softmax scale is 1/sqrt(D); LSE is the natural log of the sum of
+ *     exp(score) over the visible selected keys;
+ *   - a query with no visible selected key gets O = 0 and LSE = -inf.
+ *
+ * Arithmetic: fp16 inputs are decoded exactly into fp64 (IEEE 754 binary16:
+ * 1 sign bit, 5 exponent bits with bias 15, 10 fraction bits); all sums and
+ * the two-pass softmax run in fp64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* Exact decode of an IEEE 754 binary16 bit pattern. */
+double nsa_oracle_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);                 /* subnormal: f * 2^-14 / 2^10 */
+    } else if (e == 31) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);     /* (1 + f/2^10) * 2^(e-15) */
+    }
+    return sign ? -v : v;
+}
+
+typedef struct {
+    const uint16_t *Q, *K, *V;
+    const int32_t *idx;
+    int64_t B, M, N, H, G, D, bs, T;
+    const int64_t *units;
+    int64_t n_units;
+    double *O, *LSE;
+    int thread_id, n_threads;
+    int64_t dup_units;   /* units whose valid entries repeat a block */
+    int error;
+} job_t;
+
+static void one_unit(job_t *j, int64_t u, unsigned char *mark, int64_t *keys,
+                     double *score) {
+    const int64_t b = j->units[3 * u], m = j->units[3 * u + 1], g = j->units[3 * u + 2];
+    const int64_t N = j->N, M = j->M, H = j->H, G = j->G, D = j->D, bs = j->bs, T = j->T;
+    const int64_t gs = H / G;
+    const int64_t NB = (N + bs - 1) / bs;
+    const double scale = 1.0 / sqrt((double)D);
+
+    /* Selected-block set (union over the row). */
+    memset(mark, 0, (size_t)NB);
+    const int32_t *row = j->idx + ((b * M + m) * G + g) * T;
+    int dup = 0;
+    for (int64_t i = 0; i < T; ++i) {
+        int64_t t = row[i];
+        if (t < 0 || t >= NB) continue;
+        if (mark[t]) dup = 1;
+        mark[t] = 1;
+    }
+    if (dup) j->dup_units++;
+
+    /* Visible selected keys, ascending. */
+    int64_t nk = 0;
+    for (int64_t t = 0; t < NB; ++t) {
+        if (!mark[t]) continue;
+        for (int64_t n = t * bs; n < (t + 1) * bs && n < N; ++n)
+            if (n <= m) keys[nk++] = n;
+    }
+
+    for (int64_t i = 0; i < gs; ++i) {
+        const int64_t h = g * gs + i;
+        const uint16_t *q = j->Q + ((b * M + m) * H + h) * D;
+        double *o = j->O + (u * gs + i) * D;
+        if (nk == 0) {
+            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+            j->LSE[u * gs + i] = -INFINITY;
+            continue;
+        }
+        /* Pass 1: scores and their maximum. */
+        double mu = -INFINITY;
+        for (int64_t s = 0; s < nk; ++s) {
+            const uint16_t *k = j->K + ((b * N + keys[s]) * G + g) * D;
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d)
+                acc += nsa_oracle_half_to_double(q[d]) * nsa_oracle_half_to_double(k[d]);
+            score[s] = scale * acc;
+            if (score[s] > mu) mu = score[s];
+        }
+        /* Pass 2: normaliser and weighted sum of values. */
+        double z = 0.0;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        for (int64_t s = 0; s < nk; ++s) {
+            const double w = exp(score[s] - mu);
+            const uint16_t *v = j->V + ((b * N + keys[s]) * G + g) * D;
+            z += w;
+            for (int64_t d = 0; d < D; ++d) o[d] += w * nsa_oracle_half_to_double(v[d]);
+        }
+        for (int64_t d = 0; d < D; ++d) o[d] /= z;
+        j->LSE[u * gs + i] = mu + log(z);
+    }
+}
+
+static void *worker(void *arg) {
+    job_t *j = (job_t *)arg;
+    const int64_t NB = (j->N + j->bs - 1) / j->bs;
+    unsigned char *mark = (unsigned char *)malloc((size_t)NB);
+    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)j->N);
+    double *score = (double *)malloc(sizeof(double) * (size_t)j->N);
+    if (!mark || !keys || !score) {
+        j->error = 1;
+    } else {
+        for (int64_t u = j->thread_id; u < j->n_units; u += j->n_threads)
+            one_unit(j, u, mark, keys, score);
+    }
+    free(mark);
+    free(keys);
+    free(score);
+    return NULL;
+}
+
+/*
+ * Oracle over a list of units.
+ *   units  : int64 [n_units, 3] rows (b, m, g); each must be in range.
+ *   O      : fp64 [n_units, H/G, D]   (output; heads g*gs .. g*gs+gs-1)
+ *   LSE    : fp64 [n_units, H/G]      (output)
+ *   n_dup  : optional; receives the number of units whose row repeats a
+ *            valid block (outside the operation's contract; union is used).
+ *   n_threads <= 0 uses every online host core.
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int nsa_oracle_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                     const int32_t *block_indices, int64_t B, int64_t M, int64_t N,
+                     int64_t H, int64_t G, int64_t D, int64_t block_size, int64_t T,
+                     const int64_t *units, int64_t n_units, double *O, double *LSE,
+                     int64_t *n_dup, int n_threads) {
+    if (!Q || !K || !V || !block_indices || !units || !O || !LSE) return -1;
+    if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1 || block_size < 1 || T < 1) return -1;
+    if (H % G) return -1;
+    for (int64_t u = 0; u < n_units; ++u) {
+        if (units[3 * u] < 0 || units[3 * u] >= B || units[3 * u + 1] < 0 ||
+            units[3 * u + 1] >= M || units[3 * u + 2] < 0 || units[3 * u + 2] >= G)
+            return -1;
+    }
+    if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (n_threads < 1) n_threads = 1;
+    if (n_units < n_threads) n_threads = n_units > 0 ? (int)n_units : 1;
+
+    job_t *jobs = (job_t *)calloc((size_t)n_threads, sizeof(job_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    int rc = 0;
+    for (int i = 0; i < n_threads; ++i) {
+        job_t *j = &jobs[i];
+        j->Q = Q; j->K = K; j->V = V; j->idx = block_indices;
+        j->B = B; j->M = M; j->N = N; j->H = H; j->G = G; j->D = D;
+        j->bs = block_size; j->T = T;
+        j->units = units; j->n_units = n_units; j->O = O; j->LSE = LSE;
+        j->thread_id = i; j->n_threads = n_threads;
+    }
+    int started = 0;
+    for (int i = 0; i < n_threads; ++i) {
+        if (pthread_create(&th[i], NULL, worker, &jobs[i]) != 0) {
+            rc = -1;
+            break;
+        }
+        started++;
+    }
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    int64_t dups = 0;
+    for (int i = 0; i < started; ++i) {
+        if (jobs[i].error) rc = -1;
+        dups += jobs[i].dup_units;
+    }
+    if (started < n_threads) rc = -1;
+    if (n_dup) *n_dup = dups;
+    free(jobs);
+    free(th);
+    return rc;
+}
