@@ -1,0 +1,218 @@
+"""Benchmark of the NSA selection-attention forward (nsa_sel_fwd) on one MI355X.
+
+One step is one nsa_sel_fwd launch over the whole workload (all (b, m, g)
+units of the config) with inputs already resident in HBM.  Prints ONE JSON
+line: effective TFLOP/s as ``value``, plus ms per step, gathered-KV GB/s, the
+roofline of the kernel (HBM-bound on gathered bytes), the same kernel with
+every causal block selected (dense mode) and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+
+Work counts per launch (exact, from the index rows):
+  gathered bytes  = sum over units of (counted blocks) * bs * D * 2 B * 2 (K and V)
+  effective flops = sum over units of 4 * D * (H/G) * (visible selected keys)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from block_sparse_attention_sel_amd.inputs import CONFIGS, Config, block_indices, make_inputs  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+FP16_PEAK_TFLOPS = 2500.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "nsa_sel_fwd_64k_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_sel_amd", "csrc", "nsa_sel.hip")
+
+
+def work_counts(cfg: Config, idx: np.ndarray):
+    """(counted blocks, visible keys) summed over all units of one launch."""
+    bs = cfg.block_size
+    if cfg.rule == "dense":
+        m = np.arange(cfg.M, dtype=np.int64)
+        blocks = (np.minimum(m // bs, cfg.NB - 1) + 1).sum() * cfg.B * cfg.G
+        keys = np.minimum(m + 1, cfg.N).sum() * cfg.B * cfg.G
+        return int(blocks), int(keys)
+    blocks = 0
+    keys = 0
+    step = max(1, (1 << 22) // (cfg.G * cfg.T))
+    for b in range(cfg.B):
+        for lo in range(0, cfg.M, step):
+            hi = min(cfg.M, lo + step)
+            t = idx[b, lo:hi].astype(np.int64)                          # [m, G, T]
+            m = np.arange(lo, hi, dtype=np.int64)[:, None, None]
+            c = m // bs
+            ok = (t >= 0) & (t <= c) & (t < cfg.NB)
+            vis = np.minimum(np.minimum((t + 1) * bs, cfg.N), m + 1) - t * bs
+            blocks += int(ok.sum())
+            keys += int(np.where(ok, np.maximum(vis, 0), 0).sum())
+    return blocks, keys
+
+
+def _kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def _traffic():
+    """HBM bytes per launch from committed rocprofv3 counters, if they were
+    taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha256") != _kernel_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_launches(torch, fn, steps: int, warmup: int):
+    """Runs fn() warmup times, then times `steps` calls with HIP events on the
+    launch stream and with wall clock around the whole loop."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall_ms, float(np.mean(ev)), float(np.min(ev))
+
+
+def cpu_baseline(cfg: Config, q, k, v, idx, target_s: float = 15.0):
+    """The fp64 CPU oracle on random units of the same workload."""
+    import oracle
+    threads = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    rng = np.random.default_rng(2024)
+
+    def pick(n):
+        return np.stack([rng.integers(0, cfg.B, n), rng.integers(0, cfg.M, n),
+                         rng.integers(0, cfg.G, n)], axis=1).astype(np.int64)
+
+    def unit_flops(units):
+        bs = cfg.block_size
+        t = idx[units[:, 0], units[:, 1], units[:, 2]].astype(np.int64)    # [U, T]
+        m = units[:, 1:2]
+        ok = (t >= 0) & (t <= m // bs) & (t < cfg.NB)
+        vis = np.minimum(np.minimum((t + 1) * bs, cfg.N), m + 1) - t * bs
+        return 4.0 * cfg.D * cfg.gs * float(np.where(ok, np.maximum(vis, 0), 0).sum())
+
+    probe = pick(max(threads * 4, 64))
+    t0 = time.perf_counter()
+    oracle.oracle_units(q, k, v, idx, cfg.block_size, probe, threads)
+    dt = time.perf_counter() - t0
+    n = int(min(200000, max(probe.shape[0], probe.shape[0] * target_s / max(dt, 1e-3))))
+    units = pick(n)
+    t0 = time.perf_counter()
+    oracle.oracle_units(q, k, v, idx, cfg.block_size, units, threads)
+    dt = time.perf_counter() - t0
+    return {"value": unit_flops(units) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} random (b,m,g) units of the {cfg.name} workload, fp64, {dt:.1f} s",
+            "ms_per_unit": dt * 1e3 / n}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="64k", choices=sorted(CONFIGS))
+    ap.add_argument("--no-dense", action="store_true", help="skip the all-causal-blocks run")
+    ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_sel_amd.binding import nsa_sel_fwd
+
+    cfg = CONFIGS[args.config]
+    print(f"[bench] generating {cfg}", file=sys.stderr, flush=True)
+    q, k, v, idx = make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    tq, tk, tv, ti = (torch.from_numpy(a).to(dev) for a in (q, k, v, idx))
+    O = torch.empty((cfg.B, cfg.M, cfg.H, cfg.D), dtype=torch.float16, device=dev)
+    L = torch.empty((cfg.B, cfg.H, cfg.M), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def launch(ti_=ti, T=cfg.T):
+        nsa_sel_fwd(tq, tk, tv, ti_, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, T,
+                    stream.cuda_stream)
+
+    blocks, keys = work_counts(cfg, idx)
+    gathered = blocks * cfg.block_size * cfg.D * 2 * 2
+    flops = 4.0 * cfg.D * cfg.gs * keys
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
+    wall_ms, ev_ms, ev_min = time_launches(torch, launch, args.steps, args.warmup)
+    assert torch.isfinite(L).all().item(), "non-finite LSE"
+
+    gbps = gathered / (ev_ms * 1e-3) / 1e9
+    tflops = flops / (wall_ms * 1e-3) / 1e12
+    out = {
+        "metric": "NSA sel-attn fwd ms + eff. TFLOP/s & gathered GB/s, M=64k T=16 bs=64",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": f"nsa_sel_fwd {cfg.name}", "B": cfg.B, "M": cfg.M, "N": cfg.N, "H": cfg.H,
+                   "G": cfg.G, "D": cfg.D, "block_size": cfg.block_size, "T": cfg.T,
+                   "index_rule": cfg.rule, "seed": cfg.seed},
+        "kernel_ms": round(ev_ms, 4),
+        "kernel_ms_min": round(ev_min, 4),
+        "gathered_GBps": round(gbps, 1),
+        "eff_TFLOPs": round(flops / (ev_ms * 1e-3) / 1e12, 3),
+        "work": {"counted_blocks": blocks, "visible_keys": keys, "gathered_bytes": gathered,
+                 "effective_flops": flops},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": _traffic()},
+    }
+
+    if not args.no_dense:
+        dcfg = cfg.dense()
+        print(f"[bench] dense mode T={dcfg.T}", file=sys.stderr, flush=True)
+        didx = block_indices(dcfg)
+        tdi = torch.from_numpy(didx).to(dev)
+        del didx
+        d_wall, d_ev, _ = time_launches(torch, lambda: launch(tdi, dcfg.T), args.dense_steps, 1)
+        dblocks, dkeys = work_counts(dcfg, None)
+        out["dense_mode"] = {"T": dcfg.T, "kernel_ms": round(d_ev, 3),
+                             "eff_TFLOPs": round(4.0 * cfg.D * cfg.gs * dkeys / (d_ev * 1e-3) / 1e12, 3),
+                             "gathered_GBps": round(dblocks * cfg.block_size * cfg.D * 4 / (d_ev * 1e-3) / 1e9, 1),
+                             "ratio_dense_over_selected": round(d_ev / ev_ms, 2)}
+        del tdi
+
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, q, k, v, idx, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -4,7 +4,7 @@ The compute path is the C-ABI library ``libnsa_sel.so`` built from
 ``csrc/``; ``nsa_sel_fwd`` here marshals torch tensors into it.
 """
 
-__all__ = ["nsa_sel_fwd", "nsa_sel_fwd_raw", "load_library"]
+__all__ = ["nsa_sel_fwd", "nsa_sel_fwd_raw", "nsa_sel_status_string", "sel_attn_fwd", "load_library", "NsaSelError"]
 
 
 def __getattr__(name):

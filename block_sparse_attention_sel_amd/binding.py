@@ -1,0 +1,106 @@
+"""Thin ctypes binding of libnsa_sel.so.
+
+``nsa_sel_fwd`` and ``nsa_sel_status_string`` mirror the C entry points one to
+one (pointers may be given as ints or as torch tensors); ``sel_attn_fwd`` is a
+convenience that checks torch tensors, allocates the outputs and calls
+``nsa_sel_fwd`` on the current stream.  All arithmetic happens in the HIP
+kernels; when the library is missing every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnsa_sel.so")
+
+# Status codes (mirror include/nsa_sel.h).
+NSA_SEL_OK = 0
+NSA_SEL_ERR_NULL = 1
+NSA_SEL_ERR_SHAPE = 2
+NSA_SEL_ERR_UNSUPPORTED = 3
+NSA_SEL_ERR_ALIGN = 4
+NSA_SEL_ERR_RANGE = 5
+NSA_SEL_ERR_ALIAS = 6
+NSA_SEL_ERR_HIP = 7
+
+EXPORTED = ("nsa_sel_fwd", "nsa_sel_status_string")
+
+_lib = None
+
+
+class NsaSelError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(nsa_sel_status_string(status))
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.nsa_sel_fwd.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp]
+    lib.nsa_sel_fwd.restype = ci
+    lib.nsa_sel_status_string.argtypes = [ci]
+    lib.nsa_sel_status_string.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def nsa_sel_status_string(status: int) -> str:
+    return load_library().nsa_sel_status_string(int(status)).decode()
+
+
+def nsa_sel_fwd_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> int:
+    """Calls the C entry point and returns its status code unchanged."""
+    lib = load_library()
+    return lib.nsa_sel_fwd(_addr(Q), _addr(K), _addr(V), _addr(block_indices), _addr(O), _addr(LSE),
+                           int(B), int(M), int(N), int(H), int(G), int(D), int(block_size), int(T),
+                           ctypes.c_void_p(_addr(stream)))
+
+
+def nsa_sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> None:
+    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
+    rc = nsa_sel_fwd_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, stream=None):
+    """q [B,M,H,D] fp16, k/v [B,N,G,D] fp16, block_indices [B,M,G,T] int32, all
+    contiguous CUDA tensors.  Returns (O [B,M,H,D] fp16, LSE [B,H,M] fp32)."""
+    import torch
+
+    for name, t, dt in (("q", q, torch.float16), ("k", k, torch.float16), ("v", v, torch.float16),
+                        ("block_indices", block_indices, torch.int32)):
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-d {dt} tensor")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, M, H, D = q.shape
+    _, N, G, _ = k.shape
+    T = block_indices.shape[3]
+    if (k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape or tuple(block_indices.shape[:3]) != (B, M, G):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, M, H, D), dtype=torch.float16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    nsa_sel_fwd(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
+    return out, lse

@@ -231,13 +231,13 @@ def make_inputs(cfg: Config, threads: int | None = None):
     return q, k, v, idx
 
 
-def sample_units(cfg: Config, count: int, seed: int = 12345) -> np.ndarray:
-    """int64 [U, 3] (b, m, g) units: the first and last two query blocks of every
-    (b, g), plus ``count`` seeded random units, without repeats."""
+def sample_units(cfg: Config, count: int, seed: int = 12345, tail: int = 2) -> np.ndarray:
+    """int64 [U, 3] (b, m, g) units: the first two and the last ``tail`` query
+    blocks of every (b, g), plus ``count`` seeded random units, without repeats."""
     bs = cfg.block_size
     edge_m = np.unique(np.concatenate([
         np.arange(0, min(cfg.M, 2 * bs)),
-        np.arange(max(0, cfg.M - 2 * bs), cfg.M)]))
+        np.arange(max(0, cfg.M - tail * bs), cfg.M)]))
     b, m, g = np.meshgrid(np.arange(cfg.B), edge_m, np.arange(cfg.G), indexing="ij")
     edge = np.stack([b.ravel(), m.ravel(), g.ravel()], axis=1)
     rng = _rng(seed, 99)

@@ -1,0 +1,82 @@
+/*
+ * nsa_sel.h -- C ABI of the NSA selection-attention forward library for
+ * AMD MI355X (gfx950).
+ *
+ * Operation (wave issue "[wave] NSA: selection attention forward kernel",
+ * sections Operation, Algorithm and Requirements): for every batch b, query
+ * position m and KV group g, the T entries of block_indices[b, m, g, :] name
+ * key blocks t; each selected block contributes the keys
+ * n in [t*block_size, (t+1)*block_size).  The heads of group g (the H/G query
+ * heads g*H/G .. (g+1)*H/G - 1, which share the group's index row) attend to
+ * those keys with the causal mask n <= m, through one softmax across all
+ * selected blocks, scaled by 1/sqrt(D).  The output is the attention result
+ * O_slc and, per head and query, the natural-log log-sum-exp of the scaled
+ * scores LSE_slc (kept for a backward pass).  Matrix products take fp16
+ * operands and accumulate in fp32.
+ *
+ * Index entries: an entry t counts when 0 <= t <= m / block_size and
+ * t * block_size < N.  Any other value (negative padding such as -1, a block
+ * after the query's own block, a block past the end) contributes nothing.
+ * Counted entries of one row must be distinct: a repeated block would be
+ * weighted twice (outside the contract).  A query with no counted entry gets
+ * O = 0 and LSE = -inf.
+ */
+#ifndef NSA_SEL_H
+#define NSA_SEL_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by nsa_sel_fwd. */
+enum {
+    NSA_SEL_OK = 0,
+    NSA_SEL_ERR_NULL = 1,        /* a pointer argument is NULL                      */
+    NSA_SEL_ERR_SHAPE = 2,       /* a size < 1, or H not a multiple of G            */
+    NSA_SEL_ERR_UNSUPPORTED = 3, /* D not 64/128, block_size not 32/64, H/G > 16    */
+    NSA_SEL_ERR_ALIGN = 4,       /* Q/K/V/O not 16-byte aligned, idx/LSE not 4-byte */
+    NSA_SEL_ERR_RANGE = 5,       /* B*M*G units or a tensor size beyond the limits  */
+    NSA_SEL_ERR_ALIAS = 6,       /* an output buffer overlaps an input or the other */
+    NSA_SEL_ERR_HIP = 7          /* the HIP runtime reported an error at launch     */
+};
+
+/*
+ * nsa_sel_fwd -- selection-attention forward pass.
+ *
+ * Arguments (all tensors are device pointers to contiguous row-major memory
+ * owned by the caller; the library allocates nothing and keeps no pointer
+ * after the call returns):
+ *   Q             fp16 [B, M, H, D]   queries
+ *   K, V          fp16 [B, N, G, D]   keys and values, one head per group
+ *   block_indices int32 [B, M, G, T]  selected block ids per (b, m, g)
+ *   O             fp16 [B, M, H, D]   output, fully overwritten
+ *   LSE           fp32 [B, H, M]      output, fully overwritten (head-major)
+ *   B, M, N, H, G batch, queries, keys, query heads, KV groups
+ *   D             head dim: 64 or 128
+ *   block_size    32 or 64
+ *   T             entries per index row (>= 1)
+ *   stream        HIP stream the kernel is queued on (0 = default stream)
+ *
+ * Behaviour: every argument is checked on the host before any HIP call; a
+ * failed check returns its NSA_SEL_ERR_* code and touches nothing.  On success
+ * the work is queued asynchronously on `stream` and NSA_SEL_OK is returned;
+ * the call never synchronises.  Faults inside the kernel surface at the
+ * caller's next synchronisation, as for any HIP launch.  Inputs are only
+ * read; outputs must not overlap inputs or each other.  Calls on different
+ * streams may run concurrently; the call keeps no mutable global state.
+ */
+int nsa_sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                int block_size, int T, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *nsa_sel_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_SEL_H */

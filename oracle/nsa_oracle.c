@@ -54,6 +54,13 @@ double nsa_oracle_half_to_double(uint16_t h) {
     return sign ? -v : v;
 }
 
+/* All 2^16 decoded values, filled once from nsa_oracle_half_to_double. */
+static double g_half[65536];
+static pthread_once_t g_half_once = PTHREAD_ONCE_INIT;
+static void fill_half_table(void) {
+    for (int i = 0; i < 65536; ++i) g_half[i] = nsa_oracle_half_to_double((uint16_t)i);
+}
+
 typedef struct {
     const uint16_t *Q, *K, *V;
     const int32_t *idx;
@@ -66,8 +73,15 @@ typedef struct {
     int error;
 } job_t;
 
-static void one_unit(job_t *j, int64_t u, unsigned char *mark, int64_t *keys,
-                     double *score) {
+typedef struct {
+    unsigned char *mark;  /* [NB] selected-block flags            */
+    int64_t *keys;        /* [N] visible selected keys, ascending */
+    double *score;        /* [gs * N] scores, head-major          */
+    double *qd, *kd;      /* [gs * D], [D] decoded rows           */
+    double *mu, *z;       /* [gs] per-head max and normaliser     */
+} scratch_t;
+
+static void one_unit(job_t *j, int64_t u, scratch_t *w) {
     const int64_t b = j->units[3 * u], m = j->units[3 * u + 1], g = j->units[3 * u + 2];
     const int64_t N = j->N, M = j->M, H = j->H, G = j->G, D = j->D, bs = j->bs, T = j->T;
     const int64_t gs = H / G;
@@ -75,73 +89,96 @@ static void one_unit(job_t *j, int64_t u, unsigned char *mark, int64_t *keys,
     const double scale = 1.0 / sqrt((double)D);
 
     /* Selected-block set (union over the row). */
-    memset(mark, 0, (size_t)NB);
+    memset(w->mark, 0, (size_t)NB);
     const int32_t *row = j->idx + ((b * M + m) * G + g) * T;
     int dup = 0;
     for (int64_t i = 0; i < T; ++i) {
         int64_t t = row[i];
         if (t < 0 || t >= NB) continue;
-        if (mark[t]) dup = 1;
-        mark[t] = 1;
+        if (w->mark[t]) dup = 1;
+        w->mark[t] = 1;
     }
     if (dup) j->dup_units++;
 
     /* Visible selected keys, ascending. */
     int64_t nk = 0;
     for (int64_t t = 0; t < NB; ++t) {
-        if (!mark[t]) continue;
+        if (!w->mark[t]) continue;
         for (int64_t n = t * bs; n < (t + 1) * bs && n < N; ++n)
-            if (n <= m) keys[nk++] = n;
+            if (n <= m) w->keys[nk++] = n;
     }
 
+    /* Head h = g*gs + i of query m, decoded. */
     for (int64_t i = 0; i < gs; ++i) {
-        const int64_t h = g * gs + i;
-        const uint16_t *q = j->Q + ((b * M + m) * H + h) * D;
+        const uint16_t *q = j->Q + ((b * M + m) * H + g * gs + i) * D;
+        for (int64_t d = 0; d < D; ++d) w->qd[i * D + d] = g_half[q[d]];
+    }
+
+    /* Pass 1: scores s = scale * q.k for every head and key, and their maxima. */
+    for (int64_t i = 0; i < gs; ++i) w->mu[i] = -INFINITY;
+    for (int64_t s = 0; s < nk; ++s) {
+        const uint16_t *k = j->K + ((b * N + w->keys[s]) * G + g) * D;
+        for (int64_t d = 0; d < D; ++d) w->kd[d] = g_half[k[d]];
+        for (int64_t i = 0; i < gs; ++i) {
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += w->qd[i * D + d] * w->kd[d];
+            const double sc = scale * acc;
+            w->score[i * N + s] = sc;
+            if (sc > w->mu[i]) w->mu[i] = sc;
+        }
+    }
+
+    /* Pass 2: normaliser z = sum exp(s - mu) and O = sum exp(s - mu) v / z. */
+    for (int64_t i = 0; i < gs; ++i) {
+        w->z[i] = 0.0;
         double *o = j->O + (u * gs + i) * D;
-        if (nk == 0) {
-            for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+    }
+    for (int64_t s = 0; s < nk; ++s) {
+        const uint16_t *v = j->V + ((b * N + w->keys[s]) * G + g) * D;
+        for (int64_t d = 0; d < D; ++d) w->kd[d] = g_half[v[d]];
+        for (int64_t i = 0; i < gs; ++i) {
+            const double e = exp(w->score[i * N + s] - w->mu[i]);
+            double *o = j->O + (u * gs + i) * D;
+            w->z[i] += e;
+            for (int64_t d = 0; d < D; ++d) o[d] += e * w->kd[d];
+        }
+    }
+    for (int64_t i = 0; i < gs; ++i) {
+        double *o = j->O + (u * gs + i) * D;
+        if (nk == 0) {                      /* nothing visible: O = 0, LSE = -inf */
             j->LSE[u * gs + i] = -INFINITY;
             continue;
         }
-        /* Pass 1: scores and their maximum. */
-        double mu = -INFINITY;
-        for (int64_t s = 0; s < nk; ++s) {
-            const uint16_t *k = j->K + ((b * N + keys[s]) * G + g) * D;
-            double acc = 0.0;
-            for (int64_t d = 0; d < D; ++d)
-                acc += nsa_oracle_half_to_double(q[d]) * nsa_oracle_half_to_double(k[d]);
-            score[s] = scale * acc;
-            if (score[s] > mu) mu = score[s];
-        }
-        /* Pass 2: normaliser and weighted sum of values. */
-        double z = 0.0;
-        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-        for (int64_t s = 0; s < nk; ++s) {
-            const double w = exp(score[s] - mu);
-            const uint16_t *v = j->V + ((b * N + keys[s]) * G + g) * D;
-            z += w;
-            for (int64_t d = 0; d < D; ++d) o[d] += w * nsa_oracle_half_to_double(v[d]);
-        }
-        for (int64_t d = 0; d < D; ++d) o[d] /= z;
-        j->LSE[u * gs + i] = mu + log(z);
+        for (int64_t d = 0; d < D; ++d) o[d] /= w->z[i];
+        j->LSE[u * gs + i] = w->mu[i] + log(w->z[i]);
     }
 }
 
 static void *worker(void *arg) {
     job_t *j = (job_t *)arg;
     const int64_t NB = (j->N + j->bs - 1) / j->bs;
-    unsigned char *mark = (unsigned char *)malloc((size_t)NB);
-    int64_t *keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)j->N);
-    double *score = (double *)malloc(sizeof(double) * (size_t)j->N);
-    if (!mark || !keys || !score) {
+    const int64_t gs = j->H / j->G;
+    scratch_t w;
+    w.mark = (unsigned char *)malloc((size_t)NB);
+    w.keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)j->N);
+    w.score = (double *)malloc(sizeof(double) * (size_t)(gs * j->N));
+    w.qd = (double *)malloc(sizeof(double) * (size_t)(gs * j->D));
+    w.kd = (double *)malloc(sizeof(double) * (size_t)j->D);
+    w.mu = (double *)malloc(sizeof(double) * (size_t)gs);
+    w.z = (double *)malloc(sizeof(double) * (size_t)gs);
+    if (!w.mark || !w.keys || !w.score || !w.qd || !w.kd || !w.mu || !w.z) {
         j->error = 1;
     } else {
-        for (int64_t u = j->thread_id; u < j->n_units; u += j->n_threads)
-            one_unit(j, u, mark, keys, score);
+        for (int64_t u = j->thread_id; u < j->n_units; u += j->n_threads) one_unit(j, u, &w);
     }
-    free(mark);
-    free(keys);
-    free(score);
+    free(w.mark);
+    free(w.keys);
+    free(w.score);
+    free(w.qd);
+    free(w.kd);
+    free(w.mu);
+    free(w.z);
     return NULL;
 }
 
@@ -168,6 +205,7 @@ int nsa_oracle_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
             units[3 * u + 1] >= M || units[3 * u + 2] < 0 || units[3 * u + 2] >= G)
             return -1;
     }
+    pthread_once(&g_half_once, fill_half_table);
     if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
     if (n_threads < 1) n_threads = 1;
     if (n_units < n_threads) n_threads = n_units > 0 ? (int)n_units : 1;

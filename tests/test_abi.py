@@ -1,0 +1,118 @@
+"""The C-ABI library without a GPU: it loads, exports what the header declares,
+and rejects bad arguments on the host before any HIP call."""
+
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_attention_sel_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nsa_sel.h")
+
+GOOD = dict(B=1, M=256, N=256, H=8, G=1, D=128, block_size=64, T=4)
+# Distinct, 16-byte aligned fake addresses far apart: validation never
+# dereferences them and returns before any HIP call.
+ADDR = {name: (i + 1) << 36 for i, name in enumerate(["Q", "K", "V", "I", "O", "L"])}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libnsa_sel.so not built")
+    return binding.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_sel_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported
+        assert getattr(lib, name) is not None
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name, val in re.findall(r"(NSA_SEL_\w+)\s*=\s*(\d+)", text):
+        assert getattr(binding, name) == int(val)
+
+
+def test_status_strings(lib):
+    for code in range(0, 8):
+        s = binding.nsa_sel_status_string(code)
+        assert isinstance(s, str) and s
+    assert binding.nsa_sel_status_string(0) == "ok"
+    assert "unknown" in binding.nsa_sel_status_string(99)
+
+
+def _call(**over):
+    args = dict(GOOD)
+    ptrs = dict(ADDR)
+    for k in list(over):
+        if k in ptrs:
+            ptrs[k] = over.pop(k)
+    args.update(over)
+    return binding.nsa_sel_fwd_raw(ptrs["Q"], ptrs["K"], ptrs["V"], ptrs["I"], ptrs["O"], ptrs["L"],
+                                   args["B"], args["M"], args["N"], args["H"], args["G"], args["D"],
+                                   args["block_size"], args["T"], 0)
+
+
+@pytest.mark.parametrize("which", ["Q", "K", "V", "I", "O", "L"])
+def test_null_pointer(lib, which):
+    assert _call(**{which: 0}) == binding.NSA_SEL_ERR_NULL
+
+
+@pytest.mark.parametrize("over", [dict(B=0), dict(M=0), dict(N=-1), dict(H=0), dict(G=0), dict(D=0),
+                                  dict(block_size=0), dict(T=0), dict(H=8, G=3)])
+def test_bad_shape(lib, over):
+    assert _call(**over) == binding.NSA_SEL_ERR_SHAPE
+
+
+@pytest.mark.parametrize("over", [dict(D=96), dict(D=256), dict(block_size=16), dict(block_size=128),
+                                  dict(H=32, G=1)])
+def test_unsupported(lib, over):
+    assert _call(**over) == binding.NSA_SEL_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which,off", [("Q", 8), ("K", 2), ("V", 4), ("O", 8), ("I", 2), ("L", 1)])
+def test_misaligned(lib, which, off):
+    assert _call(**{which: ADDR[which] + off}) == binding.NSA_SEL_ERR_ALIGN
+
+
+def test_range(lib):
+    assert _call(B=1 << 12, M=1 << 20, G=1, H=1) == binding.NSA_SEL_ERR_RANGE
+
+
+def test_alias(lib):
+    assert _call(O=ADDR["Q"]) == binding.NSA_SEL_ERR_ALIAS
+    assert _call(L=ADDR["K"] + 64) == binding.NSA_SEL_ERR_ALIAS
+    assert _call(L=ADDR["O"] + 256) == binding.NSA_SEL_ERR_ALIAS
+
+
+def test_binding_raises_with_message(lib):
+    with pytest.raises(binding.NsaSelError) as ei:
+        binding.nsa_sel_fwd(0, 1, 2, 3, 4, 5, 1, 1, 1, 1, 1, 64, 32, 1, 0)
+    assert ei.value.status == binding.NSA_SEL_ERR_NULL
+    assert "NULL" in str(ei.value)
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "block_sparse_attention_sel_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"(import\s+oracle|from\s+oracle|nsa_oracle)", text), f

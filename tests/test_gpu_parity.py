@@ -1,0 +1,255 @@
+"""GPU path (C ABI -> HIP kernels) against the fp64 CPU oracle.
+
+Tolerances: O max-abs 5e-3, LSE max-abs 1e-3; rows with nothing visible must
+give O = 0 and LSE = -inf exactly; no NaN or Inf elsewhere.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_sel_amd.inputs import CONFIGS, Config, block_indices, make_inputs, sample_units
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 5e-3
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(torch, *arrs):
+    return [torch.from_numpy(np.ascontiguousarray(a)).to("cuda") for a in arrs]
+
+
+def _gpu_run(torch, q, k, v, idx, bs):
+    from block_sparse_attention_sel_amd.binding import sel_attn_fwd
+    tq, tk, tv, ti = _to_dev(torch, q, k, v, idx)
+    O, L = sel_attn_fwd(tq, tk, tv, ti, bs)
+    torch.cuda.synchronize()
+    return O, L
+
+
+def _check_full(O, L, Or, Lr):
+    O = O.astype(np.float64)
+    assert not np.isnan(O).any() and not np.isnan(L).any()
+    empty = ~np.isfinite(Lr)
+    assert np.array_equal(~np.isfinite(L), empty)
+    assert np.all(L[empty] == -np.inf)
+    errO = np.abs(O - Or).max()
+    errL = np.abs(L[~empty] - Lr[~empty]).max() if (~empty).any() else 0.0
+    _say(f"  max|dO| = {errO:.3e}  max|dLSE| = {errL:.3e}")
+    assert errO <= O_TOL
+    assert errL <= LSE_TOL
+
+
+def _parity_full(torch, cfg):
+    import oracle
+    _say(f"case {cfg}")
+    q, k, v, idx = make_inputs(cfg)
+    O, L = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    Or, Lr = oracle.oracle_full(q, k, v, idx, cfg.block_size)
+    _check_full(O.cpu().numpy(), L.cpu().numpy(), Or, Lr)
+
+
+REDUCED = {
+    "tiny": CONFIGS["tiny"],
+    "8k@2048": CONFIGS["8k"].with_(M=2048, N=2048),
+    "64k@4096": CONFIGS["64k"].with_(M=4096, N=4096),
+    "32k-bs32@2048": CONFIGS["32k-bs32"].with_(M=2048, N=2048),
+    "128k-local@4096": CONFIGS["128k-local"].with_(M=4096, N=4096),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_parity_full_coverage(torch_cuda, name):
+    _parity_full(torch_cuda, REDUCED[name])
+
+
+def _parity_sampled(torch, cfg, count, tail=2):
+    import oracle
+    _say(f"case {cfg} (sampled {count})")
+    q, k, v, idx = make_inputs(cfg)
+    O, L = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    units = sample_units(cfg, count, tail=tail)
+    Or, Lr = oracle.oracle_units(q, k, v, idx, cfg.block_size, units)
+    ub = torch.from_numpy(units).to("cuda")
+    gs = cfg.gs
+    heads = ub[:, 2:3] * gs + torch.arange(gs, device="cuda")[None, :]        # [U, gs]
+    Og = O[ub[:, 0:1], ub[:, 1:2], heads].float().cpu().numpy()              # [U, gs, D]
+    Lg = L[ub[:, 0:1], heads, ub[:, 1:2]].cpu().numpy()                      # [U, gs]
+    _check_full(Og, Lg, Or, Lr)
+    # Properties that hold at any size: finite everywhere, since every row of
+    # the index rules selects the query's own block.
+    assert torch.isfinite(L).all().item()
+    assert torch.isfinite(O).all().item()
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_parity_full_size_sampled(torch_cuda, name):
+    _parity_sampled(torch_cuda, CONFIGS[name], 2048)
+
+
+@pytest.mark.parametrize("name", ["8k", "64k"])
+def test_parity_dense_mode_sampled(torch_cuda, name):
+    # Trailing query blocks see the whole sequence; keep the oracle's share small.
+    _parity_sampled(torch_cuda, CONFIGS[name].dense(), 256, tail=2 if name == "8k" else 0)
+
+
+KERNEL_SHAPES = [
+    # B, M, N, H, G, D, bs, T
+    (1, 300, 300, 4, 4, 64, 32, 5),      # gs = 1, ragged tail
+    (2, 257, 257, 6, 2, 64, 64, 3),      # gs = 3
+    (1, 200, 333, 16, 1, 128, 32, 7),    # M < N, gs = 16
+    (1, 511, 511, 10, 5, 128, 64, 4),    # gs = 2
+    (2, 129, 129, 16, 2, 128, 64, 70),   # T > 64: several index chunks
+    (1, 96, 96, 12, 1, 64, 32, 2),       # gs = 12
+]
+
+
+def _random_rows(rng, B, M, G, T, bs, NB):
+    """Distinct counted entries mixed with padding, future and out-of-range ones."""
+    idx = np.full((B, M, G, T), -1, np.int32)
+    for b in range(B):
+        for m in range(M):
+            c = m // bs
+            for g in range(G):
+                cand = rng.permutation(np.arange(0, min(c, NB - 1) + 1))
+                take = list(cand[: max(1, T - 2)])
+                extra = [-1, NB + 5, c + 1 if c + 1 < NB else -3, -100]
+                row = (take + extra)[:T]
+                row = row + [-1] * (T - len(row))
+                rng.shuffle(row)                # counted entries land anywhere in the row
+                idx[b, m, g] = row
+    return idx
+
+
+@pytest.mark.parametrize("shape", KERNEL_SHAPES)
+def test_parity_every_instantiation(torch_cuda, shape):
+    import oracle
+    B, M, N, H, G, D, bs, T = shape
+    _say(f"case shape={shape}")
+    rng = np.random.default_rng(sum(shape))
+    q = rng.standard_normal((B, M, H, D)).astype(np.float16)
+    k = rng.standard_normal((B, N, G, D)).astype(np.float16)
+    v = rng.standard_normal((B, N, G, D)).astype(np.float16)
+    idx = _random_rows(rng, B, M, G, T, bs, -(-N // bs))
+    O, L = _gpu_run(torch_cuda, q, k, v, idx, bs)
+    Or, Lr = oracle.oracle_full(q, k, v, idx, bs)
+    _check_full(O.cpu().numpy(), L.cpu().numpy(), Or, Lr)
+
+
+def test_padding_and_invalid_entries_are_bitwise_invisible(torch_cuda):
+    torch = torch_cuda
+    cfg = CONFIGS["64k"].with_(M=2048, N=2048)
+    _say(f"case sentinel-invariance {cfg}")
+    q, k, v, idx = make_inputs(cfg)
+    B, M, G, T = idx.shape
+    NB = cfg.NB
+    rng = np.random.default_rng(1)
+    noisy = np.full((B, M, G, 2 * T), -1, np.int32)
+    for m in range(M):
+        c = m // cfg.block_size
+        for g in range(G):
+            row = [int(t) for t in idx[0, m, g] if t >= 0]
+            junk = [-1, -5, NB, NB + 100] + ([c + 1 + int(rng.integers(0, NB - c - 1))] if c + 1 < NB else [])
+            out = []
+            for t in row:                       # keep counted order, sprinkle junk in between
+                if rng.random() < 0.5:
+                    out.append(junk[int(rng.integers(0, len(junk)))])
+                out.append(t)
+            noisy[0, m, g, : len(out)] = out[: 2 * T]
+    O1, L1 = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    O2, L2 = _gpu_run(torch, q, k, v, noisy, cfg.block_size)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_repeat_runs_are_bitwise_identical(torch_cuda):
+    torch = torch_cuda
+    cfg = CONFIGS["32k-bs32"].with_(M=2048, N=2048)
+    _say(f"case determinism {cfg}")
+    q, k, v, idx = make_inputs(cfg)
+    O1, L1 = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    O2, L2 = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+
+
+def test_outputs_stay_inside_their_buffers(torch_cuda):
+    torch = torch_cuda
+    from block_sparse_attention_sel_amd.binding import nsa_sel_fwd
+    cfg = CONFIGS["8k"].with_(M=1024, N=1024)
+    _say(f"case guard-bands {cfg}")
+    q, k, v, idx = make_inputs(cfg)
+    tq, tk, tv, ti = _to_dev(torch, q, k, v, idx)
+    pad = 4096
+    o_buf = torch.full((q.size + 2 * pad,), 1234.0, dtype=torch.float16, device="cuda")
+    l_buf = torch.full((cfg.B * cfg.H * cfg.M + 2 * pad,), -777.0, dtype=torch.float32, device="cuda")
+    O = o_buf[pad:pad + q.size]
+    L = l_buf[pad:pad + cfg.B * cfg.H * cfg.M]
+    nsa_sel_fwd(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
+                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.all(o_buf[:pad] == 1234.0) and torch.all(o_buf[-pad:] == 1234.0)
+    assert torch.all(l_buf[:pad] == -777.0) and torch.all(l_buf[-pad:] == -777.0)
+    assert torch.all(L != -777.0)
+
+
+def test_rows_without_counted_entries(torch_cuda):
+    torch = torch_cuda
+    B, M, N, H, G, D, bs, T = 1, 130, 130, 8, 2, 128, 64, 3
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((B, M, H, D)).astype(np.float16)
+    k = rng.standard_normal((B, N, G, D)).astype(np.float16)
+    v = rng.standard_normal((B, N, G, D)).astype(np.float16)
+    idx = np.full((B, M, G, T), -1, np.int32)
+    idx[0, ::2, :, 0] = 0                               # even rows see block 0
+    idx[0, 1::4, :, 1] = 2                              # a future block only: still empty
+    O, L = _gpu_run(torch, q, k, v, idx, bs)
+    O, L = O.cpu().numpy(), L.cpu().numpy()
+    assert np.all(L[0][:, 1::2] == -np.inf)
+    assert not O[0, 1::2].any()
+    assert np.isfinite(L[0][:, ::2]).all()
+
+
+def test_single_visible_key_rows(torch_cuda):
+    """m = 0 sees only key 0: O equals V[0] exactly (p = 1, l = 1) and LSE is
+    the scaled score."""
+    torch = torch_cuda
+    cfg = CONFIGS["64k"].with_(M=512, N=512)
+    q, k, v, idx = make_inputs(cfg)
+    O, L = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    O, L = O.cpu().numpy(), L.cpu().numpy()
+    for h in range(cfg.H):
+        g = h // cfg.gs
+        assert np.array_equal(O[0, 0, h], v[0, 0, g])
+        s = math.fsum(float(a) * float(b) for a, b in zip(q[0, 0, h], k[0, 0, g])) / math.sqrt(cfg.D)
+        assert abs(L[0, h, 0] - s) <= LSE_TOL
+
+
+def test_non_default_stream(torch_cuda):
+    torch = torch_cuda
+    import oracle
+    from block_sparse_attention_sel_amd.binding import sel_attn_fwd
+    cfg = CONFIGS["tiny"].with_(M=512, N=512)
+    q, k, v, idx = make_inputs(cfg)
+    tq, tk, tv, ti = _to_dev(torch, q, k, v, idx)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        O, L = sel_attn_fwd(tq, tk, tv, ti, cfg.block_size)
+    s.synchronize()
+    Or, Lr = oracle.oracle_full(q, k, v, idx, cfg.block_size)
+    _check_full(O.cpu().numpy(), L.cpu().numpy(), Or, Lr)
