@@ -216,7 +216,8 @@ def test_rows_without_counted_entries(torch_cuda):
     v = rng.standard_normal((B, N, G, D)).astype(np.float16)
     idx = np.full((B, M, G, T), -1, np.int32)
     idx[0, ::2, :, 0] = 0                               # even rows see block 0
-    idx[0, 1::4, :, 1] = 2                              # a future block only: still empty
+    odd = np.arange(1, M, 2)
+    idx[0, odd, :, 1] = (odd // bs + 1)[:, None]        # a future (or past-the-end) block only
     O, L = _gpu_run(torch, q, k, v, idx, bs)
     O, L = O.cpu().numpy(), L.cpu().numpy()
     assert np.all(L[0][:, 1::2] == -np.inf)
