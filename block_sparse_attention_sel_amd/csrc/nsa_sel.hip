@@ -40,8 +40,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kThreads = kWaveSize * kWavesPerBlock;
+constexpr int kThreads = kWaveSize;  // one wavefront (one unit) per workgroup
 constexpr int kNumXcd = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -119,51 +118,115 @@ struct IndexScan {
     }
 };
 
+// LDS staging of one gathered block (K and V, BS rows of D fp16 each).
+//
+// The block is copied global -> LDS with 128-bit direct-to-LDS buffer loads
+// (buffer_load_dwordx4 ... lds).  One such instruction moves 1 KiB: lane l
+// writes bytes [16*l, 16*l + 16) of the instruction's LDS window, and the
+// global address of every lane is free.  Lanes are given consecutive 16-byte
+// pieces of the same key row (a row is D*2 bytes = LPR lanes), so each
+// instruction reads whole rows and coalesces into full cache lines.
+//
+// In LDS a row occupies D*2 contiguous bytes; its 16-byte pieces are stored
+// XOR-permuted, piece c at slot c ^ swz(row), so that the MFMA-layout reads
+// (16 lanes on 16 different rows, same piece) hit distinct banks.
+//
+// Addressing: the per-lane part of the byte offset repeats every 16/RPI
+// instructions (the swizzle depends on row % 16), so it lives in NV VGPRs;
+// the per-instruction row step and the block start are uniform (SGPR).
 template <int BS, int D>
-struct Tile {
-    static constexpr int KT = BS / 16;  // 16-key MFMA row tiles per block
-    static constexpr int DC = D / 32;   // 32-wide head-dim chunks
-    half8 k[KT][DC];
-    half8 v[KT][DC];
-};
+struct Stage {
+    static constexpr int LPR = D / 8;                // lanes (16-byte pieces) per row
+    static constexpr int RPI = kWaveSize / LPR;      // rows per 1 KiB instruction
+    static constexpr int NI = BS / RPI;              // instructions per K (or V) block
+    static constexpr int NV = 16 / RPI;              // distinct per-lane offsets
+    static constexpr int HALVES = BS * D;            // fp16 elements per K (or V) block
 
-// Gathers block t of one (b, g) head: lane l reads key row t*BS + 16*kt + l%16,
-// head-dim slice 32*c + 8*(l/16) .. +7 (16 bytes) of K and V.
-template <int BS, int D>
-__device__ __forceinline__ void load_block(Tile<BS, D> &tl, const _Float16 *Kg, const _Float16 *Vg,
-                                           int t, int N, int row_stride, int r, int q4) {
+    __device__ static __forceinline__ int swz(int row) { return (row & 15) * LPR / 16; }
+
+    __amdgpu_buffer_rsrc_t rk, rv;  // K and V of this (b, g), byte-addressed
+    unsigned lane_off[NV];          // lane part of the offset for instruction s % NV
+    unsigned row_bytes;             // bytes between consecutive keys (G * D * 2)
+    int N;
+
+    __device__ __forceinline__ void init(const _Float16 *Kg, const _Float16 *Vg, unsigned bytes,
+                                         int row_stride, int n_keys, int lane) {
+        rk = __builtin_amdgcn_make_buffer_rsrc((void *)Kg, (short)0, (int)bytes, 0x00020000);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void *)Vg, (short)0, (int)bytes, 0x00020000);
+        row_bytes = (unsigned)row_stride * 2u;
+        N = n_keys;
 #pragma unroll
-    for (int kt = 0; kt < Tile<BS, D>::KT; ++kt) {
-        int n = t * BS + kt * 16 + r;
-        n = n < N ? n : N - 1;  // rows past the end are masked; keep the address in bounds
-        const size_t off = (size_t)n * row_stride + q4 * 8;
-#pragma unroll
-        for (int c = 0; c < Tile<BS, D>::DC; ++c) {
-            tl.k[kt][c] = *(const half8 *)(Kg + off + c * 32);
-            tl.v[kt][c] = *(const half8 *)(Vg + off + c * 32);
+        for (int v = 0; v < NV; ++v) {
+            const int row = v * RPI + lane / LPR;
+            lane_off[v] = (unsigned)(lane / LPR) * row_bytes + (unsigned)(((lane % LPR) ^ swz(row)) * 16);
         }
     }
-}
 
-// Folds one gathered block into the running softmax state of the wave.
-// acc[c][hh] holds O^T rows d = 32*c + 8*(l/16) + 4*hh + i for head l%16.
+    __device__ static __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, _Float16 *lds, unsigned voff,
+                                                unsigned soff, int s) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)(lds + s * (kWaveSize * 8)), 16, voff, soff, 0, 0);
+    }
+
+    // Issues the copy of block t of K (or V) into buf; completes on vmcnt.
+    __device__ __forceinline__ void issue(bool is_v, _Float16 *buf, int t, int lane) const {
+        const __amdgpu_buffer_rsrc_t rs = is_v ? rv : rk;
+        if (t * BS + BS <= N) {
+            const unsigned base = (unsigned)(t * BS) * row_bytes;
+#pragma unroll
+            for (int s = 0; s < NI; ++s)
+                copy(rs, buf, lane_off[s % NV], base + (unsigned)(s * RPI) * row_bytes, s);
+        } else {
+            // Last, partial block: clamp rows past the end into bounds (they are
+            // masked out of the softmax), with the whole offset per lane.
+#pragma unroll
+            for (int s = 0; s < NI; ++s) {
+                const int row = s * RPI + lane / LPR;
+                int n = t * BS + row;
+                n = n < N ? n : N - 1;
+                const unsigned off = (unsigned)n * row_bytes + (unsigned)(((lane % LPR) ^ swz(row)) * 16);
+                copy(rs, buf, off, 0u, s);
+            }
+        }
+    }
+
+    // MFMA A-operand fragments of one staged block: lane l gets row
+    // 16*kt + l%16, head-dim 32*c + 8*(l/16) .. +7.
+    __device__ static __forceinline__ void read(half8 (&f)[BS / 16][D / 32], const _Float16 *buf, int r,
+                                                int q4) {
+#pragma unroll
+        for (int kt = 0; kt < BS / 16; ++kt) {
+            const int row = kt * 16 + r;
+#pragma unroll
+            for (int c = 0; c < D / 32; ++c)
+                f[kt][c] = *(const half8 *)(buf + row * D + ((c * 4 + q4) ^ swz(row)) * 8);
+        }
+    }
+};
+
+// s_waitcnt immediate for "at most n vector-memory ops outstanding"
+// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 0xC07F;  // all LDS reads done
+
+// Scores of one gathered block folded into the running softmax state:
+// S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, head l%16), scaled
+// into the log2 domain, causally masked, then the running max, the rescale
+// factor of the accumulator and the block's probabilities P^T (fp16).
 template <int BS, int D>
-__device__ __forceinline__ void process_block(const Tile<BS, D> &tl, const half8 (&qf)[D / 32],
-                                              half4 onehot, int key0, int m, int N, float scale_log2,
-                                              float &m_run, float &l_run,
-                                              float4v (&acc)[D / 32][2], int q4) {
-    constexpr int KT = Tile<BS, D>::KT;
-    constexpr int DC = Tile<BS, D>::DC;
-    // S^T = K * Q^T: lane l gets keys key0 + 16*kt + 4*(l/16) + i, head l%16.
+__device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
+                                            int key0, int m, int N, float scale_log2, float &m_run,
+                                            float &l_run, float &alpha, half4 (&pf)[BS / 16], int q4) {
+    constexpr int KT = BS / 16;
+    constexpr int DC = D / 32;
     float4v s[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         s[kt] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < DC; ++c) s[kt] = mfma_16x16x32(tl.k[kt][c], qf[c], s[kt]);
+        for (int c = 0; c < DC; ++c) s[kt] = mfma_16x16x32(kf[kt][c], qf[c], s[kt]);
     }
-    // Scale into the log2 domain and apply the causal mask where the block
-    // reaches past the query (only the query's own block) or past N.
+    // The mask only bites in the query's own block (keys past m) or past N.
     const bool need_mask = (key0 + BS - 1 > m) || (key0 + BS > N);
     float mloc = -INFINITY;
 #pragma unroll
@@ -184,29 +247,35 @@ __device__ __forceinline__ void process_block(const Tile<BS, D> &tl, const half8
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float m_new = fmaxf(m_run, mloc);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
-
-    half4 pf[KT];
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-        float4v p;
+        float4v pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            p[i] = fast_exp2(s[kt][i] - m_use);
-            psum += p[i];
+            pv[i] = fast_exp2(s[kt][i] - m_use);
+            psum += pv[i];
         }
-        pf[kt] = to_half4(p);
+        pf[kt] = to_half4(pv);
     }
     l_run = l_run * alpha + psum;  // per-lane partial; lanes are summed at the end
+}
+
+// O^T = alpha * O^T + V^T * P^T over 32-key chunks.  acc[c][hh] holds O^T rows
+// d = 32*c + 8*(l/16) + 4*hh + i for head l%16.  The B operand is P^T straight
+// from the score layout; the A operand V^T is made by the one-hot MFMA.
+template <int BS, int D>
+__device__ __forceinline__ void accumulate_block(const half8 (&vf)[BS / 16][D / 32],
+                                                 const half4 (&pf)[BS / 16], half4 onehot, float alpha,
+                                                 float4v (&acc)[D / 32][2]) {
+    constexpr int DC = D / 32;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
         acc[c][0] *= alpha;
         acc[c][1] *= alpha;
     }
-    // O^T += V^T * P^T over 32-key chunks.  The B operand is P^T straight
-    // from the score layout; the A operand is V^T, made by the one-hot MFMA.
     const float4v zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < BS / 32; ++kc) {
@@ -214,13 +283,13 @@ __device__ __forceinline__ void process_block(const Tile<BS, D> &tl, const half8
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
             {
-                const float4v t0 = mfma_16x16x16(lo4(tl.v[2 * kc][c]), onehot, zero);
-                const float4v t1 = mfma_16x16x16(lo4(tl.v[2 * kc + 1][c]), onehot, zero);
+                const float4v t0 = mfma_16x16x16(lo4(vf[2 * kc][c]), onehot, zero);
+                const float4v t1 = mfma_16x16x16(lo4(vf[2 * kc + 1][c]), onehot, zero);
                 acc[c][0] = mfma_16x16x32(cat8(to_half4(t0), to_half4(t1)), bp, acc[c][0]);
             }
             {
-                const float4v t0 = mfma_16x16x16(hi4(tl.v[2 * kc][c]), onehot, zero);
-                const float4v t1 = mfma_16x16x16(hi4(tl.v[2 * kc + 1][c]), onehot, zero);
+                const float4v t0 = mfma_16x16x16(hi4(vf[2 * kc][c]), onehot, zero);
+                const float4v t1 = mfma_16x16x16(hi4(vf[2 * kc + 1][c]), onehot, zero);
                 acc[c][1] = mfma_16x16x32(cat8(to_half4(t0), to_half4(t1)), bp, acc[c][1]);
             }
         }
@@ -230,11 +299,9 @@ __device__ __forceinline__ void process_block(const Tile<BS, D> &tl, const half8
 template <int BS, int D>
 __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
     constexpr int DC = D / 32;
-    const int lane = threadIdx.x & (kWaveSize - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x;
     const int w = blockIdx.x;
-    const int slot = (w % kNumXcd) * p.slots_per_xcd + (w / kNumXcd);
-    const int u = slot * kWavesPerBlock + wave;
+    const int u = (w % kNumXcd) * p.slots_per_xcd + (w / kNumXcd);
     if (u >= p.units) return;
     // Unit order (b, g, m) with m fastest.
     const int m = u % p.M;
@@ -285,23 +352,48 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
         acc[c][1] = float4v{0.f, 0.f, 0.f, 0.f};
     }
 
-    Tile<BS, D> ta, tb;
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf[Stage<BS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf[Stage<BS, D>::HALVES];
+    constexpr int NI = Stage<BS, D>::NI;
+    Stage<BS, D> st;
+    {
+        const size_t kv_elems = (size_t)p.B * p.N * p.G * D;
+        const size_t first = ((size_t)b * p.N * p.G + g) * D;
+        const size_t bytes = (kv_elems - first) * 2;
+        st.init(Kg, Vg, (unsigned)(bytes < 0xFFFFFFFFu ? bytes : 0xFFFFFFFFu), row_stride, p.N, lane);
+    }
+
+    // Pipeline: K and V of a block are staged in separate LDS buffers.  The
+    // next counted block's K copy is issued as soon as this block's K
+    // fragments are in registers, its V copy as soon as the V fragments are,
+    // so each copy overlaps about one block of math.
+    half8 kf[BS / 16][D / 32];
+    half8 vf[BS / 16][D / 32];
+    half4 pf[BS / 16];
     int i = scan.next(0);
     int t_cur = (i < p.T) ? scan.value(i) : 0;
-    if (i < p.T) load_block<BS, D>(ta, Kg, Vg, t_cur, p.N, row_stride, r, q4);
-    // Two-stage pipeline, unrolled by two so the buffers never need copying.
+    if (i < p.T) {
+        st.issue(false, kbuf, t_cur, lane);
+        st.issue(true, vbuf, t_cur, lane);
+    }
     while (i < p.T) {
-        int in = scan.next(i + 1);
-        int t_n = (in < p.T) ? scan.value(in) : 0;
-        if (in < p.T) load_block<BS, D>(tb, Kg, Vg, t_n, p.N, row_stride, r, q4);
-        process_block<BS, D>(ta, qf, onehot, t_cur * BS, m, p.N, p.scale_log2, m_run, l_run, acc, q4);
-        i = in;
-        t_cur = t_n;
-        if (i >= p.T) break;
-        in = scan.next(i + 1);
-        t_n = (in < p.T) ? scan.value(in) : 0;
-        if (in < p.T) load_block<BS, D>(ta, Kg, Vg, t_n, p.N, row_stride, r, q4);
-        process_block<BS, D>(tb, qf, onehot, t_cur * BS, m, p.N, p.scale_log2, m_run, l_run, acc, q4);
+        const int in = scan.next(i + 1);
+        const bool more = in < p.T;
+        const int t_n = more ? scan.value(in) : 0;
+        __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K of block i landed (its V may not have)
+        Stage<BS, D>::read(kf, kbuf, r, q4);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        if (more) st.issue(false, kbuf, t_n, lane);
+        float alpha;
+        score_block<BS, D>(kf, qf, t_cur * BS, m, p.N, p.scale_log2, m_run, l_run, alpha, pf, q4);
+        if (more)
+            __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V of block i landed (next K may not have)
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        Stage<BS, D>::read(vf, vbuf, r, q4);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        if (more) st.issue(true, vbuf, t_n, lane);
+        accumulate_block<BS, D>(vf, pf, onehot, alpha, acc);
         i = in;
         t_cur = t_n;
     }
@@ -368,8 +460,7 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     if (((uintptr_t)block_indices | (uintptr_t)LSE) & 3) return NSA_SEL_ERR_ALIGN;
 
     const int64_t units = (int64_t)B * M * G;
-    const int64_t wgs = (units + kWavesPerBlock - 1) / kWavesPerBlock;
-    const int64_t slots = (wgs + kNumXcd - 1) / kNumXcd;
+    const int64_t slots = (units + kNumXcd - 1) / kNumXcd;
     // Element counts must fit the 64-bit offsets; unit ids and the grid use int.
     const int64_t q_elems = (int64_t)B * M * H * D;
     const int64_t kv_elems = (int64_t)B * N * G * D;
