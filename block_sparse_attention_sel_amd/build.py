@@ -15,6 +15,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # Keep the compiler from forming packed fp32 VALU ops.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the softmax and the V^T conversion consume them
+    # on the VALU, so AGPR destinations would only add copies.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -10,23 +10,23 @@
 // (the "online softmax across all T blocks" requirement); O and the natural
 // log-sum-exp are written at the end.
 //
-// MI355X mapping (see the design notes for the reasoning and the roofline):
+// MI355X mapping (the design notes give the measurements behind each choice):
 //  * Scores are computed transposed, S^T = K * Q^T, on v_mfma_f32_16x16x32_f16:
 //    keys are the 16 MFMA rows, the (up to 16) heads of the group are the
-//    columns.  With keys as rows, one 128-bit global load per lane puts a K
-//    row slice straight into the MFMA A-operand layout, and the S^T result
-//    layout (lane l: head l%16, keys 4*(l/16)+i) is already the B-operand
-//    layout of the PV product, so P never leaves registers.
-//  * V arrives with the same 128-bit row loads.  PV needs V^T fragments; they
-//    are produced in registers by v_mfma_f32_16x16x16_f16 against a one-hot
-//    matrix (an exact permutation: every output is one fp16 value times 1.0).
-//    No LDS is used, so waves never synchronise and occupancy is set by VGPRs.
-//  * The T loop is software-pipelined: the next counted block's K/V loads are
-//    issued before the current block's math (register double buffering).
-//  * Workgroups (4 waves = 4 consecutive query positions of one (b, g)) are
-//    mapped XCD-aware: hardware deals workgroup w to XCD w % 8, so unit ranges
-//    are laid out so that each XCD walks a contiguous (b, g, m) range and its
-//    L2 holds the K/V prefix of few groups.
+//    columns.  The S^T result layout (lane l: head l%16, keys 4*(l/16)+i) is
+//    already the B-operand layout of the PV product, so P never leaves
+//    registers.
+//  * Each counted block is copied global -> LDS with 128-bit direct-to-LDS
+//    buffer loads whose lanes walk whole key rows (coalesced); the MFMA
+//    operand layout, which puts consecutive lanes on different rows, is only
+//    used for the LDS reads.  K fragments come from XOR-swizzled
+//    ds_read_b128; V^T fragments come straight from ds_read_b64_tr_b16.
+//  * K and V have their own LDS buffers; the next counted block's K copy is
+//    issued once this block's K fragments are in registers, its V copy once
+//    the V fragments are, so every copy overlaps about one block of math.
+//  * One wavefront per workgroup.  Hardware deals workgroup w to XCD w % 8,
+//    so units are laid out for each XCD to walk a contiguous (b, g, m)
+//    range and keep the K/V prefix of few groups in its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <limits.h>
@@ -62,12 +62,6 @@ __device__ __forceinline__ float4v mfma_16x16x32(half8 a, half8 b, float4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float4v mfma_16x16x16(half4 a, half4 b, float4v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ half4 lo4(half8 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3); }
-__device__ __forceinline__ half4 hi4(half8 v) { return __builtin_shufflevector(v, v, 4, 5, 6, 7); }
 
 __device__ __forceinline__ half4 to_half4(float4v v) {
     half4 r;
@@ -118,6 +112,129 @@ struct IndexScan {
     }
 };
 
+// Batched ds_read_b128 of one staged block into MFMA fragments, ending in
+// s_waitcnt lgkmcnt(0).  f[kt][c] comes from address a[c] + kt * 16 rows.
+template <int BS, int D>
+struct LdsBatch;
+
+#define NSA_DSR(o, a, off) "ds_read_b128 %" #o ", %" #a " offset:" #off "\n"
+
+template <>
+struct LdsBatch<64, 128> {  // 16 rows = 4096 bytes
+    __device__ static __forceinline__ void run(half8 (&f)[4][4], const unsigned (&a)[4]) {
+        asm volatile(NSA_DSR(0, 16, 0) NSA_DSR(1, 17, 0) NSA_DSR(2, 18, 0) NSA_DSR(3, 19, 0)
+                     NSA_DSR(4, 16, 4096) NSA_DSR(5, 17, 4096) NSA_DSR(6, 18, 4096) NSA_DSR(7, 19, 4096)
+                     NSA_DSR(8, 16, 8192) NSA_DSR(9, 17, 8192) NSA_DSR(10, 18, 8192) NSA_DSR(11, 19, 8192)
+                     NSA_DSR(12, 16, 12288) NSA_DSR(13, 17, 12288) NSA_DSR(14, 18, 12288)
+                     NSA_DSR(15, 19, 12288) "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[0][2]), "=&v"(f[0][3]), "=&v"(f[1][0]),
+                       "=&v"(f[1][1]), "=&v"(f[1][2]), "=&v"(f[1][3]), "=&v"(f[2][0]), "=&v"(f[2][1]),
+                       "=&v"(f[2][2]), "=&v"(f[2][3]), "=&v"(f[3][0]), "=&v"(f[3][1]), "=&v"(f[3][2]),
+                       "=&v"(f[3][3])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    }
+};
+
+template <>
+struct LdsBatch<32, 128> {
+    __device__ static __forceinline__ void run(half8 (&f)[2][4], const unsigned (&a)[4]) {
+        asm volatile(NSA_DSR(0, 8, 0) NSA_DSR(1, 9, 0) NSA_DSR(2, 10, 0) NSA_DSR(3, 11, 0)
+                     NSA_DSR(4, 8, 4096) NSA_DSR(5, 9, 4096) NSA_DSR(6, 10, 4096) NSA_DSR(7, 11, 4096)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[0][2]), "=&v"(f[0][3]), "=&v"(f[1][0]),
+                       "=&v"(f[1][1]), "=&v"(f[1][2]), "=&v"(f[1][3])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    }
+};
+
+template <>
+struct LdsBatch<64, 64> {  // 16 rows = 2048 bytes
+    __device__ static __forceinline__ void run(half8 (&f)[4][2], const unsigned (&a)[2]) {
+        asm volatile(NSA_DSR(0, 8, 0) NSA_DSR(1, 9, 0) NSA_DSR(2, 8, 2048) NSA_DSR(3, 9, 2048)
+                     NSA_DSR(4, 8, 4096) NSA_DSR(5, 9, 4096) NSA_DSR(6, 8, 6144) NSA_DSR(7, 9, 6144)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[1][0]), "=&v"(f[1][1]), "=&v"(f[2][0]),
+                       "=&v"(f[2][1]), "=&v"(f[3][0]), "=&v"(f[3][1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    }
+};
+
+template <>
+struct LdsBatch<32, 64> {
+    __device__ static __forceinline__ void run(half8 (&f)[2][2], const unsigned (&a)[2]) {
+        asm volatile(NSA_DSR(0, 4, 0) NSA_DSR(1, 5, 0) NSA_DSR(2, 4, 2048) NSA_DSR(3, 5, 2048)
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[1][0]), "=&v"(f[1][1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    }
+};
+
+#undef NSA_DSR
+
+// Transposing reads of one staged V block (ds_read_b64_tr_b16), ending in
+// s_waitcnt lgkmcnt(0).  Within each 16-lane group the instruction hands
+// lane 4a+b element b of the 8-byte pieces loaded by lanes a, a+4, a+8, a+12
+// (element j from lane a+4j).  Lane (a + 4j) of group q4 points at V row
+// 32*kc + 16*half + 4*q4 + j, head-dims 32*c + 8*a + 4*hh .. +3, so lane
+// 4a+b receives V^T[32*c + 8*a + 4*hh + b][32*kc + 16*half + 4*q4 + j]: the
+// A operand of the PV MFMA for 32-key chunk kc and head-dim set (c, hh).
+// f[kc][c][hh][half]; a[c] is the lane's address for head-dim chunk c.
+template <int BS, int D>
+struct LdsTrBatch;
+
+template <>
+struct LdsTrBatch<64, 128> {
+    __device__ static __forceinline__ void run(half4 (&f)[2][4][2][2], const unsigned (&a)[4]) {
+        asm volatile("ds_read_b64_tr_b16 %0, %16 offset:0\n" "ds_read_b64_tr_b16 %1, %16 offset:4096\n" "ds_read_b64_tr_b16 %2, %16 offset:8\n" "ds_read_b64_tr_b16 %3, %16 offset:4104\n" "ds_read_b64_tr_b16 %4, %17 offset:0\n" "ds_read_b64_tr_b16 %5, %17 offset:4096\n" "ds_read_b64_tr_b16 %6, %17 offset:8\n" "ds_read_b64_tr_b16 %7, %17 offset:4104\n" "ds_read_b64_tr_b16 %8, %18 offset:0\n" "ds_read_b64_tr_b16 %9, %18 offset:4096\n" "ds_read_b64_tr_b16 %10, %18 offset:8\n" "ds_read_b64_tr_b16 %11, %18 offset:4104\n" "ds_read_b64_tr_b16 %12, %19 offset:0\n" "ds_read_b64_tr_b16 %13, %19 offset:4096\n" "ds_read_b64_tr_b16 %14, %19 offset:8\n" "ds_read_b64_tr_b16 %15, %19 offset:4104\n" "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1]), "=&v"(f[0][2][0][0]), "=&v"(f[0][2][0][1]), "=&v"(f[0][2][1][0]), "=&v"(f[0][2][1][1]), "=&v"(f[0][3][0][0]), "=&v"(f[0][3][0][1]), "=&v"(f[0][3][1][0]), "=&v"(f[0][3][1][1])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+        asm volatile("ds_read_b64_tr_b16 %0, %16 offset:8192\n" "ds_read_b64_tr_b16 %1, %16 offset:12288\n" "ds_read_b64_tr_b16 %2, %16 offset:8200\n" "ds_read_b64_tr_b16 %3, %16 offset:12296\n" "ds_read_b64_tr_b16 %4, %17 offset:8192\n" "ds_read_b64_tr_b16 %5, %17 offset:12288\n" "ds_read_b64_tr_b16 %6, %17 offset:8200\n" "ds_read_b64_tr_b16 %7, %17 offset:12296\n" "ds_read_b64_tr_b16 %8, %18 offset:8192\n" "ds_read_b64_tr_b16 %9, %18 offset:12288\n" "ds_read_b64_tr_b16 %10, %18 offset:8200\n" "ds_read_b64_tr_b16 %11, %18 offset:12296\n" "ds_read_b64_tr_b16 %12, %19 offset:8192\n" "ds_read_b64_tr_b16 %13, %19 offset:12288\n" "ds_read_b64_tr_b16 %14, %19 offset:8200\n" "ds_read_b64_tr_b16 %15, %19 offset:12296\n" "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[1][0][0][0]), "=&v"(f[1][0][0][1]), "=&v"(f[1][0][1][0]), "=&v"(f[1][0][1][1]), "=&v"(f[1][1][0][0]), "=&v"(f[1][1][0][1]), "=&v"(f[1][1][1][0]), "=&v"(f[1][1][1][1]), "=&v"(f[1][2][0][0]), "=&v"(f[1][2][0][1]), "=&v"(f[1][2][1][0]), "=&v"(f[1][2][1][1]), "=&v"(f[1][3][0][0]), "=&v"(f[1][3][0][1]), "=&v"(f[1][3][1][0]), "=&v"(f[1][3][1][1])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    }
+};
+
+template <>
+struct LdsTrBatch<32, 128> {
+    __device__ static __forceinline__ void run(half4 (&f)[1][4][2][2], const unsigned (&a)[4]) {
+        asm volatile("ds_read_b64_tr_b16 %0, %16 offset:0\n" "ds_read_b64_tr_b16 %1, %16 offset:4096\n" "ds_read_b64_tr_b16 %2, %16 offset:8\n" "ds_read_b64_tr_b16 %3, %16 offset:4104\n" "ds_read_b64_tr_b16 %4, %17 offset:0\n" "ds_read_b64_tr_b16 %5, %17 offset:4096\n" "ds_read_b64_tr_b16 %6, %17 offset:8\n" "ds_read_b64_tr_b16 %7, %17 offset:4104\n" "ds_read_b64_tr_b16 %8, %18 offset:0\n" "ds_read_b64_tr_b16 %9, %18 offset:4096\n" "ds_read_b64_tr_b16 %10, %18 offset:8\n" "ds_read_b64_tr_b16 %11, %18 offset:4104\n" "ds_read_b64_tr_b16 %12, %19 offset:0\n" "ds_read_b64_tr_b16 %13, %19 offset:4096\n" "ds_read_b64_tr_b16 %14, %19 offset:8\n" "ds_read_b64_tr_b16 %15, %19 offset:4104\n" "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1]), "=&v"(f[0][2][0][0]), "=&v"(f[0][2][0][1]), "=&v"(f[0][2][1][0]), "=&v"(f[0][2][1][1]), "=&v"(f[0][3][0][0]), "=&v"(f[0][3][0][1]), "=&v"(f[0][3][1][0]), "=&v"(f[0][3][1][1])
+                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    }
+};
+
+template <>
+struct LdsTrBatch<64, 64> {
+    __device__ static __forceinline__ void run(half4 (&f)[2][2][2][2], const unsigned (&a)[2]) {
+        asm volatile("ds_read_b64_tr_b16 %0, %8 offset:0\n" "ds_read_b64_tr_b16 %1, %8 offset:2048\n" "ds_read_b64_tr_b16 %2, %8 offset:8\n" "ds_read_b64_tr_b16 %3, %8 offset:2056\n" "ds_read_b64_tr_b16 %4, %9 offset:0\n" "ds_read_b64_tr_b16 %5, %9 offset:2048\n" "ds_read_b64_tr_b16 %6, %9 offset:8\n" "ds_read_b64_tr_b16 %7, %9 offset:2056\n" "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+        asm volatile("ds_read_b64_tr_b16 %0, %8 offset:4096\n" "ds_read_b64_tr_b16 %1, %8 offset:6144\n" "ds_read_b64_tr_b16 %2, %8 offset:4104\n" "ds_read_b64_tr_b16 %3, %8 offset:6152\n" "ds_read_b64_tr_b16 %4, %9 offset:4096\n" "ds_read_b64_tr_b16 %5, %9 offset:6144\n" "ds_read_b64_tr_b16 %6, %9 offset:4104\n" "ds_read_b64_tr_b16 %7, %9 offset:6152\n" "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[1][0][0][0]), "=&v"(f[1][0][0][1]), "=&v"(f[1][0][1][0]), "=&v"(f[1][0][1][1]), "=&v"(f[1][1][0][0]), "=&v"(f[1][1][0][1]), "=&v"(f[1][1][1][0]), "=&v"(f[1][1][1][1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    }
+};
+
+template <>
+struct LdsTrBatch<32, 64> {
+    __device__ static __forceinline__ void run(half4 (&f)[1][2][2][2], const unsigned (&a)[2]) {
+        asm volatile("ds_read_b64_tr_b16 %0, %8 offset:0\n" "ds_read_b64_tr_b16 %1, %8 offset:2048\n" "ds_read_b64_tr_b16 %2, %8 offset:8\n" "ds_read_b64_tr_b16 %3, %8 offset:2056\n" "ds_read_b64_tr_b16 %4, %9 offset:0\n" "ds_read_b64_tr_b16 %5, %9 offset:2048\n" "ds_read_b64_tr_b16 %6, %9 offset:8\n" "ds_read_b64_tr_b16 %7, %9 offset:2056\n" "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1])
+                     : "v"(a[0]), "v"(a[1])
+                     : "memory");
+    }
+};
+
+
 // LDS staging of one gathered block (K and V, BS rows of D fp16 each).
 //
 // The block is copied global -> LDS with 128-bit direct-to-LDS buffer loads
@@ -162,15 +279,19 @@ struct Stage {
         }
     }
 
-    __device__ static __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, _Float16 *lds, unsigned voff,
+    typedef __attribute__((address_space(3))) _Float16 lds_half;
+
+    __device__ static __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, lds_half *lds, unsigned voff,
                                                 unsigned soff, int s) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (__attribute__((address_space(3))) void *)(lds + s * (kWaveSize * 8)), 16, voff, soff, 0, 0);
     }
 
-    // Issues the copy of block t of K (or V) into buf; completes on vmcnt.
-    __device__ __forceinline__ void issue(bool is_v, _Float16 *buf, int t, int lane) const {
-        const __amdgpu_buffer_rsrc_t rs = is_v ? rv : rk;
+    // Issues the copy of block t of K (rs = rk) or V (rs = rv) into buf;
+    // completes on vmcnt.
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, _Float16 *buf_generic, int t,
+                                          int lane) const {
+        lds_half *buf = (lds_half *)buf_generic;  // one address-space conversion per block
         if (t * BS + BS <= N) {
             const unsigned base = (unsigned)(t * BS) * row_bytes;
 #pragma unroll
@@ -191,23 +312,36 @@ struct Stage {
     }
 
     // MFMA A-operand fragments of one staged block: lane l gets row
-    // 16*kt + l%16, head-dim 32*c + 8*(l/16) .. +7.
+    // 16*kt + l%16, head-dim 32*c + 8*(l/16) .. +7.  The reads are issued
+    // as one inline-asm batch that ends in its own lgkmcnt(0) wait: the
+    // compiler would otherwise guard every LDS read with vmcnt(0), i.e.
+    // wait for all copies in flight, including the other buffer's.
     __device__ static __forceinline__ void read(half8 (&f)[BS / 16][D / 32], const _Float16 *buf, int r,
                                                 int q4) {
+        const unsigned base = (unsigned)(size_t)(const __attribute__((address_space(3))) _Float16 *)buf;
+        unsigned a[D / 32];
 #pragma unroll
-        for (int kt = 0; kt < BS / 16; ++kt) {
-            const int row = kt * 16 + r;
+        for (int c = 0; c < D / 32; ++c) a[c] = base + (unsigned)(r * D + ((c * 4 + q4) ^ swz(r)) * 8) * 2;
+        LdsBatch<BS, D>::run(f, a);
+    }
+
+    // V^T operands of one staged block for the PV MFMAs (see LdsTrBatch).
+    __device__ static __forceinline__ void read_vt(half4 (&f)[BS / 32][D / 32][2][2], const _Float16 *buf,
+                                                   int lane) {
+        const unsigned base = (unsigned)(size_t)(const __attribute__((address_space(3))) _Float16 *)buf;
+        const int q4 = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
+        const int row = 4 * q4 + j;  // row within a 16-row group; the group offset is immediate
+        unsigned addr[D / 32];
 #pragma unroll
-            for (int c = 0; c < D / 32; ++c)
-                f[kt][c] = *(const half8 *)(buf + row * D + ((c * 4 + q4) ^ swz(row)) * 8);
-        }
+        for (int c = 0; c < D / 32; ++c)
+            addr[c] = base + (unsigned)(row * D * 2 + ((4 * c + a) ^ swz(row)) * 16);
+        LdsTrBatch<BS, D>::run(f, addr);
     }
 };
 
 // s_waitcnt immediate for "at most n vector-memory ops outstanding"
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-constexpr int kWaitLgkm0 = 0xC07F;  // all LDS reads done
 
 // Scores of one gathered block folded into the running softmax state:
 // S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, head l%16), scaled
@@ -265,10 +399,10 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
 
 // O^T = alpha * O^T + V^T * P^T over 32-key chunks.  acc[c][hh] holds O^T rows
 // d = 32*c + 8*(l/16) + 4*hh + i for head l%16.  The B operand is P^T straight
-// from the score layout; the A operand V^T is made by the one-hot MFMA.
+// from the score layout; the A operand V^T comes from the transposing reads.
 template <int BS, int D>
-__device__ __forceinline__ void accumulate_block(const half8 (&vf)[BS / 16][D / 32],
-                                                 const half4 (&pf)[BS / 16], half4 onehot, float alpha,
+__device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 32][2][2],
+                                                 const half4 (&pf)[BS / 16], float alpha,
                                                  float4v (&acc)[D / 32][2]) {
     constexpr int DC = D / 32;
 #pragma unroll
@@ -276,23 +410,14 @@ __device__ __forceinline__ void accumulate_block(const half8 (&vf)[BS / 16][D / 
         acc[c][0] *= alpha;
         acc[c][1] *= alpha;
     }
-    const float4v zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < BS / 32; ++kc) {
         const half8 bp = cat8(pf[2 * kc], pf[2 * kc + 1]);
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            {
-                const float4v t0 = mfma_16x16x16(lo4(vf[2 * kc][c]), onehot, zero);
-                const float4v t1 = mfma_16x16x16(lo4(vf[2 * kc + 1][c]), onehot, zero);
-                acc[c][0] = mfma_16x16x32(cat8(to_half4(t0), to_half4(t1)), bp, acc[c][0]);
-            }
-            {
-                const float4v t0 = mfma_16x16x16(hi4(vf[2 * kc][c]), onehot, zero);
-                const float4v t1 = mfma_16x16x16(hi4(vf[2 * kc + 1][c]), onehot, zero);
-                acc[c][1] = mfma_16x16x32(cat8(to_half4(t0), to_half4(t1)), bp, acc[c][1]);
-            }
-        }
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                acc[c][hh] = mfma_16x16x32(cat8(vt[kc][c][hh][0], vt[kc][c][hh][1]), bp, acc[c][hh]);
     }
 }
 
@@ -326,11 +451,6 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
             qf[c] = (r < p.gs) ? x : zero8;
         }
     }
-    // One-hot B operand of the V transpose: column l%16 picks head-dim
-    // 8*((l%16)/4) + (l%16)%4 of the lane group's 4-wide slice.
-    half4 onehot = {0, 0, 0, 0};
-    if (q4 == (r >> 2)) onehot[r & 3] = (_Float16)1.0f;
-
     const int row_stride = p.G * D;
     const _Float16 *Kg = p.K + ((size_t)b * p.N * p.G + g) * D;
     const _Float16 *Vg = p.V + ((size_t)b * p.N * p.G + g) * D;
@@ -368,13 +488,13 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
     // fragments are in registers, its V copy as soon as the V fragments are,
     // so each copy overlaps about one block of math.
     half8 kf[BS / 16][D / 32];
-    half8 vf[BS / 16][D / 32];
+    half4 vt[BS / 32][D / 32][2][2];
     half4 pf[BS / 16];
     int i = scan.next(0);
     int t_cur = (i < p.T) ? scan.value(i) : 0;
     if (i < p.T) {
-        st.issue(false, kbuf, t_cur, lane);
-        st.issue(true, vbuf, t_cur, lane);
+        st.issue(st.rk, kbuf, t_cur, lane);
+        st.issue(st.rv, vbuf, t_cur, lane);
     }
     while (i < p.T) {
         const int in = scan.next(i + 1);
@@ -382,18 +502,16 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
         const int t_n = more ? scan.value(in) : 0;
         __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K of block i landed (its V may not have)
         Stage<BS, D>::read(kf, kbuf, r, q4);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        if (more) st.issue(false, kbuf, t_n, lane);
+        if (more) st.issue(st.rk, kbuf, t_n, lane);
         float alpha;
         score_block<BS, D>(kf, qf, t_cur * BS, m, p.N, p.scale_log2, m_run, l_run, alpha, pf, q4);
         if (more)
             __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V of block i landed (next K may not have)
         else
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
-        Stage<BS, D>::read(vf, vbuf, r, q4);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        if (more) st.issue(true, vbuf, t_n, lane);
-        accumulate_block<BS, D>(vf, pf, onehot, alpha, acc);
+        Stage<BS, D>::read_vt(vt, vbuf, lane);
+        if (more) st.issue(st.rv, vbuf, t_n, lane);
+        accumulate_block<BS, D>(vt, pf, alpha, acc);
         i = in;
         t_cur = t_n;
     }
