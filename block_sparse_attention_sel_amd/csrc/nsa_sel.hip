@@ -40,7 +40,9 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
-constexpr int kThreads = kWaveSize;  // one wavefront (one unit) per workgroup
+constexpr int kWavesPerWG = 4;
+constexpr int kThreads = kWaveSize * kWavesPerWG;
+constexpr int kMaxPack = 4;  // queries packed into one wavefront's 16 MFMA columns
 constexpr int kNumXcd = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -53,7 +55,9 @@ struct Params {
     _Float16 *O;
     float *LSE;
     int B, M, N, H, G, T, gs, NB;
-    int units;          // B * M * G
+    int pack;           // queries per wavefront: min(kMaxPack, 16 / gs)
+    int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / pack)
+    int wslots;         // B * G * wslots_per_bg
     int slots_per_xcd;  // workgroup slots per XCD
     float scale_log2;   // log2(e) / sqrt(D)
 };
@@ -111,6 +115,54 @@ struct IndexScan {
         return __builtin_amdgcn_readlane(val, i - base);
     }
 };
+
+constexpr int kDone = INT_MAX;
+
+// Walks the counted entries of one index row in row order.
+struct Cursor {
+    IndexScan sc;
+    int pos;
+    int cur;  // block of the current counted entry, or kDone
+
+    __device__ __forceinline__ void init(const int32_t *row, int T, int cm, int NB, int lane, bool live) {
+        sc.row = row;
+        sc.T = live ? T : 0;
+        sc.cm = cm;
+        sc.NB = NB;
+        sc.lane = lane;
+        sc.base = 0;
+        sc.mask = 0;
+        sc.val = -1;
+        if (live) sc.load(0);
+        pos = sc.next(0);
+        cur = pos < sc.T ? sc.value(pos) : kDone;
+    }
+    __device__ __forceinline__ void advance() {
+        pos = sc.next(pos + 1);
+        cur = pos < sc.T ? sc.value(pos) : kDone;
+    }
+};
+
+// Merges the rows of the packed queries: returns the smallest current block
+// and the mask of queries whose current entry is that block (advancing
+// them).  Every counted entry of every row is returned exactly once; rows
+// sorted ascending are swept in ascending block order and a block several
+// rows select at the same time is returned once for all of them.
+__device__ __forceinline__ int merge_next(Cursor (&c)[kMaxPack], unsigned &active) {
+    int t = c[0].cur;
+#pragma unroll
+    for (int k = 1; k < kMaxPack; ++k) t = c[k].cur < t ? c[k].cur : t;
+    active = 0;
+    if (t == kDone) return t;
+#pragma unroll
+    for (int k = 0; k < kMaxPack; ++k) {
+        if (c[k].cur == t) {
+            active |= 1u << k;
+            c[k].advance();
+        }
+    }
+    return t;
+}
 
 // Batched ds_read_b128 of one staged block into MFMA fragments, ending in
 // s_waitcnt lgkmcnt(0).  f[kt][c] comes from address a[c] + kt * 16 rows.
@@ -344,13 +396,24 @@ struct Stage {
 constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Scores of one gathered block folded into the running softmax state:
-// S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, head l%16), scaled
-// into the log2 domain, causally masked, then the running max, the rescale
-// factor of the accumulator and the block's probabilities P^T (fp16).
+// S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, column l%16), then
+// the running max, the rescale factor of the accumulator and the block's
+// probabilities P^T (fp16), all in the log2 domain (x * log2(e) / sqrt(D)).
+//
+// causal: the block reaches past the smallest packed query or past N, so
+//   keys past the column's query (my_m) or past N are masked to -inf.
+// col_mask: some packed query did not select this block; for those columns
+//   (col_on false) the running state is left unchanged and P is zero.
+// The running max is only raised when a block's max exceeds it by more than
+// kLazyMax (P then stays below 2^kLazyMax, well inside fp16), so most blocks
+// need no rescale of the accumulator (alpha == 1 exactly).
+constexpr float kLazyMax = 8.0f;
+
 template <int BS, int D>
 __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
-                                            int key0, int m, int N, float scale_log2, float &m_run,
-                                            float &l_run, float &alpha, half4 (&pf)[BS / 16], int q4) {
+                                            int key0, bool causal, bool col_mask, bool col_on, int my_m,
+                                            int N, float scale_log2, float &m_run, float &l_run,
+                                            float &alpha, half4 (&pf)[BS / 16], int q4) {
     constexpr int KT = BS / 16;
     constexpr int DC = D / 32;
     float4v s[KT];
@@ -360,28 +423,28 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
 #pragma unroll
         for (int c = 0; c < DC; ++c) s[kt] = mfma_16x16x32(kf[kt][c], qf[c], s[kt]);
     }
-    // The mask only bites in the query's own block (keys past m) or past N.
-    const bool need_mask = (key0 + BS - 1 > m) || (key0 + BS > N);
+    if (causal) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = key0 + kt * 16 + q4 * 4 + i;
+                if (key > my_m || key >= N) s[kt][i] = -INFINITY;
+            }
+    }
+    // Row max of the raw scores (the scale is positive), then over the 4
+    // lanes (l, l^16, l^32, l^48) that share a column.
     float mloc = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float x = s[kt][i] * scale_log2;
-            if (need_mask) {
-                const int key = key0 + kt * 16 + q4 * 4 + i;
-                if (key > m || key >= N) x = -INFINITY;
-            }
-            s[kt][i] = x;
-            mloc = fmaxf(mloc, x);
-        }
-    }
-    // Row max over the 4 lanes (l, l^16, l^32, l^48) that share a head.
+    for (int kt = 0; kt < KT; ++kt) mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+    const float m_blk = mloc * scale_log2;
+    float m_new = (m_blk > m_run + kLazyMax) ? m_blk : m_run;
+    const bool off = col_mask && !col_on;
+    if (off) m_new = m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    alpha = fast_exp2(m_run - m_use);
+    alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_use);
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
@@ -389,7 +452,8 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
         float4v pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pv[i] = fast_exp2(s[kt][i] - m_use);
+            pv[i] = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -m_use));
+            if (off) pv[i] = 0.f;
             psum += pv[i];
         }
         pf[kt] = to_half4(pv);
@@ -405,10 +469,12 @@ __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 
                                                  const half4 (&pf)[BS / 16], float alpha,
                                                  float4v (&acc)[D / 32][2]) {
     constexpr int DC = D / 32;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // wave-uniform: some column rescales
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-        acc[c][0] *= alpha;
-        acc[c][1] *= alpha;
+        for (int c = 0; c < DC; ++c) {
+            acc[c][0] *= alpha;
+            acc[c][1] *= alpha;
+        }
     }
 #pragma unroll
     for (int kc = 0; kc < BS / 32; ++kc) {
@@ -424,44 +490,51 @@ __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 
 template <int BS, int D>
 __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
     constexpr int DC = D / 32;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x;
-    const int u = (w % kNumXcd) * p.slots_per_xcd + (w / kNumXcd);
-    if (u >= p.units) return;
-    // Unit order (b, g, m) with m fastest.
-    const int m = u % p.M;
-    const int bg = u / p.M;
+    const int ws = ((w % kNumXcd) * p.slots_per_xcd + (w / kNumXcd)) * kWavesPerWG + wave;
+    if (ws >= p.wslots) return;
+    // Wavefront slot -> (b, g) and the queries m0 .. m0 + nq - 1 it packs.
+    const int bg = ws / p.wslots_per_bg;
+    const int m0 = (ws - bg * p.wslots_per_bg) * p.pack;
+    const int nq = min(p.pack, p.M - m0);
     const int g = bg % p.G;
     const int b = bg / p.G;
     const int r = lane & 15;
     const int q4 = lane >> 4;
     const int h0 = g * p.gs;
+    // MFMA column r carries head h0 + r % gs of query m0 + r / gs.
+    const int my_q = r / p.gs;
+    const bool my_live = my_q < nq;
+    const int my_m = m0 + (my_live ? my_q : 0);
+    const int my_h = h0 + (r - my_q * p.gs);
 
-    // Q^T fragments (B operand): lane l holds head h0 + l%16, head-dim slice
-    // 32*c + 8*(l/16) .. +7; heads past the group are zero columns.
+    // Q^T fragments (B operand): lane l holds column l%16, head-dim slice
+    // 32*c + 8*(l/16) .. +7; columns without a query are zero.
     half8 qf[DC];
     {
-        // Padding columns read a real head row (kept in bounds) and are zeroed.
-        const int hq = (r < p.gs) ? h0 + r : h0;
-        const _Float16 *qrow = p.Q + ((size_t)(b * (size_t)p.M + m) * p.H + hq) * D;
+        const _Float16 *qrow = p.Q + ((size_t)(b * (size_t)p.M + my_m) * p.H + (my_live ? my_h : h0)) * D;
         const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
             const half8 x = *(const half8 *)(qrow + c * 32 + q4 * 8);
-            qf[c] = (r < p.gs) ? x : zero8;
+            qf[c] = my_live ? x : zero8;
         }
     }
+
     const int row_stride = p.G * D;
     const _Float16 *Kg = p.K + ((size_t)b * p.N * p.G + g) * D;
     const _Float16 *Vg = p.V + ((size_t)b * p.N * p.G + g) * D;
 
-    IndexScan scan;
-    scan.row = p.idx + ((size_t)(b * (size_t)p.M + m) * p.G + g) * p.T;
-    scan.T = p.T;
-    scan.cm = m / BS;
-    scan.NB = p.NB;
-    scan.lane = lane;
-    scan.load(0);
+    Cursor cur[kMaxPack];
+#pragma unroll
+    for (int k = 0; k < kMaxPack; ++k) {
+        const int mk = m0 + (k < nq ? k : 0);
+        cur[k].init(p.idx + ((size_t)(b * (size_t)p.M + mk) * p.G + g) * p.T, p.T, mk / BS, p.NB, lane,
+                    k < nq);
+    }
+    const unsigned all_live = (1u << nq) - 1u;
 
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -472,8 +545,10 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
         acc[c][1] = float4v{0.f, 0.f, 0.f, 0.f};
     }
 
-    __shared__ __attribute__((aligned(16))) _Float16 kbuf[Stage<BS, D>::HALVES];
-    __shared__ __attribute__((aligned(16))) _Float16 vbuf[Stage<BS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
+    _Float16 *kbuf = kbuf_all[wave];
+    _Float16 *vbuf = vbuf_all[wave];
     constexpr int NI = Stage<BS, D>::NI;
     Stage<BS, D> st;
     {
@@ -483,45 +558,51 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
         st.init(Kg, Vg, (unsigned)(bytes < 0xFFFFFFFFu ? bytes : 0xFFFFFFFFu), row_stride, p.N, lane);
     }
 
-    // Pipeline: K and V of a block are staged in separate LDS buffers.  The
-    // next counted block's K copy is issued as soon as this block's K
-    // fragments are in registers, its V copy as soon as the V fragments are,
-    // so each copy overlaps about one block of math.
+    // Pipeline over the merged block sequence: while block t0 is computed,
+    // the copies of the next block t1 into LDS are in flight -- its K copy
+    // is issued as soon as t0's K fragments are in registers, its V copy as
+    // soon as t0's V operands are, so each copy overlaps about one block of
+    // math.  Loads complete in issue order, so each wait names how many later
+    // loads may still be pending.
     half8 kf[BS / 16][D / 32];
     half4 vt[BS / 32][D / 32][2][2];
     half4 pf[BS / 16];
-    int i = scan.next(0);
-    int t_cur = (i < p.T) ? scan.value(i) : 0;
-    if (i < p.T) {
-        st.issue(st.rk, kbuf, t_cur, lane);
-        st.issue(st.rv, vbuf, t_cur, lane);
+    unsigned a0, a1;
+    int t0 = merge_next(cur, a0);
+    if (t0 != kDone) {
+        st.issue(st.rk, kbuf, t0, lane);
+        st.issue(st.rv, vbuf, t0, lane);
     }
-    while (i < p.T) {
-        const int in = scan.next(i + 1);
-        const bool more = in < p.T;
-        const int t_n = more ? scan.value(in) : 0;
-        __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K of block i landed (its V may not have)
+    while (t0 != kDone) {
+        const int t1 = merge_next(cur, a1);
+        const bool has1 = t1 != kDone;
+        __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K(t0) landed; V(t0) may be pending
         Stage<BS, D>::read(kf, kbuf, r, q4);
-        if (more) st.issue(st.rk, kbuf, t_n, lane);
+        if (has1) st.issue(st.rk, kbuf, t1, lane);
+        const int key0 = t0 * BS;
+        const bool causal = (key0 + BS - 1 > m0) || (key0 + BS > p.N);
+        const bool col_mask = a0 != all_live;
+        const bool col_on = my_live && ((a0 >> my_q) & 1u);
         float alpha;
-        score_block<BS, D>(kf, qf, t_cur * BS, m, p.N, p.scale_log2, m_run, l_run, alpha, pf, q4);
-        if (more)
-            __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V of block i landed (next K may not have)
+        score_block<BS, D>(kf, qf, key0, causal, col_mask, col_on, my_m, p.N, p.scale_log2, m_run, l_run,
+                           alpha, pf, q4);
+        if (has1)
+            __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(t0) landed; K(t1) may be pending
         else
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
         Stage<BS, D>::read_vt(vt, vbuf, lane);
-        if (more) st.issue(st.rv, vbuf, t_n, lane);
+        if (has1) st.issue(st.rv, vbuf, t1, lane);
         accumulate_block<BS, D>(vt, pf, alpha, acc);
-        i = in;
-        t_cur = t_n;
+        t0 = t1;
+        a0 = a1;
     }
 
-    // Epilogue: total row sum over the 4 lanes of a head, normalise, store.
+    // Epilogue: total row sum over the 4 lanes of a column, normalise, store.
     float l = l_run + __shfl_xor(l_run, 16);
     l += __shfl_xor(l, 32);
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    if (r < p.gs) {
-        _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + m) * p.H + h0 + r) * D;
+    if (my_live) {
+        _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + my_m) * p.H + my_h) * D;
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
             const half4 lo = to_half4(acc[c][0] * inv);
@@ -530,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
         }
         if (q4 == 0) {
             const float lse = l > 0.f ? m_run * kLn2 + logf(l) : -INFINITY;
-            p.LSE[((size_t)b * p.H + h0 + r) * p.M + m] = lse;
+            p.LSE[((size_t)b * p.H + my_h) * p.M + my_m] = lse;
         }
     }
 }
@@ -578,7 +659,11 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     if (((uintptr_t)block_indices | (uintptr_t)LSE) & 3) return NSA_SEL_ERR_ALIGN;
 
     const int64_t units = (int64_t)B * M * G;
-    const int64_t slots = (units + kNumXcd - 1) / kNumXcd;
+    const int pack = (16 / gs) < kMaxPack ? (16 / gs) : kMaxPack;
+    const int64_t wslots_per_bg = ((int64_t)M + pack - 1) / pack;
+    const int64_t wslots = (int64_t)B * G * wslots_per_bg;
+    const int64_t wgs = (wslots + kWavesPerWG - 1) / kWavesPerWG;
+    const int64_t slots = (wgs + kNumXcd - 1) / kNumXcd;
     // Element counts must fit the 64-bit offsets; unit ids and the grid use int.
     const int64_t q_elems = (int64_t)B * M * H * D;
     const int64_t kv_elems = (int64_t)B * N * G * D;
@@ -607,7 +692,9 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     p.LSE = LSE;
     p.B = B; p.M = M; p.N = N; p.H = H; p.G = G; p.T = T; p.gs = gs;
     p.NB = (N + block_size - 1) / block_size;
-    p.units = (int)units;
+    p.pack = pack;
+    p.wslots_per_bg = (int)wslots_per_bg;
+    p.wslots = (int)wslots;
     p.slots_per_xcd = (int)slots;
     p.scale_log2 = kLog2e / sqrtf((float)D);
     const int grid = (int)(slots * kNumXcd);
