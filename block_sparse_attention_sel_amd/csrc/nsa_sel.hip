@@ -31,6 +31,8 @@
 #include <stdint.h>
 #include <limits.h>
 
+#include <atomic>
+
 #include "nsa_sel.h"
 
 namespace {
@@ -42,7 +44,6 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 constexpr int kWaveSize = 64;
 constexpr int kWavesPerWG = 4;
 constexpr int kThreads = kWaveSize * kWavesPerWG;
-constexpr int kMaxPack = 4;  // queries packed into one wavefront's 16 MFMA columns
 constexpr int kNumXcd = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -55,10 +56,12 @@ struct Params {
     _Float16 *O;
     float *LSE;
     int B, M, N, H, G, T, gs, NB;
-    int pack;           // queries per wavefront: min(kMaxPack, 16 / gs)
+    int pack;           // queries per wavefront (1, 2 or 4; see nsa_sel_fwd)
     int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / pack)
     int wslots;         // B * G * wslots_per_bg
-    int slots_per_xcd;  // workgroup slots per XCD
+    int per_xcd;        // wavefront slots owned by each XCD: ceil(wslots / 8)
+    int gen_step;       // wavefront slots one XCD runs per launch (its CUs x 4)
+    int gen;            // generation (launch) index
     float scale_log2;   // log2(e) / sqrt(D)
 };
 
@@ -148,14 +151,15 @@ struct Cursor {
 // them).  Every counted entry of every row is returned exactly once; rows
 // sorted ascending are swept in ascending block order and a block several
 // rows select at the same time is returned once for all of them.
-__device__ __forceinline__ int merge_next(Cursor (&c)[kMaxPack], unsigned &active) {
+template <int PACK>
+__device__ __forceinline__ int merge_next(Cursor (&c)[PACK], unsigned &active) {
     int t = c[0].cur;
 #pragma unroll
-    for (int k = 1; k < kMaxPack; ++k) t = c[k].cur < t ? c[k].cur : t;
+    for (int k = 1; k < PACK; ++k) t = c[k].cur < t ? c[k].cur : t;
     active = 0;
     if (t == kDone) return t;
 #pragma unroll
-    for (int k = 0; k < kMaxPack; ++k) {
+    for (int k = 0; k < PACK; ++k) {
         if (c[k].cur == t) {
             active |= 1u << k;
             c[k].advance();
@@ -487,18 +491,16 @@ __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 
     }
 }
 
-template <int BS, int D>
-__global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
+// One wavefront slot: the packed queries m0 .. m0 + nq - 1 of one (b, g),
+// from index rows to stored O and LSE.  kbuf/vbuf are the wavefront's LDS
+// staging buffers.
+template <int BS, int D, int PACK>
+__device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf) {
     constexpr int DC = D / 32;
-    const int lane = threadIdx.x & (kWaveSize - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int w = blockIdx.x;
-    const int ws = ((w % kNumXcd) * p.slots_per_xcd + (w / kNumXcd)) * kWavesPerWG + wave;
-    if (ws >= p.wslots) return;
     // Wavefront slot -> (b, g) and the queries m0 .. m0 + nq - 1 it packs.
     const int bg = ws / p.wslots_per_bg;
-    const int m0 = (ws - bg * p.wslots_per_bg) * p.pack;
-    const int nq = min(p.pack, p.M - m0);
+    const int m0 = (ws - bg * p.wslots_per_bg) * PACK;
+    const int nq = min(PACK, p.M - m0);
     const int g = bg % p.G;
     const int b = bg / p.G;
     const int r = lane & 15;
@@ -527,9 +529,9 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
     const _Float16 *Kg = p.K + ((size_t)b * p.N * p.G + g) * D;
     const _Float16 *Vg = p.V + ((size_t)b * p.N * p.G + g) * D;
 
-    Cursor cur[kMaxPack];
+    Cursor cur[PACK];
 #pragma unroll
-    for (int k = 0; k < kMaxPack; ++k) {
+    for (int k = 0; k < PACK; ++k) {
         const int mk = m0 + (k < nq ? k : 0);
         cur[k].init(p.idx + ((size_t)(b * (size_t)p.M + mk) * p.G + g) * p.T, p.T, mk / BS, p.NB, lane,
                     k < nq);
@@ -545,10 +547,6 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
         acc[c][1] = float4v{0.f, 0.f, 0.f, 0.f};
     }
 
-    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
-    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
-    _Float16 *kbuf = kbuf_all[wave];
-    _Float16 *vbuf = vbuf_all[wave];
     constexpr int NI = Stage<BS, D>::NI;
     Stage<BS, D> st;
     {
@@ -616,15 +614,61 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
     }
 }
 
+template <int BS, int D, int PACK>
+__global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int w = blockIdx.x;
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
+    // Generation p.gen: XCD w % 8 runs the next gen_step wavefront slots of its
+    // contiguous range, one workgroup per CU.
+    const int loc = p.gen * p.gen_step + (w / kNumXcd) * kWavesPerWG + wave;
+    const int ws = (w % kNumXcd) * p.per_xcd + loc;
+    if (loc >= p.per_xcd || ws >= p.wslots) return;
+    run_slot<BS, D, PACK>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+}
+
 bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
 }
 
-template <int BS, int D>
-hipError_t launch(const Params &p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, D>), dim3(grid), dim3(kThreads), 0, stream, p);
+// Queues the generations in order on the stream.  Every generation starts
+// all its workgroups together and ends before the next starts, so the units
+// resident on an XCD sweep key space in step and share its L2.
+template <int BS, int D, int PACK>
+hipError_t launch(const Params &p, int wg_per_xcd, hipStream_t stream) {
+    const int gens = (p.per_xcd + p.gen_step - 1) / p.gen_step;
+    Params q = p;
+    for (int g = 0; g < gens; ++g) {
+        q.gen = g;
+        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, D, PACK>), dim3(wg_per_xcd * kNumXcd), dim3(kThreads), 0, stream,
+                           q);
+    }
     return hipGetLastError();
+}
+
+template <int BS, int D>
+hipError_t launch_pack(const Params &p, int wg_per_xcd, hipStream_t stream) {
+    if (p.pack == 4) return launch<BS, D, 4>(p, wg_per_xcd, stream);
+    if (p.pack == 2) return launch<BS, D, 2>(p, wg_per_xcd, stream);
+    return launch<BS, D, 1>(p, wg_per_xcd, stream);
+}
+
+// Compute units of the current device, cached per device (the first call on a
+// device asks the runtime; a failed query falls back to 256).
+int device_cus() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 }  // namespace
@@ -659,18 +703,17 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     if (((uintptr_t)block_indices | (uintptr_t)LSE) & 3) return NSA_SEL_ERR_ALIGN;
 
     const int64_t units = (int64_t)B * M * G;
-    const int pack = (16 / gs) < kMaxPack ? (16 / gs) : kMaxPack;
+    // Queries per wavefront: as many whole groups of gs heads as fit the 16
+    // MFMA columns, rounded down to 1, 2 or 4.
+    const int pack = (16 / gs) >= 4 ? 4 : (16 / gs) >= 2 ? 2 : 1;
     const int64_t wslots_per_bg = ((int64_t)M + pack - 1) / pack;
     const int64_t wslots = (int64_t)B * G * wslots_per_bg;
-    const int64_t wgs = (wslots + kWavesPerWG - 1) / kWavesPerWG;
-    const int64_t slots = (wgs + kNumXcd - 1) / kNumXcd;
+    const int64_t per_xcd = (wslots + kNumXcd - 1) / kNumXcd;
     // Element counts must fit the 64-bit offsets; unit ids and the grid use int.
     const int64_t q_elems = (int64_t)B * M * H * D;
     const int64_t kv_elems = (int64_t)B * N * G * D;
     const int64_t idx_elems = (int64_t)B * M * G * T;
-    if (units > INT_MAX || slots * kNumXcd * kThreads > (int64_t)UINT32_MAX ||
-        (int64_t)N * G * D > INT_MAX)
-        return NSA_SEL_ERR_RANGE;
+    if (units > INT_MAX || (int64_t)N * G * D > INT_MAX) return NSA_SEL_ERR_RANGE;
 
     const size_t q_bytes = (size_t)q_elems * 2, kv_bytes = (size_t)kv_elems * 2;
     const size_t idx_bytes = (size_t)idx_elems * 4, lse_bytes = (size_t)B * H * M * 4;
@@ -695,14 +738,16 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     p.pack = pack;
     p.wslots_per_bg = (int)wslots_per_bg;
     p.wslots = (int)wslots;
-    p.slots_per_xcd = (int)slots;
+    p.per_xcd = (int)per_xcd;
     p.scale_log2 = kLog2e / sqrtf((float)D);
-    const int grid = (int)(slots * kNumXcd);
+    const int wg_per_xcd = device_cus() / kNumXcd > 0 ? device_cus() / kNumXcd : 1;
+    p.gen_step = wg_per_xcd * kWavesPerWG;
+    p.gen = 0;
 
     hipError_t e;
     if (block_size == 64)
-        e = (D == 128) ? launch<64, 128>(p, grid, stream) : launch<64, 64>(p, grid, stream);
+        e = (D == 128) ? launch_pack<64, 128>(p, wg_per_xcd, stream) : launch_pack<64, 64>(p, wg_per_xcd, stream);
     else
-        e = (D == 128) ? launch<32, 128>(p, grid, stream) : launch<32, 64>(p, grid, stream);
+        e = (D == 128) ? launch_pack<32, 128>(p, wg_per_xcd, stream) : launch_pack<32, 64>(p, wg_per_xcd, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
 }
