@@ -30,7 +30,7 @@ from block_sparse_attention_sel_amd.inputs import CONFIGS, Config, block_indices
 
 HBM_PEAK_GBPS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "nsa_sel_fwd_64k_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "nsa_sel_fwd_64k_hbm_counters.json")
 KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_sel_amd", "csrc", "nsa_sel.hip")
 
 
@@ -63,15 +63,50 @@ def _kernel_sha() -> str:
 
 
 def _traffic():
-    """HBM bytes per launch from committed rocprofv3 counters, if they were
-    taken on the current kernel source; else None."""
+    """HBM bytes per nsa_sel_fwd call from committed rocprofv3 counters, if
+    they were taken on the current kernel source; else None."""
     try:
         rec = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_sha256") != _kernel_sha():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_call")
+
+
+def _counter_sums(csv_path: str, counter: str):
+    """Per-dispatch sums of one counter: {dispatch_id: (kernel_name, value)}."""
+    import csv
+    out = {}
+    for row in csv.DictReader(open(csv_path)):
+        if row["Counter_Name"] != counter:
+            continue
+        d = int(row["Dispatch_Id"])
+        name, v = out.get(d, (row["Kernel_Name"], 0.0))
+        out[d] = (name, v + float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, calls: int, copy_mib: int, out_path: str):
+    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-probe-mib N --steps S --warmup W --no-dense
+    --no-cpu-baseline` into HBM bytes per nsa_sel_fwd call.  Each counter is
+    scaled by what it reads for the plain N MiB device copy in the same run."""
+    res = {"kernel_sha256": _kernel_sha(), "calls": calls, "copy_probe_mib": copy_mib}
+    for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
+        sums = _counter_sums(path, counter)
+        copy = [v for (n, v) in sums.values() if "copyBuffer" in n and v > 1000]
+        kern = [v for (n, v) in sums.values() if "nsa_sel_fwd_kernel" in n]
+        scale = (copy_mib * 1024.0) / copy[0]
+        res[f"{tag}_kib_raw_per_call"] = sum(kern) / calls
+        res[f"{tag}_copy_scale"] = scale
+        res[f"{tag}_bytes_per_call"] = sum(kern) / calls * scale * 1024.0
+        res["dispatches_per_call"] = len(kern) / calls
+    res["hbm_bytes_per_call"] = res["fetch_bytes_per_call"] + res["write_bytes_per_call"]
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    return res
 
 
 def time_launches(torch, fn, steps: int, warmup: int):
@@ -138,7 +173,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for HBM counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-calls", type=int, default=0, help="nsa_sel_fwd calls in the --pmc runs")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_calls,
+                            args.copy_probe_mib, COUNTERS_FILE)
+        print(json.dumps(res))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU only; --gpus must be 1", file=sys.stderr)

@@ -62,11 +62,13 @@ enum {
  *
  * Behaviour: every argument is checked on the host before any HIP call; a
  * failed check returns its NSA_SEL_ERR_* code and touches nothing.  On success
- * the work is queued asynchronously on `stream` and NSA_SEL_OK is returned;
- * the call never synchronises.  Faults inside the kernel surface at the
- * caller's next synchronisation, as for any HIP launch.  Inputs are only
- * read; outputs must not overlap inputs or each other.  Calls on different
- * streams may run concurrently; the call keeps no mutable global state.
+ * the work is queued asynchronously on `stream` (as a short sequence of
+ * kernel dispatches) and NSA_SEL_OK is returned; the call never synchronises
+ * and allocates no memory.  Faults inside the kernel surface at the caller's
+ * next synchronisation, as for any HIP launch.  Inputs are only read; outputs
+ * must not overlap inputs or each other.  Calls on different streams may run
+ * concurrently; the only global state is a per-device cache of the compute
+ * unit count, filled on the first call on each device.
  */
 int nsa_sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
                 void *O, float *LSE, int B, int M, int N, int H, int G, int D,
