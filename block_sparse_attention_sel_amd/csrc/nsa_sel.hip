@@ -42,7 +42,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
-constexpr int kWavesPerWG = 4;
+constexpr int kWavesPerWG = 5;  // 5 x 32 KiB of staging fills the CU's 160 KiB LDS
 constexpr int kThreads = kWaveSize * kWavesPerWG;
 constexpr int kNumXcd = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -60,7 +60,7 @@ struct Params {
     int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / pack)
     int wslots;         // B * G * wslots_per_bg
     int per_xcd;        // wavefront slots owned by each XCD: ceil(wslots / 8)
-    int gen_step;       // wavefront slots one XCD runs per launch (its CUs x 4)
+    int gen_step;       // wavefront slots one XCD runs per launch (its workgroup slots x waves)
     int gen;            // generation (launch) index
     float scale_log2;   // log2(e) / sqrt(D)
 };
@@ -98,7 +98,7 @@ struct IndexScan {
     __device__ __forceinline__ void load(int b) {
         base = b;
         const int j = b + lane;
-        const int v = (j < T) ? row[j] : -1;
+        const int v = (j < T) ? __builtin_nontemporal_load(&row[j]) : -1;
         val = v;
         const bool ok = v >= 0 && v <= cm && v < NB;
         mask = __ballot(ok);
@@ -513,14 +513,16 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     const int my_h = h0 + (r - my_q * p.gs);
 
     // Q^T fragments (B operand): lane l holds column l%16, head-dim slice
-    // 32*c + 8*(l/16) .. +7; columns without a query are zero.
+    // 32*c + 8*(l/16) .. +7; columns without a query are zero.  Q, O, LSE and
+    // the index rows are touched once, so they use non-temporal accesses and
+    // leave the L2 to the gathered K/V blocks.
     half8 qf[DC];
     {
         const _Float16 *qrow = p.Q + ((size_t)(b * (size_t)p.M + my_m) * p.H + (my_live ? my_h : h0)) * D;
         const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-            const half8 x = *(const half8 *)(qrow + c * 32 + q4 * 8);
+            const half8 x = __builtin_nontemporal_load((const half8 *)(qrow + c * 32 + q4 * 8));
             qf[c] = my_live ? x : zero8;
         }
     }
@@ -605,11 +607,11 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
         for (int c = 0; c < DC; ++c) {
             const half4 lo = to_half4(acc[c][0] * inv);
             const half4 hi = to_half4(acc[c][1] * inv);
-            *(half8 *)(orow + c * 32 + q4 * 8) = cat8(lo, hi);
+            __builtin_nontemporal_store(cat8(lo, hi), (half8 *)(orow + c * 32 + q4 * 8));
         }
         if (q4 == 0) {
             const float lse = l > 0.f ? m_run * kLn2 + logf(l) : -INFINITY;
-            p.LSE[((size_t)b * p.H + my_h) * p.M + my_m] = lse;
+            __builtin_nontemporal_store(lse, &p.LSE[((size_t)b * p.H + my_h) * p.M + my_m]);
         }
     }
 }
@@ -622,7 +624,7 @@ __global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
     __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
     // Generation p.gen: XCD w % 8 runs the next gen_step wavefront slots of its
-    // contiguous range, one workgroup per CU.
+    // contiguous range, filling every workgroup slot of its CUs.
     const int loc = p.gen * p.gen_step + (w / kNumXcd) * kWavesPerWG + wave;
     const int ws = (w % kNumXcd) * p.per_xcd + loc;
     if (loc >= p.per_xcd || ws >= p.wslots) return;
@@ -649,8 +651,15 @@ hipError_t launch(const Params &p, int wg_per_xcd, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// One generation fills every workgroup slot of every CU: the staging buffers
+// (K and V, one block each per wavefront) set how many workgroups fit the
+// CU's 160 KiB of LDS.
 template <int BS, int D>
-hipError_t launch_pack(const Params &p, int wg_per_xcd, hipStream_t stream) {
+hipError_t launch_pack(Params p, int cus, hipStream_t stream) {
+    constexpr int lds_per_wg = 2 * Stage<BS, D>::HALVES * 2 * kWavesPerWG;
+    constexpr int wg_per_cu = (160 * 1024 / lds_per_wg) < 4 ? (160 * 1024 / lds_per_wg) : 4;
+    const int wg_per_xcd = (cus / kNumXcd > 0 ? cus / kNumXcd : 1) * (wg_per_cu > 0 ? wg_per_cu : 1);
+    p.gen_step = wg_per_xcd * kWavesPerWG;
     if (p.pack == 4) return launch<BS, D, 4>(p, wg_per_xcd, stream);
     if (p.pack == 2) return launch<BS, D, 2>(p, wg_per_xcd, stream);
     return launch<BS, D, 1>(p, wg_per_xcd, stream);
@@ -740,14 +749,13 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     p.wslots = (int)wslots;
     p.per_xcd = (int)per_xcd;
     p.scale_log2 = kLog2e / sqrtf((float)D);
-    const int wg_per_xcd = device_cus() / kNumXcd > 0 ? device_cus() / kNumXcd : 1;
-    p.gen_step = wg_per_xcd * kWavesPerWG;
     p.gen = 0;
+    const int cus = device_cus();
 
     hipError_t e;
     if (block_size == 64)
-        e = (D == 128) ? launch_pack<64, 128>(p, wg_per_xcd, stream) : launch_pack<64, 64>(p, wg_per_xcd, stream);
+        e = (D == 128) ? launch_pack<64, 128>(p, cus, stream) : launch_pack<64, 64>(p, cus, stream);
     else
-        e = (D == 128) ? launch_pack<32, 128>(p, wg_per_xcd, stream) : launch_pack<32, 64>(p, wg_per_xcd, stream);
+        e = (D == 128) ? launch_pack<32, 128>(p, cus, stream) : launch_pack<32, 64>(p, cus, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
 }
