@@ -42,8 +42,10 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
-constexpr int kWavesPerWG = 5;  // 5 x 32 KiB of staging fills the CU's 160 KiB LDS
-constexpr int kThreads = kWaveSize * kWavesPerWG;
+// Wavefronts per workgroup: 5 (5 x 32 KiB of staging fills the CU's 160 KiB
+// of LDS), or 4 for the four-tile mode, whose state needs a SIMD to itself
+// (one wavefront per SIMD may use 512 registers).
+constexpr int waves_per_wg(int mode) { return mode == 4 ? 4 : 5; }
 constexpr int kNumXcd = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -56,8 +58,9 @@ struct Params {
     _Float16 *O;
     float *LSE;
     int B, M, N, H, G, T, gs, NB;
-    int pack;           // queries per wavefront (1, 2 or 4; see nsa_sel_fwd)
-    int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / pack)
+    int pack;           // queries per 16-column MFMA tile (1, 2 or 4; see nsa_sel_fwd)
+    int mode;           // 0: cursor merge, one tile; 1/2/4: register merge with that many tiles
+    int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / queries per wavefront)
     int wslots;         // B * G * wslots_per_bg
     int per_xcd;        // wavefront slots owned by each XCD: ceil(wslots / 8)
     int gen_step;       // wavefront slots one XCD runs per launch (its workgroup slots x waves)
@@ -395,6 +398,82 @@ struct Stage {
     }
 };
 
+// The queries of one wavefront slot: QW consecutive positions m0 .. m0+nq-1
+// of one (b, g).  A merger yields the union of their counted index entries in
+// ascending block order (for any row order) together with the mask of the
+// queries whose rows hold that block.
+
+// Streams each row through an IndexScan; handles any T.
+template <int QW, int BS>
+struct CursorMerger {
+    Cursor c[QW];
+
+    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane) {
+#pragma unroll
+        for (int k = 0; k < QW; ++k) {
+            const int mk = m0 + (k < nq ? k : 0);
+            c[k].init(p.idx + ((size_t)(b * (size_t)p.M + mk) * p.G + g) * p.T, p.T, mk / BS, p.NB, lane,
+                      k < nq);
+        }
+    }
+    __device__ __forceinline__ int next(unsigned &active) { return merge_next<QW>(c, active); }
+};
+
+// Wave-wide reductions over 64 lanes: DPP prefix within each 16-lane row,
+// then the four row results.
+__device__ __forceinline__ int wave_min(int x) {
+    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x111, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x112, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x114, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x118, 0xf, 0xf, false));
+    const int a = __builtin_amdgcn_readlane(x, 15), b = __builtin_amdgcn_readlane(x, 31);
+    const int c = __builtin_amdgcn_readlane(x, 47), d = __builtin_amdgcn_readlane(x, 63);
+    return min(min(a, b), min(c, d));
+}
+__device__ __forceinline__ unsigned wave_or(unsigned x) {
+    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);
+    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);
+    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);
+    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);
+    return (unsigned)(__builtin_amdgcn_readlane((int)x, 15) | __builtin_amdgcn_readlane((int)x, 31) |
+                      __builtin_amdgcn_readlane((int)x, 47) | __builtin_amdgcn_readlane((int)x, 63));
+}
+
+// Holds all QW*T entries (QW*T <= 128) in two registers per lane: entry
+// e = lane + 64*v belongs to query e / T.  Each step takes the smallest
+// remaining counted block and retires every entry equal to it, so a block
+// repeated within a row, or shared by several rows, is returned once.
+template <int QW, int BS>
+struct RegMerger {
+    int e[2];
+    unsigned bit[2];
+
+    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            const int ent = lane + 64 * v;
+            const int qi = ent / p.T;
+            const bool slot = ent < QW * p.T && qi < nq;
+            const int m = m0 + (slot ? qi : 0);
+            const int32_t *row = p.idx + ((size_t)(b * (size_t)p.M + m) * p.G + g) * p.T;
+            const int t = slot ? __builtin_nontemporal_load(&row[ent - qi * p.T]) : -1;
+            const bool ok = t >= 0 && t <= m / BS && t < p.NB;
+            e[v] = ok ? t : INT_MAX;
+            bit[v] = slot ? 1u << qi : 0u;
+        }
+    }
+    __device__ __forceinline__ int next(unsigned &active) {
+        const int t = wave_min(min(e[0], e[1]));
+        active = 0;
+        if (t == INT_MAX) return kDone;
+        const bool h0 = e[0] == t, h1 = e[1] == t;
+        active = wave_or((h0 ? bit[0] : 0u) | (h1 ? bit[1] : 0u));
+        e[0] = h0 ? INT_MAX : e[0];
+        e[1] = h1 ? INT_MAX : e[1];
+        return t;
+    }
+};
+
 // s_waitcnt immediate for "at most n vector-memory ops outstanding"
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -494,36 +573,50 @@ __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 
 // One wavefront slot: the packed queries m0 .. m0 + nq - 1 of one (b, g),
 // from index rows to stored O and LSE.  kbuf/vbuf are the wavefront's LDS
 // staging buffers.
-template <int BS, int D, int PACK>
+// One wavefront slot: QW = PACK * NT consecutive queries m0 .. m0+nq-1 of one
+// (b, g), from index rows to stored O and LSE.  The wavefront's MFMA columns
+// form NT tiles of 16; tile nt carries queries nt*PACK .. nt*PACK+PACK-1, gs
+// heads each.  Every block of the merged sequence is staged once (kbuf/vbuf
+// are the wavefront's LDS buffers) and multiplied only for the tiles whose
+// queries selected it.
+template <int BS, int D, int PACK, int NT, class Merger>
 __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf) {
     constexpr int DC = D / 32;
-    // Wavefront slot -> (b, g) and the queries m0 .. m0 + nq - 1 it packs.
+    constexpr int KT = BS / 16;
+    constexpr int QW = PACK * NT;
     const int bg = ws / p.wslots_per_bg;
-    const int m0 = (ws - bg * p.wslots_per_bg) * PACK;
-    const int nq = min(PACK, p.M - m0);
+    const int m0 = (ws - bg * p.wslots_per_bg) * QW;
+    const int nq = min(QW, p.M - m0);
     const int g = bg % p.G;
     const int b = bg / p.G;
     const int r = lane & 15;
     const int q4 = lane >> 4;
     const int h0 = g * p.gs;
-    // MFMA column r carries head h0 + r % gs of query m0 + r / gs.
-    const int my_q = r / p.gs;
-    const bool my_live = my_q < nq;
-    const int my_m = m0 + (my_live ? my_q : 0);
-    const int my_h = h0 + (r - my_q * p.gs);
+    // Column r of tile nt carries head h0 + r % gs of query nt*PACK + r / gs.
+    const int q_in_tile = r / p.gs;
+    const int my_h = h0 + (r - q_in_tile * p.gs);
+    bool live[NT];
+    int my_m[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int qi = nt * PACK + q_in_tile;
+        live[nt] = q_in_tile < PACK && qi < nq;
+        my_m[nt] = m0 + (live[nt] ? qi : 0);
+    }
 
     // Q^T fragments (B operand): lane l holds column l%16, head-dim slice
     // 32*c + 8*(l/16) .. +7; columns without a query are zero.  Q, O, LSE and
     // the index rows are touched once, so they use non-temporal accesses and
     // leave the L2 to the gathered K/V blocks.
-    half8 qf[DC];
-    {
-        const _Float16 *qrow = p.Q + ((size_t)(b * (size_t)p.M + my_m) * p.H + (my_live ? my_h : h0)) * D;
+    half8 qf[NT][DC];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const _Float16 *qrow = p.Q + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + (live[nt] ? my_h : h0)) * D;
         const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
             const half8 x = __builtin_nontemporal_load((const half8 *)(qrow + c * 32 + q4 * 8));
-            qf[c] = my_live ? x : zero8;
+            qf[nt][c] = live[nt] ? x : zero8;
         }
     }
 
@@ -531,22 +624,21 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     const _Float16 *Kg = p.K + ((size_t)b * p.N * p.G + g) * D;
     const _Float16 *Vg = p.V + ((size_t)b * p.N * p.G + g) * D;
 
-    Cursor cur[PACK];
-#pragma unroll
-    for (int k = 0; k < PACK; ++k) {
-        const int mk = m0 + (k < nq ? k : 0);
-        cur[k].init(p.idx + ((size_t)(b * (size_t)p.M + mk) * p.G + g) * p.T, p.T, mk / BS, p.NB, lane,
-                    k < nq);
-    }
-    const unsigned all_live = (1u << nq) - 1u;
+    Merger mg;
+    mg.init(p, b, g, m0, nq, lane);
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    float4v acc[DC][2];
+    float m_run[NT], l_run[NT], alpha[NT];
+    float4v acc[NT][DC][2];
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-        acc[c][0] = float4v{0.f, 0.f, 0.f, 0.f};
-        acc[c][1] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = -INFINITY;
+        l_run[nt] = 0.f;
+        alpha[nt] = 1.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            acc[nt][c][0] = float4v{0.f, 0.f, 0.f, 0.f};
+            acc[nt][c][1] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
     }
 
     constexpr int NI = Stage<BS, D>::NI;
@@ -557,6 +649,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
         const size_t bytes = (kv_elems - first) * 2;
         st.init(Kg, Vg, (unsigned)(bytes < 0xFFFFFFFFu ? bytes : 0xFFFFFFFFu), row_stride, p.N, lane);
     }
+    const unsigned tile_bits = (1u << PACK) - 1u;
 
     // Pipeline over the merged block sequence: while block t0 is computed,
     // the copies of the next block t1 into LDS are in flight -- its K copy
@@ -564,71 +657,88 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     // soon as t0's V operands are, so each copy overlaps about one block of
     // math.  Loads complete in issue order, so each wait names how many later
     // loads may still be pending.
-    half8 kf[BS / 16][D / 32];
-    half4 vt[BS / 32][D / 32][2][2];
-    half4 pf[BS / 16];
+    half8 kf[KT][DC];
+    half4 vt[BS / 32][DC][2][2];
+    half4 pf[NT][KT];
     unsigned a0, a1;
-    int t0 = merge_next(cur, a0);
+    int t0 = mg.next(a0);
     if (t0 != kDone) {
         st.issue(st.rk, kbuf, t0, lane);
         st.issue(st.rv, vbuf, t0, lane);
     }
     while (t0 != kDone) {
-        const int t1 = merge_next(cur, a1);
+        const int t1 = mg.next(a1);
         const bool has1 = t1 != kDone;
         __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K(t0) landed; V(t0) may be pending
         Stage<BS, D>::read(kf, kbuf, r, q4);
         if (has1) st.issue(st.rk, kbuf, t1, lane);
         const int key0 = t0 * BS;
-        const bool causal = (key0 + BS - 1 > m0) || (key0 + BS > p.N);
-        const bool col_mask = a0 != all_live;
-        const bool col_on = my_live && ((a0 >> my_q) & 1u);
-        float alpha;
-        score_block<BS, D>(kf, qf, key0, causal, col_mask, col_on, my_m, p.N, p.scale_log2, m_run, l_run,
-                           alpha, pf, q4);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const unsigned tb = (a0 >> (nt * PACK)) & tile_bits;
+            if (tb == 0) continue;  // wave-uniform: no query of this tile selected t0
+            const int first_m = m0 + nt * PACK;
+            const bool causal = (key0 + BS - 1 > first_m) || (key0 + BS > p.N);
+            const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
+            score_block<BS, D>(kf, qf[nt], key0, causal, true, col_on, my_m[nt], p.N, p.scale_log2, m_run[nt],
+                               l_run[nt], alpha[nt], pf[nt], q4);
+        }
         if (has1)
             __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(t0) landed; K(t1) may be pending
         else
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
         Stage<BS, D>::read_vt(vt, vbuf, lane);
         if (has1) st.issue(st.rv, vbuf, t1, lane);
-        accumulate_block<BS, D>(vt, pf, alpha, acc);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            if (((a0 >> (nt * PACK)) & tile_bits) == 0) continue;
+            accumulate_block<BS, D>(vt, pf[nt], alpha[nt], acc[nt]);
+        }
         t0 = t1;
         a0 = a1;
     }
 
     // Epilogue: total row sum over the 4 lanes of a column, normalise, store.
-    float l = l_run + __shfl_xor(l_run, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-    if (my_live) {
-        _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + my_m) * p.H + my_h) * D;
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            const half4 lo = to_half4(acc[c][0] * inv);
-            const half4 hi = to_half4(acc[c][1] * inv);
-            __builtin_nontemporal_store(cat8(lo, hi), (half8 *)(orow + c * 32 + q4 * 8));
-        }
-        if (q4 == 0) {
-            const float lse = l > 0.f ? m_run * kLn2 + logf(l) : -INFINITY;
-            __builtin_nontemporal_store(lse, &p.LSE[((size_t)b * p.H + my_h) * p.M + my_m]);
+    for (int nt = 0; nt < NT; ++nt) {
+        float l = l_run[nt] + __shfl_xor(l_run[nt], 16);
+        l += __shfl_xor(l, 32);
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        if (live[nt]) {
+            _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + my_h) * D;
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                const half4 lo = to_half4(acc[nt][c][0] * inv);
+                const half4 hi = to_half4(acc[nt][c][1] * inv);
+                __builtin_nontemporal_store(cat8(lo, hi), (half8 *)(orow + c * 32 + q4 * 8));
+            }
+            if (q4 == 0) {
+                const float lse = l > 0.f ? m_run[nt] * kLn2 + logf(l) : -INFINITY;
+                __builtin_nontemporal_store(lse, &p.LSE[((size_t)b * p.H + my_h) * p.M + my_m[nt]]);
+            }
         }
     }
 }
 
-template <int BS, int D, int PACK>
-__global__ __launch_bounds__(kThreads) void nsa_sel_fwd_kernel(Params p) {
+// MODE 0: rows streamed through cursors (any T), one tile.  MODE 1/2/4:
+// rows held in registers, NT = MODE tiles.
+template <int BS, int D, int PACK, int MODE>
+__global__ __launch_bounds__(kWaveSize * waves_per_wg(MODE)) void nsa_sel_fwd_kernel(Params p) {
+    constexpr int WAVES = waves_per_wg(MODE);
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x;
-    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
-    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[kWavesPerWG][Stage<BS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<BS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<BS, D>::HALVES];
     // Generation p.gen: XCD w % 8 runs the next gen_step wavefront slots of its
     // contiguous range, filling every workgroup slot of its CUs.
-    const int loc = p.gen * p.gen_step + (w / kNumXcd) * kWavesPerWG + wave;
+    const int loc = p.gen * p.gen_step + (w / kNumXcd) * WAVES + wave;
     const int ws = (w % kNumXcd) * p.per_xcd + loc;
     if (loc >= p.per_xcd || ws >= p.wslots) return;
-    run_slot<BS, D, PACK>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+    if constexpr (MODE == 0)
+        run_slot<BS, D, PACK, 1, CursorMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+    else
+        run_slot<BS, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
 }
 
 bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
@@ -639,30 +749,47 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
 // Queues the generations in order on the stream.  Every generation starts
 // all its workgroups together and ends before the next starts, so the units
 // resident on an XCD sweep key space in step and share its L2.
-template <int BS, int D, int PACK>
+template <int BS, int D, int PACK, int MODE>
 hipError_t launch(const Params &p, int wg_per_xcd, hipStream_t stream) {
     const int gens = (p.per_xcd + p.gen_step - 1) / p.gen_step;
     Params q = p;
     for (int g = 0; g < gens; ++g) {
         q.gen = g;
-        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, D, PACK>), dim3(wg_per_xcd * kNumXcd), dim3(kThreads), 0, stream,
-                           q);
+        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, D, PACK, MODE>), dim3(wg_per_xcd * kNumXcd),
+                           dim3(kWaveSize * waves_per_wg(MODE)), 0, stream, q);
     }
     return hipGetLastError();
 }
 
 // One generation fills every workgroup slot of every CU: the staging buffers
 // (K and V, one block each per wavefront) set how many workgroups fit the
-// CU's 160 KiB of LDS.
+// CU's 160 KiB of LDS (the four-tile mode also needs one wavefront per SIMD).
+template <int BS, int D, int PACK, int MODE>
+hipError_t launch_sized(Params p, int cus, hipStream_t stream) {
+    constexpr int WAVES = waves_per_wg(MODE);
+    constexpr int lds_per_wg = 2 * Stage<BS, D>::HALVES * 2 * WAVES;
+    constexpr int by_lds = 160 * 1024 / lds_per_wg;
+    constexpr int wg_per_cu = MODE == 4 ? 1 : (by_lds < 4 ? (by_lds > 0 ? by_lds : 1) : 4);
+    const int wg_per_xcd = (cus / kNumXcd > 0 ? cus / kNumXcd : 1) * wg_per_cu;
+    p.gen_step = wg_per_xcd * WAVES;
+    return launch<BS, D, PACK, MODE>(p, wg_per_xcd, stream);
+}
+
+template <int BS, int D, int PACK>
+hipError_t launch_mode(const Params &p, int cus, hipStream_t stream) {
+    switch (p.mode) {
+        case 4: return launch_sized<BS, D, PACK, 4>(p, cus, stream);
+        case 2: return launch_sized<BS, D, PACK, 2>(p, cus, stream);
+        case 1: return launch_sized<BS, D, PACK, 1>(p, cus, stream);
+        default: return launch_sized<BS, D, PACK, 0>(p, cus, stream);
+    }
+}
+
 template <int BS, int D>
-hipError_t launch_pack(Params p, int cus, hipStream_t stream) {
-    constexpr int lds_per_wg = 2 * Stage<BS, D>::HALVES * 2 * kWavesPerWG;
-    constexpr int wg_per_cu = (160 * 1024 / lds_per_wg) < 4 ? (160 * 1024 / lds_per_wg) : 4;
-    const int wg_per_xcd = (cus / kNumXcd > 0 ? cus / kNumXcd : 1) * (wg_per_cu > 0 ? wg_per_cu : 1);
-    p.gen_step = wg_per_xcd * kWavesPerWG;
-    if (p.pack == 4) return launch<BS, D, 4>(p, wg_per_xcd, stream);
-    if (p.pack == 2) return launch<BS, D, 2>(p, wg_per_xcd, stream);
-    return launch<BS, D, 1>(p, wg_per_xcd, stream);
+hipError_t launch_pack(const Params &p, int cus, hipStream_t stream) {
+    if (p.pack == 4) return launch_mode<BS, D, 4>(p, cus, stream);
+    if (p.pack == 2) return launch_mode<BS, D, 2>(p, cus, stream);
+    return launch_mode<BS, D, 1>(p, cus, stream);
 }
 
 // Compute units of the current device, cached per device (the first call on a
@@ -715,7 +842,22 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     // Queries per wavefront: as many whole groups of gs heads as fit the 16
     // MFMA columns, rounded down to 1, 2 or 4.
     const int pack = (16 / gs) >= 4 ? 4 : (16 / gs) >= 2 ? 2 : 1;
-    const int64_t wslots_per_bg = ((int64_t)M + pack - 1) / pack;
+    const int cus = device_cus();
+    // Tiles per wavefront (measured on MI355X): the most whose index rows fit
+    // in two registers per lane (else one tile with streamed rows), at most
+    // two for bs=32 (the four-tile mode runs one wavefront per SIMD, too few
+    // for 16 KiB blocks), and fewer while the grid would give a CU less than
+    // 8 wavefront slots.
+    int mode = 0;
+    for (int nt = block_size == 32 ? 2 : 4; nt >= 1; nt /= 2) {
+        if ((int64_t)pack * nt * T <= 128) {
+            mode = nt;
+            break;
+        }
+    }
+    while (mode > 1 && (int64_t)B * G * ((M + pack * mode - 1) / (pack * mode)) < 8LL * cus) mode /= 2;
+    const int qw = pack * (mode > 0 ? mode : 1);
+    const int64_t wslots_per_bg = ((int64_t)M + qw - 1) / qw;
     const int64_t wslots = (int64_t)B * G * wslots_per_bg;
     const int64_t per_xcd = (wslots + kNumXcd - 1) / kNumXcd;
     // Element counts must fit the 64-bit offsets; unit ids and the grid use int.
@@ -745,12 +887,12 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     p.B = B; p.M = M; p.N = N; p.H = H; p.G = G; p.T = T; p.gs = gs;
     p.NB = (N + block_size - 1) / block_size;
     p.pack = pack;
+    p.mode = mode;
     p.wslots_per_bg = (int)wslots_per_bg;
     p.wslots = (int)wslots;
     p.per_xcd = (int)per_xcd;
     p.scale_log2 = kLog2e / sqrtf((float)D);
     p.gen = 0;
-    const int cus = device_cus();
 
     hipError_t e;
     if (block_size == 64)
