@@ -42,10 +42,10 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
-// Wavefronts per workgroup: 5 (5 x 32 KiB of staging fills the CU's 160 KiB
-// of LDS), or 4 for the four-tile mode, whose state needs a SIMD to itself
-// (one wavefront per SIMD may use 512 registers).
-constexpr int waves_per_wg(int mode) { return mode == 4 ? 4 : 5; }
+// Wavefronts per workgroup: with 32-key stages (16 KiB per wavefront at
+// D = 128) two 4-wavefront workgroups share a CU, two wavefronts per SIMD;
+// with 64-key stages five wavefronts fill the CU's 160 KiB of LDS.
+constexpr int waves_per_wg(int sbs) { return sbs == 32 ? 4 : 5; }
 constexpr int kNumXcd = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -59,7 +59,7 @@ struct Params {
     float *LSE;
     int B, M, N, H, G, T, gs, NB;
     int pack;           // queries per 16-column MFMA tile (1, 2 or 4; see nsa_sel_fwd)
-    int mode;           // 0: cursor merge, one tile; 1/2/4: register merge with that many tiles
+    int mode;           // 0: cursor merge, one tile; 1/2: register merge with that many tiles
     int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / queries per wavefront)
     int wslots;         // B * G * wslots_per_bg
     int per_xcd;        // wavefront slots owned by each XCD: ceil(wslots / 8)
@@ -579,10 +579,15 @@ __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 
 // heads each.  Every block of the merged sequence is staged once (kbuf/vbuf
 // are the wavefront's LDS buffers) and multiplied only for the tiles whose
 // queries selected it.
-template <int BS, int D, int PACK, int NT, class Merger>
+//
+// SPLIT > 1 stages and computes each selected block as SPLIT consecutive
+// sub-blocks of SBS = BS / SPLIT keys: half the LDS per wavefront, so twice as
+// many wavefronts fit a CU.
+template <int BS, int SPLIT, int D, int PACK, int NT, class Merger>
 __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf) {
+    constexpr int SBS = BS / SPLIT;
     constexpr int DC = D / 32;
-    constexpr int KT = BS / 16;
+    constexpr int KT = SBS / 16;
     constexpr int QW = PACK * NT;
     const int bg = ws / p.wslots_per_bg;
     const int m0 = (ws - bg * p.wslots_per_bg) * QW;
@@ -641,8 +646,8 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
         }
     }
 
-    constexpr int NI = Stage<BS, D>::NI;
-    Stage<BS, D> st;
+    constexpr int NI = Stage<SBS, D>::NI;
+    Stage<SBS, D> st;
     {
         const size_t kv_elems = (size_t)p.B * p.N * p.G * D;
         const size_t first = ((size_t)b * p.N * p.G + g) * D;
@@ -651,50 +656,58 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     }
     const unsigned tile_bits = (1u << PACK) - 1u;
 
-    // Pipeline over the merged block sequence: while block t0 is computed,
-    // the copies of the next block t1 into LDS are in flight -- its K copy
-    // is issued as soon as t0's K fragments are in registers, its V copy as
-    // soon as t0's V operands are, so each copy overlaps about one block of
-    // math.  Loads complete in issue order, so each wait names how many later
-    // loads may still be pending.
+    // Pipeline over the merged sequence of sub-blocks (block t, part h): while
+    // sub-block s0 is computed, the copies of the next one s1 into LDS are in
+    // flight -- its K copy is issued as soon as s0's K fragments are in
+    // registers, its V copy as soon as s0's V operands are, so each copy
+    // overlaps about one sub-block of math.  Loads complete in issue order,
+    // so each wait names how many later loads may still be pending.
     half8 kf[KT][DC];
-    half4 vt[BS / 32][DC][2][2];
+    half4 vt[SBS / 32][DC][2][2];
     half4 pf[NT][KT];
     unsigned a0, a1;
-    int t0 = mg.next(a0);
-    if (t0 != kDone) {
-        st.issue(st.rk, kbuf, t0, lane);
-        st.issue(st.rv, vbuf, t0, lane);
+    const int t_first = mg.next(a0);
+    int s0 = t_first == kDone ? kDone : t_first * SPLIT;  // sub-block index = key0 / SBS
+    if (s0 != kDone) {
+        st.issue(st.rk, kbuf, s0, lane);
+        st.issue(st.rv, vbuf, s0, lane);
     }
-    while (t0 != kDone) {
-        const int t1 = mg.next(a1);
-        const bool has1 = t1 != kDone;
-        __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K(t0) landed; V(t0) may be pending
-        Stage<BS, D>::read(kf, kbuf, r, q4);
-        if (has1) st.issue(st.rk, kbuf, t1, lane);
-        const int key0 = t0 * BS;
+    while (s0 != kDone) {
+        int s1;
+        if ((s0 + 1) % SPLIT != 0) {  // next part of the same block, same queries
+            s1 = s0 + 1;
+            a1 = a0;
+        } else {
+            const int t1 = mg.next(a1);
+            s1 = t1 == kDone ? kDone : t1 * SPLIT;
+        }
+        const bool has1 = s1 != kDone;
+        __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K(s0) landed; V(s0) may be pending
+        Stage<SBS, D>::read(kf, kbuf, r, q4);
+        if (has1) st.issue(st.rk, kbuf, s1, lane);
+        const int key0 = s0 * SBS;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const unsigned tb = (a0 >> (nt * PACK)) & tile_bits;
-            if (tb == 0) continue;  // wave-uniform: no query of this tile selected t0
+            if (tb == 0) continue;  // wave-uniform: no query of this tile selected the block
             const int first_m = m0 + nt * PACK;
-            const bool causal = (key0 + BS - 1 > first_m) || (key0 + BS > p.N);
+            const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
             const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
-            score_block<BS, D>(kf, qf[nt], key0, causal, true, col_on, my_m[nt], p.N, p.scale_log2, m_run[nt],
-                               l_run[nt], alpha[nt], pf[nt], q4);
+            score_block<SBS, D>(kf, qf[nt], key0, causal, true, col_on, my_m[nt], p.N, p.scale_log2, m_run[nt],
+                                l_run[nt], alpha[nt], pf[nt], q4);
         }
         if (has1)
-            __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(t0) landed; K(t1) may be pending
+            __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(s0) landed; K(s1) may be pending
         else
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
-        Stage<BS, D>::read_vt(vt, vbuf, lane);
-        if (has1) st.issue(st.rv, vbuf, t1, lane);
+        Stage<SBS, D>::read_vt(vt, vbuf, lane);
+        if (has1) st.issue(st.rv, vbuf, s1, lane);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (((a0 >> (nt * PACK)) & tile_bits) == 0) continue;
-            accumulate_block<BS, D>(vt, pf[nt], alpha[nt], acc[nt]);
+            accumulate_block<SBS, D>(vt, pf[nt], alpha[nt], acc[nt]);
         }
-        t0 = t1;
+        s0 = s1;
         a0 = a1;
     }
 
@@ -722,23 +735,25 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
 
 // MODE 0: rows streamed through cursors (any T), one tile.  MODE 1/2/4:
 // rows held in registers, NT = MODE tiles.
-template <int BS, int D, int PACK, int MODE>
-__global__ __launch_bounds__(kWaveSize * waves_per_wg(MODE)) void nsa_sel_fwd_kernel(Params p) {
-    constexpr int WAVES = waves_per_wg(MODE);
+template <int BS, int SPLIT, int D, int PACK, int MODE>
+__global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_fwd_kernel(Params p) {
+    constexpr int SBS = BS / SPLIT;
+    constexpr int WAVES = waves_per_wg(SBS);
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w = blockIdx.x;
-    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<BS, D>::HALVES];
-    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<BS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
     // Generation p.gen: XCD w % 8 runs the next gen_step wavefront slots of its
     // contiguous range, filling every workgroup slot of its CUs.
     const int loc = p.gen * p.gen_step + (w / kNumXcd) * WAVES + wave;
     const int ws = (w % kNumXcd) * p.per_xcd + loc;
     if (loc >= p.per_xcd || ws >= p.wslots) return;
     if constexpr (MODE == 0)
-        run_slot<BS, D, PACK, 1, CursorMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+        run_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
     else
-        run_slot<BS, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+        run_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, ws, lane, kbuf_all[wave],
+                                                                         vbuf_all[wave]);
 }
 
 bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
@@ -749,14 +764,14 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
 // Queues the generations in order on the stream.  Every generation starts
 // all its workgroups together and ends before the next starts, so the units
 // resident on an XCD sweep key space in step and share its L2.
-template <int BS, int D, int PACK, int MODE>
+template <int BS, int SPLIT, int D, int PACK, int MODE>
 hipError_t launch(const Params &p, int wg_per_xcd, hipStream_t stream) {
     const int gens = (p.per_xcd + p.gen_step - 1) / p.gen_step;
     Params q = p;
     for (int g = 0; g < gens; ++g) {
         q.gen = g;
-        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, D, PACK, MODE>), dim3(wg_per_xcd * kNumXcd),
-                           dim3(kWaveSize * waves_per_wg(MODE)), 0, stream, q);
+        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE>), dim3(wg_per_xcd * kNumXcd),
+                           dim3(kWaveSize * waves_per_wg(BS / SPLIT)), 0, stream, q);
     }
     return hipGetLastError();
 }
@@ -764,24 +779,25 @@ hipError_t launch(const Params &p, int wg_per_xcd, hipStream_t stream) {
 // One generation fills every workgroup slot of every CU: the staging buffers
 // (K and V, one block each per wavefront) set how many workgroups fit the
 // CU's 160 KiB of LDS (the four-tile mode also needs one wavefront per SIMD).
-template <int BS, int D, int PACK, int MODE>
+template <int BS, int SPLIT, int D, int PACK, int MODE>
 hipError_t launch_sized(Params p, int cus, hipStream_t stream) {
-    constexpr int WAVES = waves_per_wg(MODE);
-    constexpr int lds_per_wg = 2 * Stage<BS, D>::HALVES * 2 * WAVES;
+    constexpr int WAVES = waves_per_wg(BS / SPLIT);
+    constexpr int lds_per_wg = 2 * Stage<BS / SPLIT, D>::HALVES * 2 * WAVES;
     constexpr int by_lds = 160 * 1024 / lds_per_wg;
-    constexpr int wg_per_cu = MODE == 4 ? 1 : (by_lds < 4 ? (by_lds > 0 ? by_lds : 1) : 4);
+    constexpr int wg_per_cu = by_lds < 4 ? (by_lds > 0 ? by_lds : 1) : 4;
     const int wg_per_xcd = (cus / kNumXcd > 0 ? cus / kNumXcd : 1) * wg_per_cu;
     p.gen_step = wg_per_xcd * WAVES;
-    return launch<BS, D, PACK, MODE>(p, wg_per_xcd, stream);
+    return launch<BS, SPLIT, D, PACK, MODE>(p, wg_per_xcd, stream);
 }
 
+// 64-key blocks are always staged as two 32-key halves.
 template <int BS, int D, int PACK>
 hipError_t launch_mode(const Params &p, int cus, hipStream_t stream) {
+    constexpr int SPLIT = BS / 32;
     switch (p.mode) {
-        case 4: return launch_sized<BS, D, PACK, 4>(p, cus, stream);
-        case 2: return launch_sized<BS, D, PACK, 2>(p, cus, stream);
-        case 1: return launch_sized<BS, D, PACK, 1>(p, cus, stream);
-        default: return launch_sized<BS, D, PACK, 0>(p, cus, stream);
+        case 2: return launch_sized<BS, SPLIT, D, PACK, 2>(p, cus, stream);
+        case 1: return launch_sized<BS, SPLIT, D, PACK, 1>(p, cus, stream);
+        default: return launch_sized<BS, SPLIT, D, PACK, 0>(p, cus, stream);
     }
 }
 
@@ -843,13 +859,13 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     // MFMA columns, rounded down to 1, 2 or 4.
     const int pack = (16 / gs) >= 4 ? 4 : (16 / gs) >= 2 ? 2 : 1;
     const int cus = device_cus();
-    // Tiles per wavefront (measured on MI355X): the most whose index rows fit
-    // in two registers per lane (else one tile with streamed rows), at most
-    // two for bs=32 (the four-tile mode runs one wavefront per SIMD, too few
-    // for 16 KiB blocks), and fewer while the grid would give a CU less than
-    // 8 wavefront slots.
+    // Tiles per wavefront (measured on MI355X): up to two, while the index
+    // rows of the wavefront's queries fit in two registers per lane (else one
+    // tile with streamed rows), and fewer while the grid would give a CU less
+    // than 8 wavefront slots.  Two tiles keep a wavefront within 256
+    // registers, so two wavefronts share each SIMD.
     int mode = 0;
-    for (int nt = block_size == 32 ? 2 : 4; nt >= 1; nt /= 2) {
+    for (int nt = 2; nt >= 1; nt /= 2) {
         if ((int64_t)pack * nt * T <= 128) {
             mode = nt;
             break;
