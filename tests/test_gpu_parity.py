@@ -152,6 +152,48 @@ def test_parity_every_instantiation(torch_cuda, shape):
     _check_full(O.cpu().numpy(), L.cpu().numpy(), Or, Lr)
 
 
+# Shapes large enough that the library picks its two-tile wavefronts (the
+# grid-size rule only drops to one tile for small problems), covering each
+# queries-per-tile packing (1, 2, 4), both block sizes and both head dims.
+TWO_TILE_SHAPES = [
+    # B, M, N, H, G, D, bs, T
+    (1, 4096, 4096, 16, 8, 64, 64, 8),      # gs = 2 -> 4 queries per tile
+    (2, 2048, 2048, 8, 8, 64, 32, 16),      # gs = 1 -> 4 queries per tile
+    (1, 4096, 4096, 32, 2, 64, 64, 8),      # gs = 16 -> 1 query per tile
+    (1, 4096, 4096, 40, 8, 128, 64, 8),     # gs = 5 -> 2 queries per tile, 6 padding columns
+    (1, 4096, 4096, 48, 8, 128, 32, 12),    # gs = 6, bs = 32
+    (1, 4000, 4000, 16, 8, 128, 64, 8),     # ragged last block (N % bs = 32)
+    (1, 3000, 4030, 16, 8, 64, 32, 8),      # M < N, ragged last block
+]
+
+
+def _noisy_rows(cfg, rng):
+    """The uniform rule's rows, shuffled, with padding, future and
+    out-of-range entries in place of some of the -1 slots."""
+    idx = block_indices(cfg).copy()
+    B, M, G, T = idx.shape
+    c = (np.arange(M) // cfg.block_size)[None, :, None, None]
+    junk = np.stack([np.full_like(idx, -3), np.broadcast_to(c + 1, idx.shape), np.full_like(idx, cfg.NB + 2)])
+    pick = rng.integers(0, 3, size=idx.shape)
+    filler = np.take_along_axis(junk, pick[None], axis=0)[0]
+    idx = np.where((idx < 0) & (rng.random(idx.shape) < 0.7), filler, idx)
+    perm = np.argsort(rng.random(idx.shape), axis=-1)
+    return np.ascontiguousarray(np.take_along_axis(idx, perm, axis=-1)).astype(np.int32)
+
+
+@pytest.mark.parametrize("shape", TWO_TILE_SHAPES)
+def test_parity_two_tile_wavefronts(torch_cuda, shape):
+    import oracle
+    B, M, N, H, G, D, bs, T = shape
+    _say(f"case two-tile shape={shape}")
+    cfg = Config("t", B=B, M=M, N=N, H=H, G=G, D=D, block_size=bs, T=T, seed=sum(shape))
+    q, k, v, _ = make_inputs(cfg)
+    idx = _noisy_rows(cfg, np.random.default_rng(sum(shape)))
+    O, L = _gpu_run(torch_cuda, q, k, v, idx, bs)
+    Or, Lr = oracle.oracle_full(q, k, v, idx, bs)
+    _check_full(O.cpu().numpy(), L.cpu().numpy(), Or, Lr)
+
+
 def test_padding_and_invalid_entries_are_bitwise_invisible(torch_cuda):
     torch = torch_cuda
     cfg = CONFIGS["64k"].with_(M=2048, N=2048)
