@@ -3,9 +3,10 @@
 One step is one nsa_sel_fwd launch over the whole workload (all (b, m, g)
 units of the config) with inputs already resident in HBM.  Prints ONE JSON
 line: effective TFLOP/s as ``value``, plus ms per step, gathered-KV GB/s, the
-roofline of the kernel (HBM-bound on gathered bytes), the same kernel with
-every causal block selected (dense mode) and the fp64 CPU oracle timed on a
-bounded sample of the same workload.
+roofline of the kernel (HBM-bound on gathered bytes), cold-cache timings, the
+gather-ceiling probe (the kernel's block-gather stream alone), the MFMA
+utilisation, the same kernel with every causal block selected (dense mode) and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 
 Work counts per launch (exact, from the index rows):
   gathered bytes  = sum over units of (counted blocks) * bs * D * 2 B * 2 (K and V)
@@ -31,7 +32,9 @@ from block_sparse_attention_sel_amd.inputs import CONFIGS, Config, block_indices
 HBM_PEAK_GBPS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "nsa_sel_fwd_64k_hbm_counters.json")
-KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_sel_amd", "csrc", "nsa_sel.hip")
+# The forward kernel's sources: the counters in COUNTERS_FILE hold for this exact text.
+KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_sel_amd", "csrc", f)
+               for f in ("nsa_sel.hip", "nsa_sel_common.h")]
 
 
 def work_counts(cfg: Config, idx: np.ndarray):
@@ -59,7 +62,10 @@ def work_counts(cfg: Config, idx: np.ndarray):
 
 
 def _kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 def _traffic():
@@ -129,6 +135,50 @@ def time_launches(torch, fn, steps: int, warmup: int):
     return wall_ms, float(np.mean(ev)), float(np.min(ev))
 
 
+def time_cold(torch, fn, steps: int, flush_mib: int = 1024):
+    """Times `steps` calls one by one with HIP events, writing a flush_mib
+    buffer before each (outside the timed region) so that no K/V line is left
+    in the L2s or the 256 MB Infinity Cache.  Returns (median, min) ms."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda")
+    ev = []
+    for _ in range(steps):
+        scratch.zero_()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ev.append(a.elapsed_time(b))
+    del scratch
+    return float(np.median(ev)), float(np.min(ev))
+
+
+def slot_blocks(idx: np.ndarray, bs: int, N: int, qps: int) -> int:
+    """Sum over groups of qps consecutive queries of one (b, g), from m = 0, of
+    the number of distinct counted blocks in their rows: the blocks a
+    wavefront slot of qps queries stages (qps = the slot's queries), or the
+    (tile, block) pairs its MFMAs run (qps = queries per 16-column tile)."""
+    B, M, G, T = idx.shape
+    NB = -(-N // bs)
+    total = 0
+    step = max(1, (1 << 22) // max(1, G * T))     # bounded temporaries
+    step -= step % qps
+    step = max(step, qps)
+    for lo in range(0, M, step):
+        hi = min(M, lo + step)
+        c = (np.arange(lo, hi) // bs)[None, :, None, None]
+        e = idx[:, lo:hi].astype(np.int64)
+        e = np.where((e >= 0) & (e <= c) & (e < NB), e, -1)
+        pad = (-(hi - lo)) % qps
+        if pad:
+            e = np.concatenate([e, np.full((B, pad, G, T), -1, np.int64)], axis=1)
+        e = np.sort(e.transpose(0, 2, 1, 3).reshape(B, G, -1, qps * T), axis=-1)
+        total += int(((e[..., 1:] != e[..., :-1]) & (e[..., 1:] >= 0)).sum() + (e[..., 0] >= 0).sum())
+    return total
+
+
 def cpu_baseline(cfg: Config, q, k, v, idx, target_s: float = 15.0):
     """The fp64 CPU oracle on random units of the same workload."""
     import oracle
@@ -170,6 +220,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the all-causal-blocks run")
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10, help="cold-cache timed calls (0 = skip)")
+    ap.add_argument("--no-probe", action="store_true", help="skip the gather-ceiling probe")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for HBM counters)")
@@ -247,6 +299,42 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": _traffic()},
     }
+
+    if args.cold_steps > 0:
+        print(f"[bench] cold timing, {args.cold_steps} calls", file=sys.stderr, flush=True)
+        c_med, c_min = time_cold(torch, launch, args.cold_steps)
+        out["cold"] = {"ms_median": round(c_med, 4), "ms_min": round(c_min, 4), "flush_MiB": 1024,
+                       "eff_TFLOPs": round(flops / (c_med * 1e-3) / 1e12, 3),
+                       "gathered_GBps": round(gathered / (c_med * 1e-3) / 1e9, 1)}
+
+    # MFMA work actually issued: every (16-column tile, staged block) pair runs
+    # the QK and PV products over the whole block, 4 * 16 * bs * D flops.
+    pack = 4 if 16 // cfg.gs >= 4 else 2 if 16 // cfg.gs >= 2 else 1
+    tile_blocks = slot_blocks(idx, cfg.block_size, cfg.N, pack)
+    mfma_flops = 4.0 * 16 * cfg.block_size * cfg.D * tile_blocks
+    out["mfma"] = {"tile_blocks": tile_blocks, "executed_flops": mfma_flops,
+                   "TFLOPs": round(mfma_flops / (ev_ms * 1e-3) / 1e12, 2),
+                   "util": round(mfma_flops / (ev_ms * 1e-3) / (FP16_PEAK_TFLOPS * 1e12), 4)}
+
+    if not args.no_probe:
+        from block_sparse_attention_sel_amd.binding import nsa_gather_probe
+        print("[bench] gather-ceiling probe", file=sys.stderr, flush=True)
+        staged = torch.zeros(1, dtype=torch.int64, device=dev)
+        qps = nsa_gather_probe(tk, tv, ti, staged, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size,
+                               cfg.T, stream.cuda_stream)
+        torch.cuda.synchronize()
+        n_staged = int(staged.item())
+
+        def probe():
+            nsa_gather_probe(tk, tv, ti, staged, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size,
+                             cfg.T, stream.cuda_stream)
+
+        _, p_ev, p_min = time_launches(torch, probe, args.steps, args.warmup)
+        staged_bytes = n_staged * cfg.block_size * cfg.D * 4
+        out["gather_ceiling"] = {"kernel": "nsa_gather_probe", "ms": round(p_ev, 4), "ms_min": round(p_min, 4),
+                                 "kernel_over_probe": round(ev_ms / p_ev, 4), "queries_per_slot": qps,
+                                 "staged_blocks": n_staged, "staged_bytes": staged_bytes,
+                                 "staged_GBps": round(staged_bytes / (p_ev * 1e-3) / 1e9, 1)}
 
     if not args.no_dense:
         dcfg = cfg.dense()

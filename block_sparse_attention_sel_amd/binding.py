@@ -1,10 +1,11 @@
-"""Thin ctypes binding of libnsa_sel.so.
+"""Thin ctypes binding of libnsa_sel.so and libnsa_gather_probe.so.
 
 ``nsa_sel_fwd`` and ``nsa_sel_status_string`` mirror the C entry points one to
 one (pointers may be given as ints or as torch tensors); ``sel_attn_fwd`` is a
 convenience that checks torch tensors, allocates the outputs and calls
-``nsa_sel_fwd`` on the current stream.  All arithmetic happens in the HIP
-kernels; when the library is missing every call raises.
+``nsa_sel_fwd`` on the current stream.  ``nsa_gather_probe`` mirrors the
+measurement probe of include/nsa_gather_probe.h.  All arithmetic happens in the
+HIP kernels; when a library is missing every call into it raises.
 """
 
 from __future__ import annotations
@@ -14,6 +15,7 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa_sel.so")
+PROBE_LIB_PATH = os.path.join(_PKG, "libnsa_gather_probe.so")
 
 # Status codes (mirror include/nsa_sel.h).
 NSA_SEL_OK = 0
@@ -26,8 +28,10 @@ NSA_SEL_ERR_ALIAS = 6
 NSA_SEL_ERR_HIP = 7
 
 EXPORTED = ("nsa_sel_fwd", "nsa_sel_status_string")
+PROBE_EXPORTED = ("nsa_gather_probe",)
 
 _lib = None
+_probe_lib = None
 
 
 class NsaSelError(RuntimeError):
@@ -104,3 +108,37 @@ def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, st
         stream = torch.cuda.current_stream(q.device).cuda_stream
     nsa_sel_fwd(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
     return out, lse
+
+
+def load_probe_library(path: str = PROBE_LIB_PATH) -> ctypes.CDLL:
+    global _probe_lib
+    if _probe_lib is not None and path == PROBE_LIB_PATH:
+        return _probe_lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, ci = ctypes.c_void_p, ctypes.c_int
+    lib.nsa_gather_probe.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [ctypes.POINTER(ci), vp]
+    lib.nsa_gather_probe.restype = ci
+    if path == PROBE_LIB_PATH:
+        _probe_lib = lib
+    return lib
+
+
+def nsa_gather_probe_raw(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream=0):
+    """Calls the probe's C entry point; returns (status, queries per slot)."""
+    lib = load_probe_library()
+    qps = ctypes.c_int(0)
+    rc = lib.nsa_gather_probe(_addr(K), _addr(V), _addr(block_indices), _addr(staged), int(B), int(M), int(N),
+                              int(H), int(G), int(D), int(block_size), int(T), ctypes.byref(qps),
+                              ctypes.c_void_p(_addr(stream)))
+    return rc, qps.value
+
+
+def nsa_gather_probe(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream=0) -> int:
+    """Queues the probe; raises NsaSelError on a nonzero status and returns the
+    number of consecutive queries each wavefront slot carries."""
+    rc, qps = nsa_gather_probe_raw(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+    return qps

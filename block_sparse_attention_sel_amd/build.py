@@ -1,4 +1,9 @@
-"""Builds libnsa_sel.so (HIP, gfx950) in-tree with hipcc."""
+"""Builds the HIP libraries (gfx950) in-tree with hipcc:
+
+- libnsa_sel.so: the selection-attention forward (include/nsa_sel.h);
+- libnsa_gather_probe.so: the gather-ceiling probe (include/nsa_gather_probe.h),
+  a measurement aid that replays the forward kernel's block gathers.
+"""
 
 from __future__ import annotations
 
@@ -7,8 +12,11 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "nsa_sel.hip")
+CSRC = os.path.join(PKG, "csrc")
+SRC = os.path.join(CSRC, "nsa_sel.hip")
 LIB = os.path.join(PKG, "libnsa_sel.so")
+PROBE_SRC = os.path.join(CSRC, "gather_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libnsa_gather_probe.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 HIPCC_FLAGS = [
@@ -24,7 +32,7 @@ HIPCC_FLAGS = [
 def build(extra_flags=(), out: str = LIB, src: str = SRC) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, src]
+    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
@@ -32,5 +40,10 @@ def build(extra_flags=(), out: str = LIB, src: str = SRC) -> str:
     return out
 
 
+def build_all() -> list[str]:
+    return [build(), build(out=PROBE_LIB, src=PROBE_SRC)]
+
+
 if __name__ == "__main__":
-    print(build())
+    for path in build_all():
+        print(path)

@@ -2,71 +2,34 @@
 //
 // Operation: wave issue "[wave] NSA: selection attention forward kernel",
 // sections Operation, Algorithm, Requirements and "MI350 considerations".
-// One wavefront owns one unit (b, m, g) -- the page's program instance -- and
-// computes all H/G heads of the group together (the page's BLOCK_H register
-// tiling).  For each counted entry t of block_indices[b, m, g, :] it gathers
-// the bs keys of block t for group g, forms scores for all heads, applies the
-// causal mask, and folds the block into a running-max / running-sum softmax
-// (the "online softmax across all T blocks" requirement); O and the natural
-// log-sum-exp are written at the end.
+// The page's program instance is one unit (b, m, g): all H/G heads of group g
+// for query m attend, through one online softmax, to the keys of the blocks
+// that block_indices[b, m, g, :] selects, under the causal mask; O and the
+// natural-log log-sum-exp are written at the end.
 //
 // MI355X mapping (the design notes give the measurements behind each choice):
+//  * A wavefront carries a slot of 1-8 consecutive queries of one (b, g):
+//    PACK queries (gs heads each) fill a 16-column MFMA tile, and a wavefront
+//    holds one or two tiles.  Their index rows are merged into one ascending
+//    sequence of distinct blocks; each block is gathered once for the slot and
+//    multiplied only for the tiles whose queries selected it.
 //  * Scores are computed transposed, S^T = K * Q^T, on v_mfma_f32_16x16x32_f16:
-//    keys are the 16 MFMA rows, the (up to 16) heads of the group are the
-//    columns.  The S^T result layout (lane l: head l%16, keys 4*(l/16)+i) is
-//    already the B-operand layout of the PV product, so P never leaves
-//    registers.
-//  * Each counted block is copied global -> LDS with 128-bit direct-to-LDS
-//    buffer loads whose lanes walk whole key rows (coalesced); the MFMA
-//    operand layout, which puts consecutive lanes on different rows, is only
-//    used for the LDS reads.  K fragments come from XOR-swizzled
-//    ds_read_b128; V^T fragments come straight from ds_read_b64_tr_b16.
-//  * K and V have their own LDS buffers; the next counted block's K copy is
-//    issued once this block's K fragments are in registers, its V copy once
-//    the V fragments are, so every copy overlaps about one block of math.
-//  * One wavefront per workgroup.  Hardware deals workgroup w to XCD w % 8,
-//    so units are laid out for each XCD to walk a contiguous (b, g, m)
-//    range and keep the K/V prefix of few groups in its L2.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-#include <limits.h>
-
-#include <atomic>
-
-#include "nsa_sel.h"
+//    keys are the 16 MFMA rows, heads (and packed queries) the columns.  The
+//    S^T result layout is already the B-operand layout of the PV product, so
+//    P never leaves registers.
+//  * Each block is copied global -> LDS as 32-key sub-blocks with 128-bit
+//    direct-to-LDS buffer loads whose lanes walk whole key rows (coalesced).
+//    K fragments come from XOR-swizzled ds_read_b128, V^T fragments straight
+//    from ds_read_b64_tr_b16.  The next sub-block's K copy is issued once this
+//    one's K fragments are in registers, its V copy once the V fragments are.
+//  * Four wavefronts per workgroup, two workgroups per CU (two wavefronts per
+//    SIMD).  Workgroup w runs on XCD w % 8; slots are launched in generations
+//    that fill every workgroup slot, each XCD walking a contiguous range of
+//    (b, g, m), so the wavefronts resident on an XCD sweep the same key range
+//    in step and share its L2.
+#include "nsa_sel_common.h"
 
 namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-
-constexpr int kWaveSize = 64;
-// Wavefronts per workgroup: with 32-key stages (16 KiB per wavefront at
-// D = 128) two 4-wavefront workgroups share a CU, two wavefronts per SIMD;
-// with 64-key stages five wavefronts fill the CU's 160 KiB of LDS.
-constexpr int waves_per_wg(int sbs) { return sbs == 32 ? 4 : 5; }
-constexpr int kNumXcd = 8;
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-
-struct Params {
-    const _Float16 *Q;
-    const _Float16 *K;
-    const _Float16 *V;
-    const int32_t *idx;
-    _Float16 *O;
-    float *LSE;
-    int B, M, N, H, G, T, gs, NB;
-    int pack;           // queries per 16-column MFMA tile (1, 2 or 4; see nsa_sel_fwd)
-    int mode;           // 0: cursor merge, one tile; 1/2: register merge with that many tiles
-    int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / queries per wavefront)
-    int wslots;         // B * G * wslots_per_bg
-    int per_xcd;        // wavefront slots owned by each XCD: ceil(wslots / 8)
-    int gen_step;       // wavefront slots one XCD runs per launch (its workgroup slots x waves)
-    int gen;            // generation (launch) index
-    float scale_log2;   // log2(e) / sqrt(D)
-};
 
 __device__ __forceinline__ float4v mfma_16x16x32(half8 a, half8 b, float4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -87,396 +50,6 @@ __device__ __forceinline__ half8 cat8(half4 a, half4 b) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Scans one index row in chunks of 64 entries: lane j holds entry base + j and
-// a wave ballot marks the counted ones, so finding the next counted entry is
-// scalar bit arithmetic.
-struct IndexScan {
-    const int32_t *row;
-    int T, cm, NB, lane;
-    int base;
-    uint64_t mask;
-    int val;
-
-    __device__ __forceinline__ void load(int b) {
-        base = b;
-        const int j = b + lane;
-        const int v = (j < T) ? __builtin_nontemporal_load(&row[j]) : -1;
-        val = v;
-        const bool ok = v >= 0 && v <= cm && v < NB;
-        mask = __ballot(ok);
-    }
-    // Position of the first counted entry at or after i, or T.
-    __device__ __forceinline__ int next(int i) {
-        while (i < T) {
-            if (i >= base + kWaveSize) load(i);
-            const uint64_t mm = mask >> (i - base);
-            if (mm) return i + __builtin_ctzll(mm);
-            i = base + kWaveSize;
-        }
-        return T;
-    }
-    // Entry at position i; valid while i lies in the loaded chunk.
-    __device__ __forceinline__ int value(int i) const {
-        return __builtin_amdgcn_readlane(val, i - base);
-    }
-};
-
-constexpr int kDone = INT_MAX;
-
-// Walks the counted entries of one index row in row order.
-struct Cursor {
-    IndexScan sc;
-    int pos;
-    int cur;  // block of the current counted entry, or kDone
-
-    __device__ __forceinline__ void init(const int32_t *row, int T, int cm, int NB, int lane, bool live) {
-        sc.row = row;
-        sc.T = live ? T : 0;
-        sc.cm = cm;
-        sc.NB = NB;
-        sc.lane = lane;
-        sc.base = 0;
-        sc.mask = 0;
-        sc.val = -1;
-        if (live) sc.load(0);
-        pos = sc.next(0);
-        cur = pos < sc.T ? sc.value(pos) : kDone;
-    }
-    __device__ __forceinline__ void advance() {
-        pos = sc.next(pos + 1);
-        cur = pos < sc.T ? sc.value(pos) : kDone;
-    }
-};
-
-// Merges the rows of the packed queries: returns the smallest current block
-// and the mask of queries whose current entry is that block (advancing
-// them).  Every counted entry of every row is returned exactly once; rows
-// sorted ascending are swept in ascending block order and a block several
-// rows select at the same time is returned once for all of them.
-template <int PACK>
-__device__ __forceinline__ int merge_next(Cursor (&c)[PACK], unsigned &active) {
-    int t = c[0].cur;
-#pragma unroll
-    for (int k = 1; k < PACK; ++k) t = c[k].cur < t ? c[k].cur : t;
-    active = 0;
-    if (t == kDone) return t;
-#pragma unroll
-    for (int k = 0; k < PACK; ++k) {
-        if (c[k].cur == t) {
-            active |= 1u << k;
-            c[k].advance();
-        }
-    }
-    return t;
-}
-
-// Batched ds_read_b128 of one staged block into MFMA fragments, ending in
-// s_waitcnt lgkmcnt(0).  f[kt][c] comes from address a[c] + kt * 16 rows.
-template <int BS, int D>
-struct LdsBatch;
-
-#define NSA_DSR(o, a, off) "ds_read_b128 %" #o ", %" #a " offset:" #off "\n"
-
-template <>
-struct LdsBatch<64, 128> {  // 16 rows = 4096 bytes
-    __device__ static __forceinline__ void run(half8 (&f)[4][4], const unsigned (&a)[4]) {
-        asm volatile(NSA_DSR(0, 16, 0) NSA_DSR(1, 17, 0) NSA_DSR(2, 18, 0) NSA_DSR(3, 19, 0)
-                     NSA_DSR(4, 16, 4096) NSA_DSR(5, 17, 4096) NSA_DSR(6, 18, 4096) NSA_DSR(7, 19, 4096)
-                     NSA_DSR(8, 16, 8192) NSA_DSR(9, 17, 8192) NSA_DSR(10, 18, 8192) NSA_DSR(11, 19, 8192)
-                     NSA_DSR(12, 16, 12288) NSA_DSR(13, 17, 12288) NSA_DSR(14, 18, 12288)
-                     NSA_DSR(15, 19, 12288) "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[0][2]), "=&v"(f[0][3]), "=&v"(f[1][0]),
-                       "=&v"(f[1][1]), "=&v"(f[1][2]), "=&v"(f[1][3]), "=&v"(f[2][0]), "=&v"(f[2][1]),
-                       "=&v"(f[2][2]), "=&v"(f[2][3]), "=&v"(f[3][0]), "=&v"(f[3][1]), "=&v"(f[3][2]),
-                       "=&v"(f[3][3])
-                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-                     : "memory");
-    }
-};
-
-template <>
-struct LdsBatch<32, 128> {
-    __device__ static __forceinline__ void run(half8 (&f)[2][4], const unsigned (&a)[4]) {
-        asm volatile(NSA_DSR(0, 8, 0) NSA_DSR(1, 9, 0) NSA_DSR(2, 10, 0) NSA_DSR(3, 11, 0)
-                     NSA_DSR(4, 8, 4096) NSA_DSR(5, 9, 4096) NSA_DSR(6, 10, 4096) NSA_DSR(7, 11, 4096)
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[0][2]), "=&v"(f[0][3]), "=&v"(f[1][0]),
-                       "=&v"(f[1][1]), "=&v"(f[1][2]), "=&v"(f[1][3])
-                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-                     : "memory");
-    }
-};
-
-template <>
-struct LdsBatch<64, 64> {  // 16 rows = 2048 bytes
-    __device__ static __forceinline__ void run(half8 (&f)[4][2], const unsigned (&a)[2]) {
-        asm volatile(NSA_DSR(0, 8, 0) NSA_DSR(1, 9, 0) NSA_DSR(2, 8, 2048) NSA_DSR(3, 9, 2048)
-                     NSA_DSR(4, 8, 4096) NSA_DSR(5, 9, 4096) NSA_DSR(6, 8, 6144) NSA_DSR(7, 9, 6144)
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[1][0]), "=&v"(f[1][1]), "=&v"(f[2][0]),
-                       "=&v"(f[2][1]), "=&v"(f[3][0]), "=&v"(f[3][1])
-                     : "v"(a[0]), "v"(a[1])
-                     : "memory");
-    }
-};
-
-template <>
-struct LdsBatch<32, 64> {
-    __device__ static __forceinline__ void run(half8 (&f)[2][2], const unsigned (&a)[2]) {
-        asm volatile(NSA_DSR(0, 4, 0) NSA_DSR(1, 5, 0) NSA_DSR(2, 4, 2048) NSA_DSR(3, 5, 2048)
-                     "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0]), "=&v"(f[0][1]), "=&v"(f[1][0]), "=&v"(f[1][1])
-                     : "v"(a[0]), "v"(a[1])
-                     : "memory");
-    }
-};
-
-#undef NSA_DSR
-
-// Transposing reads of one staged V block (ds_read_b64_tr_b16), ending in
-// s_waitcnt lgkmcnt(0).  Within each 16-lane group the instruction hands
-// lane 4a+b element b of the 8-byte pieces loaded by lanes a, a+4, a+8, a+12
-// (element j from lane a+4j).  Lane (a + 4j) of group q4 points at V row
-// 32*kc + 16*half + 4*q4 + j, head-dims 32*c + 8*a + 4*hh .. +3, so lane
-// 4a+b receives V^T[32*c + 8*a + 4*hh + b][32*kc + 16*half + 4*q4 + j]: the
-// A operand of the PV MFMA for 32-key chunk kc and head-dim set (c, hh).
-// f[kc][c][hh][half]; a[c] is the lane's address for head-dim chunk c.
-template <int BS, int D>
-struct LdsTrBatch;
-
-template <>
-struct LdsTrBatch<64, 128> {
-    __device__ static __forceinline__ void run(half4 (&f)[2][4][2][2], const unsigned (&a)[4]) {
-        asm volatile("ds_read_b64_tr_b16 %0, %16 offset:0\n" "ds_read_b64_tr_b16 %1, %16 offset:4096\n" "ds_read_b64_tr_b16 %2, %16 offset:8\n" "ds_read_b64_tr_b16 %3, %16 offset:4104\n" "ds_read_b64_tr_b16 %4, %17 offset:0\n" "ds_read_b64_tr_b16 %5, %17 offset:4096\n" "ds_read_b64_tr_b16 %6, %17 offset:8\n" "ds_read_b64_tr_b16 %7, %17 offset:4104\n" "ds_read_b64_tr_b16 %8, %18 offset:0\n" "ds_read_b64_tr_b16 %9, %18 offset:4096\n" "ds_read_b64_tr_b16 %10, %18 offset:8\n" "ds_read_b64_tr_b16 %11, %18 offset:4104\n" "ds_read_b64_tr_b16 %12, %19 offset:0\n" "ds_read_b64_tr_b16 %13, %19 offset:4096\n" "ds_read_b64_tr_b16 %14, %19 offset:8\n" "ds_read_b64_tr_b16 %15, %19 offset:4104\n" "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1]), "=&v"(f[0][2][0][0]), "=&v"(f[0][2][0][1]), "=&v"(f[0][2][1][0]), "=&v"(f[0][2][1][1]), "=&v"(f[0][3][0][0]), "=&v"(f[0][3][0][1]), "=&v"(f[0][3][1][0]), "=&v"(f[0][3][1][1])
-                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-                     : "memory");
-        asm volatile("ds_read_b64_tr_b16 %0, %16 offset:8192\n" "ds_read_b64_tr_b16 %1, %16 offset:12288\n" "ds_read_b64_tr_b16 %2, %16 offset:8200\n" "ds_read_b64_tr_b16 %3, %16 offset:12296\n" "ds_read_b64_tr_b16 %4, %17 offset:8192\n" "ds_read_b64_tr_b16 %5, %17 offset:12288\n" "ds_read_b64_tr_b16 %6, %17 offset:8200\n" "ds_read_b64_tr_b16 %7, %17 offset:12296\n" "ds_read_b64_tr_b16 %8, %18 offset:8192\n" "ds_read_b64_tr_b16 %9, %18 offset:12288\n" "ds_read_b64_tr_b16 %10, %18 offset:8200\n" "ds_read_b64_tr_b16 %11, %18 offset:12296\n" "ds_read_b64_tr_b16 %12, %19 offset:8192\n" "ds_read_b64_tr_b16 %13, %19 offset:12288\n" "ds_read_b64_tr_b16 %14, %19 offset:8200\n" "ds_read_b64_tr_b16 %15, %19 offset:12296\n" "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[1][0][0][0]), "=&v"(f[1][0][0][1]), "=&v"(f[1][0][1][0]), "=&v"(f[1][0][1][1]), "=&v"(f[1][1][0][0]), "=&v"(f[1][1][0][1]), "=&v"(f[1][1][1][0]), "=&v"(f[1][1][1][1]), "=&v"(f[1][2][0][0]), "=&v"(f[1][2][0][1]), "=&v"(f[1][2][1][0]), "=&v"(f[1][2][1][1]), "=&v"(f[1][3][0][0]), "=&v"(f[1][3][0][1]), "=&v"(f[1][3][1][0]), "=&v"(f[1][3][1][1])
-                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-                     : "memory");
-    }
-};
-
-template <>
-struct LdsTrBatch<32, 128> {
-    __device__ static __forceinline__ void run(half4 (&f)[1][4][2][2], const unsigned (&a)[4]) {
-        asm volatile("ds_read_b64_tr_b16 %0, %16 offset:0\n" "ds_read_b64_tr_b16 %1, %16 offset:4096\n" "ds_read_b64_tr_b16 %2, %16 offset:8\n" "ds_read_b64_tr_b16 %3, %16 offset:4104\n" "ds_read_b64_tr_b16 %4, %17 offset:0\n" "ds_read_b64_tr_b16 %5, %17 offset:4096\n" "ds_read_b64_tr_b16 %6, %17 offset:8\n" "ds_read_b64_tr_b16 %7, %17 offset:4104\n" "ds_read_b64_tr_b16 %8, %18 offset:0\n" "ds_read_b64_tr_b16 %9, %18 offset:4096\n" "ds_read_b64_tr_b16 %10, %18 offset:8\n" "ds_read_b64_tr_b16 %11, %18 offset:4104\n" "ds_read_b64_tr_b16 %12, %19 offset:0\n" "ds_read_b64_tr_b16 %13, %19 offset:4096\n" "ds_read_b64_tr_b16 %14, %19 offset:8\n" "ds_read_b64_tr_b16 %15, %19 offset:4104\n" "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1]), "=&v"(f[0][2][0][0]), "=&v"(f[0][2][0][1]), "=&v"(f[0][2][1][0]), "=&v"(f[0][2][1][1]), "=&v"(f[0][3][0][0]), "=&v"(f[0][3][0][1]), "=&v"(f[0][3][1][0]), "=&v"(f[0][3][1][1])
-                     : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-                     : "memory");
-    }
-};
-
-template <>
-struct LdsTrBatch<64, 64> {
-    __device__ static __forceinline__ void run(half4 (&f)[2][2][2][2], const unsigned (&a)[2]) {
-        asm volatile("ds_read_b64_tr_b16 %0, %8 offset:0\n" "ds_read_b64_tr_b16 %1, %8 offset:2048\n" "ds_read_b64_tr_b16 %2, %8 offset:8\n" "ds_read_b64_tr_b16 %3, %8 offset:2056\n" "ds_read_b64_tr_b16 %4, %9 offset:0\n" "ds_read_b64_tr_b16 %5, %9 offset:2048\n" "ds_read_b64_tr_b16 %6, %9 offset:8\n" "ds_read_b64_tr_b16 %7, %9 offset:2056\n" "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1])
-                     : "v"(a[0]), "v"(a[1])
-                     : "memory");
-        asm volatile("ds_read_b64_tr_b16 %0, %8 offset:4096\n" "ds_read_b64_tr_b16 %1, %8 offset:6144\n" "ds_read_b64_tr_b16 %2, %8 offset:4104\n" "ds_read_b64_tr_b16 %3, %8 offset:6152\n" "ds_read_b64_tr_b16 %4, %9 offset:4096\n" "ds_read_b64_tr_b16 %5, %9 offset:6144\n" "ds_read_b64_tr_b16 %6, %9 offset:4104\n" "ds_read_b64_tr_b16 %7, %9 offset:6152\n" "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[1][0][0][0]), "=&v"(f[1][0][0][1]), "=&v"(f[1][0][1][0]), "=&v"(f[1][0][1][1]), "=&v"(f[1][1][0][0]), "=&v"(f[1][1][0][1]), "=&v"(f[1][1][1][0]), "=&v"(f[1][1][1][1])
-                     : "v"(a[0]), "v"(a[1])
-                     : "memory");
-    }
-};
-
-template <>
-struct LdsTrBatch<32, 64> {
-    __device__ static __forceinline__ void run(half4 (&f)[1][2][2][2], const unsigned (&a)[2]) {
-        asm volatile("ds_read_b64_tr_b16 %0, %8 offset:0\n" "ds_read_b64_tr_b16 %1, %8 offset:2048\n" "ds_read_b64_tr_b16 %2, %8 offset:8\n" "ds_read_b64_tr_b16 %3, %8 offset:2056\n" "ds_read_b64_tr_b16 %4, %9 offset:0\n" "ds_read_b64_tr_b16 %5, %9 offset:2048\n" "ds_read_b64_tr_b16 %6, %9 offset:8\n" "ds_read_b64_tr_b16 %7, %9 offset:2056\n" "s_waitcnt lgkmcnt(0)"
-                     : "=&v"(f[0][0][0][0]), "=&v"(f[0][0][0][1]), "=&v"(f[0][0][1][0]), "=&v"(f[0][0][1][1]), "=&v"(f[0][1][0][0]), "=&v"(f[0][1][0][1]), "=&v"(f[0][1][1][0]), "=&v"(f[0][1][1][1])
-                     : "v"(a[0]), "v"(a[1])
-                     : "memory");
-    }
-};
-
-
-// LDS staging of one gathered block (K and V, BS rows of D fp16 each).
-//
-// The block is copied global -> LDS with 128-bit direct-to-LDS buffer loads
-// (buffer_load_dwordx4 ... lds).  One such instruction moves 1 KiB: lane l
-// writes bytes [16*l, 16*l + 16) of the instruction's LDS window, and the
-// global address of every lane is free.  Lanes are given consecutive 16-byte
-// pieces of the same key row (a row is D*2 bytes = LPR lanes), so each
-// instruction reads whole rows and coalesces into full cache lines.
-//
-// In LDS a row occupies D*2 contiguous bytes; its 16-byte pieces are stored
-// XOR-permuted, piece c at slot c ^ swz(row), so that the MFMA-layout reads
-// (16 lanes on 16 different rows, same piece) hit distinct banks.
-//
-// Addressing: the per-lane part of the byte offset repeats every 16/RPI
-// instructions (the swizzle depends on row % 16), so it lives in NV VGPRs;
-// the per-instruction row step and the block start are uniform (SGPR).
-template <int BS, int D>
-struct Stage {
-    static constexpr int LPR = D / 8;                // lanes (16-byte pieces) per row
-    static constexpr int RPI = kWaveSize / LPR;      // rows per 1 KiB instruction
-    static constexpr int NI = BS / RPI;              // instructions per K (or V) block
-    static constexpr int NV = 16 / RPI;              // distinct per-lane offsets
-    static constexpr int HALVES = BS * D;            // fp16 elements per K (or V) block
-
-    __device__ static __forceinline__ int swz(int row) { return (row & 15) * LPR / 16; }
-
-    __amdgpu_buffer_rsrc_t rk, rv;  // K and V of this (b, g), byte-addressed
-    unsigned lane_off[NV];          // lane part of the offset for instruction s % NV
-    unsigned row_bytes;             // bytes between consecutive keys (G * D * 2)
-    int N;
-
-    __device__ __forceinline__ void init(const _Float16 *Kg, const _Float16 *Vg, unsigned bytes,
-                                         int row_stride, int n_keys, int lane) {
-        rk = __builtin_amdgcn_make_buffer_rsrc((void *)Kg, (short)0, (int)bytes, 0x00020000);
-        rv = __builtin_amdgcn_make_buffer_rsrc((void *)Vg, (short)0, (int)bytes, 0x00020000);
-        row_bytes = (unsigned)row_stride * 2u;
-        N = n_keys;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int row = v * RPI + lane / LPR;
-            lane_off[v] = (unsigned)(lane / LPR) * row_bytes + (unsigned)(((lane % LPR) ^ swz(row)) * 16);
-        }
-    }
-
-    typedef __attribute__((address_space(3))) _Float16 lds_half;
-
-    __device__ static __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, lds_half *lds, unsigned voff,
-                                                unsigned soff, int s) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void *)(lds + s * (kWaveSize * 8)), 16, voff, soff, 0, 0);
-    }
-
-    // Issues the copy of block t of K (rs = rk) or V (rs = rv) into buf;
-    // completes on vmcnt.
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, _Float16 *buf_generic, int t,
-                                          int lane) const {
-        lds_half *buf = (lds_half *)buf_generic;  // one address-space conversion per block
-        if (t * BS + BS <= N) {
-            const unsigned base = (unsigned)(t * BS) * row_bytes;
-#pragma unroll
-            for (int s = 0; s < NI; ++s)
-                copy(rs, buf, lane_off[s % NV], base + (unsigned)(s * RPI) * row_bytes, s);
-        } else {
-            // Last, partial block: clamp rows past the end into bounds (they are
-            // masked out of the softmax), with the whole offset per lane.
-#pragma unroll
-            for (int s = 0; s < NI; ++s) {
-                const int row = s * RPI + lane / LPR;
-                int n = t * BS + row;
-                n = n < N ? n : N - 1;
-                const unsigned off = (unsigned)n * row_bytes + (unsigned)(((lane % LPR) ^ swz(row)) * 16);
-                copy(rs, buf, off, 0u, s);
-            }
-        }
-    }
-
-    // MFMA A-operand fragments of one staged block: lane l gets row
-    // 16*kt + l%16, head-dim 32*c + 8*(l/16) .. +7.  The reads are issued
-    // as one inline-asm batch that ends in its own lgkmcnt(0) wait: the
-    // compiler would otherwise guard every LDS read with vmcnt(0), i.e.
-    // wait for all copies in flight, including the other buffer's.
-    __device__ static __forceinline__ void read(half8 (&f)[BS / 16][D / 32], const _Float16 *buf, int r,
-                                                int q4) {
-        const unsigned base = (unsigned)(size_t)(const __attribute__((address_space(3))) _Float16 *)buf;
-        unsigned a[D / 32];
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) a[c] = base + (unsigned)(r * D + ((c * 4 + q4) ^ swz(r)) * 8) * 2;
-        LdsBatch<BS, D>::run(f, a);
-    }
-
-    // V^T operands of one staged block for the PV MFMAs (see LdsTrBatch).
-    __device__ static __forceinline__ void read_vt(half4 (&f)[BS / 32][D / 32][2][2], const _Float16 *buf,
-                                                   int lane) {
-        const unsigned base = (unsigned)(size_t)(const __attribute__((address_space(3))) _Float16 *)buf;
-        const int q4 = lane >> 4, a = lane & 3, j = (lane >> 2) & 3;
-        const int row = 4 * q4 + j;  // row within a 16-row group; the group offset is immediate
-        unsigned addr[D / 32];
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c)
-            addr[c] = base + (unsigned)(row * D * 2 + ((4 * c + a) ^ swz(row)) * 16);
-        LdsTrBatch<BS, D>::run(f, addr);
-    }
-};
-
-// The queries of one wavefront slot: QW consecutive positions m0 .. m0+nq-1
-// of one (b, g).  A merger yields the union of their counted index entries in
-// ascending block order (for any row order) together with the mask of the
-// queries whose rows hold that block.
-
-// Streams each row through an IndexScan; handles any T.
-template <int QW, int BS>
-struct CursorMerger {
-    Cursor c[QW];
-
-    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane) {
-#pragma unroll
-        for (int k = 0; k < QW; ++k) {
-            const int mk = m0 + (k < nq ? k : 0);
-            c[k].init(p.idx + ((size_t)(b * (size_t)p.M + mk) * p.G + g) * p.T, p.T, mk / BS, p.NB, lane,
-                      k < nq);
-        }
-    }
-    __device__ __forceinline__ int next(unsigned &active) { return merge_next<QW>(c, active); }
-};
-
-// Wave-wide reductions over 64 lanes: DPP prefix within each 16-lane row,
-// then the four row results.
-__device__ __forceinline__ int wave_min(int x) {
-    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x111, 0xf, 0xf, false));
-    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x112, 0xf, 0xf, false));
-    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x114, 0xf, 0xf, false));
-    x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x118, 0xf, 0xf, false));
-    const int a = __builtin_amdgcn_readlane(x, 15), b = __builtin_amdgcn_readlane(x, 31);
-    const int c = __builtin_amdgcn_readlane(x, 47), d = __builtin_amdgcn_readlane(x, 63);
-    return min(min(a, b), min(c, d));
-}
-__device__ __forceinline__ unsigned wave_or(unsigned x) {
-    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);
-    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);
-    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);
-    x |= (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);
-    return (unsigned)(__builtin_amdgcn_readlane((int)x, 15) | __builtin_amdgcn_readlane((int)x, 31) |
-                      __builtin_amdgcn_readlane((int)x, 47) | __builtin_amdgcn_readlane((int)x, 63));
-}
-
-// Holds all QW*T entries (QW*T <= 128) in two registers per lane: entry
-// e = lane + 64*v belongs to query e / T.  Each step takes the smallest
-// remaining counted block and retires every entry equal to it, so a block
-// repeated within a row, or shared by several rows, is returned once.
-template <int QW, int BS>
-struct RegMerger {
-    int e[2];
-    unsigned bit[2];
-
-    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane) {
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            const int ent = lane + 64 * v;
-            const int qi = ent / p.T;
-            const bool slot = ent < QW * p.T && qi < nq;
-            const int m = m0 + (slot ? qi : 0);
-            const int32_t *row = p.idx + ((size_t)(b * (size_t)p.M + m) * p.G + g) * p.T;
-            const int t = slot ? __builtin_nontemporal_load(&row[ent - qi * p.T]) : -1;
-            const bool ok = t >= 0 && t <= m / BS && t < p.NB;
-            e[v] = ok ? t : INT_MAX;
-            bit[v] = slot ? 1u << qi : 0u;
-        }
-    }
-    __device__ __forceinline__ int next(unsigned &active) {
-        const int t = wave_min(min(e[0], e[1]));
-        active = 0;
-        if (t == INT_MAX) return kDone;
-        const bool h0 = e[0] == t, h1 = e[1] == t;
-        active = wave_or((h0 ? bit[0] : 0u) | (h1 ? bit[1] : 0u));
-        e[0] = h0 ? INT_MAX : e[0];
-        e[1] = h1 ? INT_MAX : e[1];
-        return t;
-    }
-};
-
-// s_waitcnt immediate for "at most n vector-memory ops outstanding"
-// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
-constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 // Scores of one gathered block folded into the running softmax state:
 // S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, column l%16), then
@@ -570,9 +143,6 @@ __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 
     }
 }
 
-// One wavefront slot: the packed queries m0 .. m0 + nq - 1 of one (b, g),
-// from index rows to stored O and LSE.  kbuf/vbuf are the wavefront's LDS
-// staging buffers.
 // One wavefront slot: QW = PACK * NT consecutive queries m0 .. m0+nq-1 of one
 // (b, g), from index rows to stored O and LSE.  The wavefront's MFMA columns
 // form NT tiles of 16; tile nt carries queries nt*PACK .. nt*PACK+PACK-1, gs
@@ -589,11 +159,8 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     constexpr int DC = D / 32;
     constexpr int KT = SBS / 16;
     constexpr int QW = PACK * NT;
-    const int bg = ws / p.wslots_per_bg;
-    const int m0 = (ws - bg * p.wslots_per_bg) * QW;
-    const int nq = min(QW, p.M - m0);
-    const int g = bg % p.G;
-    const int b = bg / p.G;
+    const Slot sl = decode_slot(p, ws, QW);
+    const int b = sl.b, g = sl.g, m0 = sl.m0, nq = sl.nq;
     const int r = lane & 15;
     const int q4 = lane >> 4;
     const int h0 = g * p.gs;
@@ -608,6 +175,11 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
         live[nt] = q_in_tile < PACK && qi < nq;
         my_m[nt] = m0 + (live[nt] ? qi : 0);
     }
+
+    // Staging descriptors first: set up before the per-lane index and Q
+    // loads, the compiler keeps them in scalar registers.
+    Stage<SBS, D> st;
+    init_stage(st, p, b, g, lane);
 
     // Q^T fragments (B operand): lane l holds column l%16, head-dim slice
     // 32*c + 8*(l/16) .. +7; columns without a query are zero.  Q, O, LSE and
@@ -624,10 +196,6 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             qf[nt][c] = live[nt] ? x : zero8;
         }
     }
-
-    const int row_stride = p.G * D;
-    const _Float16 *Kg = p.K + ((size_t)b * p.N * p.G + g) * D;
-    const _Float16 *Vg = p.V + ((size_t)b * p.N * p.G + g) * D;
 
     Merger mg;
     mg.init(p, b, g, m0, nq, lane);
@@ -647,13 +215,6 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     }
 
     constexpr int NI = Stage<SBS, D>::NI;
-    Stage<SBS, D> st;
-    {
-        const size_t kv_elems = (size_t)p.B * p.N * p.G * D;
-        const size_t first = ((size_t)b * p.N * p.G + g) * D;
-        const size_t bytes = (kv_elems - first) * 2;
-        st.init(Kg, Vg, (unsigned)(bytes < 0xFFFFFFFFu ? bytes : 0xFFFFFFFFu), row_stride, p.N, lane);
-    }
     const unsigned tile_bits = (1u << PACK) - 1u;
 
     // Pipeline over the merged sequence of sub-blocks (block t, part h): while
@@ -733,22 +294,19 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     }
 }
 
-// MODE 0: rows streamed through cursors (any T), one tile.  MODE 1/2/4:
-// rows held in registers, NT = MODE tiles.
+
+// MODE 0: rows streamed through cursors (any T), one tile.  MODE 1/2: rows
+// held in registers, NT = MODE tiles.
 template <int BS, int SPLIT, int D, int PACK, int MODE>
 __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_fwd_kernel(Params p) {
     constexpr int SBS = BS / SPLIT;
     constexpr int WAVES = waves_per_wg(SBS);
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int w = blockIdx.x;
     __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
     __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
-    // Generation p.gen: XCD w % 8 runs the next gen_step wavefront slots of its
-    // contiguous range, filling every workgroup slot of its CUs.
-    const int loc = p.gen * p.gen_step + (w / kNumXcd) * WAVES + wave;
-    const int ws = (w % kNumXcd) * p.per_xcd + loc;
-    if (loc >= p.per_xcd || ws >= p.wslots) return;
+    const int ws = wave_slot<WAVES>(p, wave);
+    if (ws < 0) return;
     if constexpr (MODE == 0)
         run_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
     else
@@ -756,72 +314,12 @@ __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_
                                                                          vbuf_all[wave]);
 }
 
-bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
-    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
-    return x < y + nb && y < x + na;
-}
-
-// Queues the generations in order on the stream.  Every generation starts
-// all its workgroups together and ends before the next starts, so the units
-// resident on an XCD sweep key space in step and share its L2.
-template <int BS, int SPLIT, int D, int PACK, int MODE>
-hipError_t launch(const Params &p, int wg_per_xcd, hipStream_t stream) {
-    const int gens = (p.per_xcd + p.gen_step - 1) / p.gen_step;
-    Params q = p;
-    for (int g = 0; g < gens; ++g) {
-        q.gen = g;
-        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE>), dim3(wg_per_xcd * kNumXcd),
-                           dim3(kWaveSize * waves_per_wg(BS / SPLIT)), 0, stream, q);
+struct FwdKernel {
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
+        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE>), grid, block, 0, stream, p);
     }
-    return hipGetLastError();
-}
-
-// One generation fills every workgroup slot of every CU: the staging buffers
-// (K and V, one block each per wavefront) set how many workgroups fit the
-// CU's 160 KiB of LDS (the four-tile mode also needs one wavefront per SIMD).
-template <int BS, int SPLIT, int D, int PACK, int MODE>
-hipError_t launch_sized(Params p, int cus, hipStream_t stream) {
-    constexpr int WAVES = waves_per_wg(BS / SPLIT);
-    constexpr int lds_per_wg = 2 * Stage<BS / SPLIT, D>::HALVES * 2 * WAVES;
-    constexpr int by_lds = 160 * 1024 / lds_per_wg;
-    constexpr int wg_per_cu = by_lds < 4 ? (by_lds > 0 ? by_lds : 1) : 4;
-    const int wg_per_xcd = (cus / kNumXcd > 0 ? cus / kNumXcd : 1) * wg_per_cu;
-    p.gen_step = wg_per_xcd * WAVES;
-    return launch<BS, SPLIT, D, PACK, MODE>(p, wg_per_xcd, stream);
-}
-
-// 64-key blocks are always staged as two 32-key halves.
-template <int BS, int D, int PACK>
-hipError_t launch_mode(const Params &p, int cus, hipStream_t stream) {
-    constexpr int SPLIT = BS / 32;
-    switch (p.mode) {
-        case 2: return launch_sized<BS, SPLIT, D, PACK, 2>(p, cus, stream);
-        case 1: return launch_sized<BS, SPLIT, D, PACK, 1>(p, cus, stream);
-        default: return launch_sized<BS, SPLIT, D, PACK, 0>(p, cus, stream);
-    }
-}
-
-template <int BS, int D>
-hipError_t launch_pack(const Params &p, int cus, hipStream_t stream) {
-    if (p.pack == 4) return launch_mode<BS, D, 4>(p, cus, stream);
-    if (p.pack == 2) return launch_mode<BS, D, 2>(p, cus, stream);
-    return launch_mode<BS, D, 1>(p, cus, stream);
-}
-
-// Compute units of the current device, cached per device (the first call on a
-// device asks the runtime; a failed query falls back to 256).
-int device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
+};
 
 }  // namespace
 
@@ -845,45 +343,14 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
                            void *O, float *LSE, int B, int M, int N, int H, int G, int D,
                            int block_size, int T, hipStream_t stream) {
     if (!Q || !K || !V || !block_indices || !O || !LSE) return NSA_SEL_ERR_NULL;
-    if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1 || block_size < 1 || T < 1)
-        return NSA_SEL_ERR_SHAPE;
-    if (H % G != 0) return NSA_SEL_ERR_SHAPE;
-    const int gs = H / G;
-    if ((D != 64 && D != 128) || (block_size != 32 && block_size != 64) || gs > 16)
-        return NSA_SEL_ERR_UNSUPPORTED;
+    Params p;
+    const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
+    if (st != NSA_SEL_OK) return st;
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15) return NSA_SEL_ERR_ALIGN;
     if (((uintptr_t)block_indices | (uintptr_t)LSE) & 3) return NSA_SEL_ERR_ALIGN;
 
-    const int64_t units = (int64_t)B * M * G;
-    // Queries per wavefront: as many whole groups of gs heads as fit the 16
-    // MFMA columns, rounded down to 1, 2 or 4.
-    const int pack = (16 / gs) >= 4 ? 4 : (16 / gs) >= 2 ? 2 : 1;
-    const int cus = device_cus();
-    // Tiles per wavefront (measured on MI355X): up to two, while the index
-    // rows of the wavefront's queries fit in two registers per lane (else one
-    // tile with streamed rows), and fewer while the grid would give a CU less
-    // than 8 wavefront slots.  Two tiles keep a wavefront within 256
-    // registers, so two wavefronts share each SIMD.
-    int mode = 0;
-    for (int nt = 2; nt >= 1; nt /= 2) {
-        if ((int64_t)pack * nt * T <= 128) {
-            mode = nt;
-            break;
-        }
-    }
-    while (mode > 1 && (int64_t)B * G * ((M + pack * mode - 1) / (pack * mode)) < 8LL * cus) mode /= 2;
-    const int qw = pack * (mode > 0 ? mode : 1);
-    const int64_t wslots_per_bg = ((int64_t)M + qw - 1) / qw;
-    const int64_t wslots = (int64_t)B * G * wslots_per_bg;
-    const int64_t per_xcd = (wslots + kNumXcd - 1) / kNumXcd;
-    // Element counts must fit the 64-bit offsets; unit ids and the grid use int.
-    const int64_t q_elems = (int64_t)B * M * H * D;
-    const int64_t kv_elems = (int64_t)B * N * G * D;
-    const int64_t idx_elems = (int64_t)B * M * G * T;
-    if (units > INT_MAX || (int64_t)N * G * D > INT_MAX) return NSA_SEL_ERR_RANGE;
-
-    const size_t q_bytes = (size_t)q_elems * 2, kv_bytes = (size_t)kv_elems * 2;
-    const size_t idx_bytes = (size_t)idx_elems * 4, lse_bytes = (size_t)B * H * M * 4;
+    const size_t q_bytes = (size_t)B * M * H * D * 2, kv_bytes = (size_t)B * N * G * D * 2;
+    const size_t idx_bytes = (size_t)B * M * G * T * 4, lse_bytes = (size_t)B * H * M * 4;
     const void *ins[4] = {Q, K, V, block_indices};
     const size_t in_bytes[4] = {q_bytes, kv_bytes, kv_bytes, idx_bytes};
     for (int i = 0; i < 4; ++i) {
@@ -893,27 +360,14 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     }
     if (ranges_overlap(O, q_bytes, LSE, lse_bytes)) return NSA_SEL_ERR_ALIAS;
 
-    Params p;
+    const int cus = device_cus();
+    plan_slots(p, cus);
     p.Q = (const _Float16 *)Q;
     p.K = (const _Float16 *)K;
     p.V = (const _Float16 *)V;
     p.idx = block_indices;
     p.O = (_Float16 *)O;
     p.LSE = LSE;
-    p.B = B; p.M = M; p.N = N; p.H = H; p.G = G; p.T = T; p.gs = gs;
-    p.NB = (N + block_size - 1) / block_size;
-    p.pack = pack;
-    p.mode = mode;
-    p.wslots_per_bg = (int)wslots_per_bg;
-    p.wslots = (int)wslots;
-    p.per_xcd = (int)per_xcd;
-    p.scale_log2 = kLog2e / sqrtf((float)D);
-    p.gen = 0;
-
-    hipError_t e;
-    if (block_size == 64)
-        e = (D == 128) ? launch_pack<64, 128>(p, cus, stream) : launch_pack<64, 64>(p, cus, stream);
-    else
-        e = (D == 128) ? launch_pack<32, 128>(p, cus, stream) : launch_pack<32, 64>(p, cus, stream);
+    const hipError_t e = launch_all(FwdKernel{}, p, block_size, D, cus, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
 }

@@ -116,3 +116,60 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"(import\s+oracle|from\s+oracle|nsa_oracle)", text), f
+
+
+# --- gather-ceiling probe (include/nsa_gather_probe.h) -------------------------
+
+PROBE_HEADER = os.path.join(ROOT, "include", "nsa_gather_probe.h")
+PADDR = {name: (i + 1) << 36 for i, name in enumerate(["K", "V", "I", "S"])}
+
+
+@pytest.fixture(scope="module")
+def probe_lib():
+    if not os.path.exists(binding.PROBE_LIB_PATH):
+        pytest.skip("libnsa_gather_probe.so not built")
+    return binding.load_probe_library()
+
+
+def test_probe_header_declares_the_binding_names():
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    assert sorted(set(re.findall(r"\b(nsa_\w+)\s*\(", text))) == sorted(binding.PROBE_EXPORTED)
+
+
+def test_probe_library_exports_every_declared_symbol(probe_lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.PROBE_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in binding.PROBE_EXPORTED:
+        assert name in exported
+
+
+def _probe_call(**over):
+    args = dict(GOOD)
+    ptrs = dict(PADDR)
+    for k in list(over):
+        if k in ptrs:
+            ptrs[k] = over.pop(k)
+    args.update(over)
+    return binding.nsa_gather_probe_raw(ptrs["K"], ptrs["V"], ptrs["I"], ptrs["S"], args["B"], args["M"],
+                                        args["N"], args["H"], args["G"], args["D"], args["block_size"],
+                                        args["T"], 0)[0]
+
+
+@pytest.mark.parametrize("which", ["K", "V", "I", "S"])
+def test_probe_null_pointer(probe_lib, which):
+    assert _probe_call(**{which: 0}) == binding.NSA_SEL_ERR_NULL
+
+
+@pytest.mark.parametrize("over,code", [(dict(M=0), binding.NSA_SEL_ERR_SHAPE),
+                                       (dict(H=8, G=3), binding.NSA_SEL_ERR_SHAPE),
+                                       (dict(D=96), binding.NSA_SEL_ERR_UNSUPPORTED),
+                                       (dict(block_size=16), binding.NSA_SEL_ERR_UNSUPPORTED),
+                                       (dict(B=1 << 12, M=1 << 20, G=1, H=1), binding.NSA_SEL_ERR_RANGE)])
+def test_probe_bad_sizes(probe_lib, over, code):
+    assert _probe_call(**over) == code
+
+
+@pytest.mark.parametrize("which,off", [("K", 8), ("V", 2), ("I", 2), ("S", 4)])
+def test_probe_misaligned(probe_lib, which, off):
+    assert _probe_call(**{which: PADDR[which] + off}) == binding.NSA_SEL_ERR_ALIGN
