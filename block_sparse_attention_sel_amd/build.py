@@ -26,6 +26,10 @@ HIPCC_FLAGS = [
     # MFMA results in VGPRs: the softmax and the V^T conversion consume them
     # on the VALU, so AGPR destinations would only add copies.
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # No NaN is ever produced or tested for (masked scores are -inf, which
+    # stays legal): lets fmaxf compile to a bare v_max without quieting its
+    # inputs first.
+    "-fno-honor-nans",
 ]
 
 

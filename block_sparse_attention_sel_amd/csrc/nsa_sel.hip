@@ -51,6 +51,23 @@ __device__ __forceinline__ half8 cat8(half4 a, half4 b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max and sum over the four lanes l%16 + 16*j of an MFMA result (one column)
+// with the gfx950 row-swap permutes, which stay in VALU: permlane16_swap with
+// both operands x leaves rows (0, 0, 2, 2) in the first result and (1, 1, 3,
+// 3) in the second, permlane32_swap the low and the high half likewise.
+__device__ __forceinline__ float col_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Scores of one gathered block folded into the running softmax state:
 // S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, column l%16), then
 // the running max, the rescale factor of the accumulator and the block's
@@ -93,8 +110,7 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
     float mloc = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = col_max(mloc);
     const float m_blk = mloc * scale_log2;
     float m_new = (m_blk > m_run + kLazyMax) ? m_blk : m_run;
     const bool off = col_mask && !col_on;
@@ -102,14 +118,15 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_use);
     m_run = m_new;
+    // A column left out of this block gets P = exp2(-inf) = 0.
+    const float m_exp = off ? INFINITY : m_use;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         float4v pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pv[i] = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -m_use));
-            if (off) pv[i] = 0.f;
+            pv[i] = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -m_exp));
             psum += pv[i];
         }
         pf[kt] = to_half4(pv);
@@ -275,8 +292,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     // Epilogue: total row sum over the 4 lanes of a column, normalise, store.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        float l = l_run[nt] + __shfl_xor(l_run[nt], 16);
-        l += __shfl_xor(l, 32);
+        const float l = col_sum(l_run[nt]);
         const float inv = l > 0.f ? 1.0f / l : 0.f;
         if (live[nt]) {
             _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + my_h) * D;
