@@ -5,8 +5,10 @@ units of the config) with inputs already resident in HBM.  Prints ONE JSON
 line: effective TFLOP/s as ``value``, plus ms per step, gathered-KV GB/s, the
 roofline of the kernel (HBM-bound on gathered bytes), cold-cache timings, the
 gather-ceiling probe (the kernel's block-gather stream alone), the MFMA
-utilisation, the same kernel with every causal block selected (dense mode) and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+utilisation, the same kernel with every causal block selected (dense mode),
+the dense causal attention kernel on the same tensors (the reference point of
+the speed-up goal) and the fp64 CPU oracle timed on a bounded sample of the
+same workload.
 
 Work counts per launch (exact, from the index rows):
   gathered bytes  = sum over units of (counted blocks) * bs * D * 2 B * 2 (K and V)
@@ -219,6 +221,7 @@ def main():
     ap.add_argument("--config", default="64k", choices=sorted(CONFIGS))
     ap.add_argument("--no-dense", action="store_true", help="skip the all-causal-blocks run")
     ap.add_argument("--dense-steps", type=int, default=3)
+    ap.add_argument("--no-dense-fa", action="store_true", help="skip the dense causal attention kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10, help="cold-cache timed calls (0 = skip)")
     ap.add_argument("--no-probe", action="store_true", help="skip the gather-ceiling probe")
@@ -349,6 +352,23 @@ def main():
                              "gathered_GBps": round(dblocks * cfg.block_size * cfg.D * 4 / (d_ev * 1e-3) / 1e9, 1),
                              "ratio_dense_over_selected": round(d_ev / ev_ms, 2)}
         del tdi
+
+    if not args.no_dense_fa:
+        # The dense causal attention the selection is measured against (same
+        # Q, K, V and layouts; every key n <= m visible).
+        from block_sparse_attention_sel_amd.binding import nsa_dense_fwd
+        print("[bench] dense causal attention (nsa_dense_fwd)", file=sys.stderr, flush=True)
+
+        def dense():
+            nsa_dense_fwd(tq, tk, tv, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, stream.cuda_stream)
+
+        _, f_ev, f_min = time_launches(torch, dense, args.dense_steps, 1)
+        _, dkeys = work_counts(cfg.dense(), None)
+        f_flops = 4.0 * cfg.D * cfg.gs * dkeys
+        out["dense_fa"] = {"kernel": "nsa_dense_fwd", "ms": round(f_ev, 3), "ms_min": round(f_min, 3),
+                           "eff_TFLOPs": round(f_flops / (f_ev * 1e-3) / 1e12, 2),
+                           "mfma_frac": round(f_flops / (f_ev * 1e-3) / (FP16_PEAK_TFLOPS * 1e12), 4),
+                           "ratio_dense_fa_over_selected": round(f_ev / ev_ms, 2)}
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -1,9 +1,9 @@
 """Thin ctypes binding of libnsa_sel.so and libnsa_gather_probe.so.
 
-``nsa_sel_fwd`` and ``nsa_sel_status_string`` mirror the C entry points one to
-one (pointers may be given as ints or as torch tensors); ``sel_attn_fwd`` is a
-convenience that checks torch tensors, allocates the outputs and calls
-``nsa_sel_fwd`` on the current stream.  ``nsa_gather_probe`` mirrors the
+``nsa_sel_fwd``, ``nsa_dense_fwd`` and ``nsa_sel_status_string`` mirror the C
+entry points one to one (pointers may be given as ints or as torch tensors);
+``sel_attn_fwd`` and ``dense_attn_fwd`` are conveniences that check torch
+tensors, allocate the outputs and call the entry point on the current stream.  ``nsa_gather_probe`` mirrors the
 measurement probe of include/nsa_gather_probe.h.  All arithmetic happens in the
 HIP kernels; when a library is missing every call into it raises.
 """
@@ -28,6 +28,7 @@ NSA_SEL_ERR_ALIAS = 6
 NSA_SEL_ERR_HIP = 7
 
 EXPORTED = ("nsa_sel_fwd", "nsa_sel_status_string")
+DENSE_EXPORTED = ("nsa_dense_fwd",)
 PROBE_EXPORTED = ("nsa_gather_probe",)
 
 _lib = None
@@ -52,6 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nsa_sel_fwd.restype = ci
     lib.nsa_sel_status_string.argtypes = [ci]
     lib.nsa_sel_status_string.restype = ctypes.c_char_p
+    lib.nsa_dense_fwd.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
+    lib.nsa_dense_fwd.restype = ci
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -107,6 +110,44 @@ def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, st
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     nsa_sel_fwd(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
+    return out, lse
+
+
+def nsa_dense_fwd_raw(Q, K, V, O, LSE, B, M, N, H, G, D, stream=0) -> int:
+    """Calls the dense entry point and returns its status code unchanged."""
+    lib = load_library()
+    return lib.nsa_dense_fwd(_addr(Q), _addr(K), _addr(V), _addr(O), _addr(LSE), int(B), int(M), int(N), int(H),
+                             int(G), int(D), ctypes.c_void_p(_addr(stream)))
+
+
+def nsa_dense_fwd(Q, K, V, O, LSE, B, M, N, H, G, D, stream=0) -> None:
+    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
+    rc = nsa_dense_fwd_raw(Q, K, V, O, LSE, B, M, N, H, G, D, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def dense_attn_fwd(q, k, v, out=None, lse=None, stream=None):
+    """Dense causal GQA attention: q [B,M,H,D] fp16, k/v [B,N,G,D] fp16,
+    contiguous CUDA tensors.  Returns (O [B,M,H,D] fp16, LSE [B,H,M] fp32)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-d float16 tensor")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, M, H, D = q.shape
+    _, N, G, _ = k.shape
+    if (k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape:
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, M, H, D), dtype=torch.float16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    nsa_dense_fwd(q, k, v, out, lse, B, M, N, H, G, D, stream)
     return out, lse
 
 

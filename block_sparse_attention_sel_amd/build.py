@@ -1,6 +1,7 @@
 """Builds the HIP libraries (gfx950) in-tree with hipcc:
 
-- libnsa_sel.so: the selection-attention forward (include/nsa_sel.h);
+- libnsa_sel.so: the selection-attention forward (include/nsa_sel.h) and the
+  dense causal attention forward it is compared with (include/nsa_dense.h);
 - libnsa_gather_probe.so: the gather-ceiling probe (include/nsa_gather_probe.h),
   a measurement aid that replays the forward kernel's block gathers.
 """
@@ -14,6 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 SRC = os.path.join(CSRC, "nsa_sel.hip")
+DENSE_SRC = os.path.join(CSRC, "nsa_dense.hip")
 LIB = os.path.join(PKG, "libnsa_sel.so")
 PROBE_SRC = os.path.join(CSRC, "gather_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libnsa_gather_probe.so")
@@ -33,10 +35,10 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(extra_flags=(), out: str = LIB, src: str = SRC) -> str:
+def build(extra_flags=(), out: str = LIB, srcs=(SRC, DENSE_SRC)) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, src]
+    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
@@ -45,7 +47,7 @@ def build(extra_flags=(), out: str = LIB, src: str = SRC) -> str:
 
 
 def build_all() -> list[str]:
-    return [build(), build(out=PROBE_LIB, src=PROBE_SRC)]
+    return [build(), build(out=PROBE_LIB, srcs=(PROBE_SRC,))]
 
 
 if __name__ == "__main__":

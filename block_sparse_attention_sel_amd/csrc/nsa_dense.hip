@@ -1,0 +1,242 @@
+// Dense causal GQA attention forward for AMD MI355X (gfx950): the baseline
+// the selection kernel is compared with (include/nsa_dense.h).
+//
+// Operation: every causal key of the query (n <= m, n < N) for all H/G heads
+// of the group, one softmax, O and the natural-log LSE -- selection attention
+// with every block selected (wave issue "[wave] NSA: selection attention
+// forward kernel", section Performance target, names this dense attention as
+// the reference point).
+//
+// MI355X mapping.  The per-step math is the selection kernel's (transposed
+// scores S^T = K Q^T on v_mfma_f32_16x16x32_f16 with P kept in registers as
+// the PV B operand, lazy running max, V^T from ds_read_b64_tr_b16).  What
+// changes is the sharing: a workgroup of 8 wavefronts (two per SIMD) carries
+// 16 column tiles -- 16 * PACK consecutive queries of one (b, g) -- and all of
+// them consume one stream of 32-key K/V sub-blocks, staged once per workgroup
+// through a ring of kStages LDS buffers:
+//   * each wavefront copies its share of every sub-block (1/8 of the K and V
+//     copy instructions, 128-bit direct-to-LDS, coalesced rows);
+//   * per sub-block: wait for the own share, one LDS barrier (all shares in,
+//     the oldest buffer free), issue the copies kStages-1 sub-blocks ahead,
+//     then read K fragments, score the active tiles, read V^T, accumulate;
+//   * query tiles run longest first, and each XCD takes a contiguous range of
+//     (b, g, tile) units, so the workgroups resident on an XCD sweep the same
+//     group's keys.
+#include "nsa_sel_common.h"
+#include "nsa_dense.h"
+
+namespace {
+
+constexpr int kDenseWaves = 8;   // wavefronts per workgroup (two per SIMD)
+constexpr int kDenseTiles = 2;   // 16-column tiles per wavefront
+constexpr int kStages = 4;       // LDS ring of 32-key sub-blocks
+constexpr int kDenseSbs = 32;
+
+struct DenseParams {
+    const _Float16 *Q;
+    const _Float16 *K;
+    const _Float16 *V;
+    _Float16 *O;
+    float *LSE;
+    int B, M, N, H, G, gs;
+    int qtiles;   // query tiles per (b, g)
+    int units;    // B * G * qtiles
+    int per_xcd;  // ceil(units / 8)
+    float scale_log2;
+};
+
+template <int D, int PACK>
+__global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(DenseParams p) {
+    constexpr int NT = kDenseTiles;
+    constexpr int QWG = kDenseWaves * NT * PACK;  // queries per workgroup
+    constexpr int SBS = kDenseSbs;
+    constexpr int DC = D / 32;
+    constexpr int KT = SBS / 16;
+    constexpr int NI = Stage<SBS, D>::NI;              // copy instructions per K (or V) sub-block
+    constexpr int IPW = (2 * NI) / kDenseWaves;        // of which each wavefront issues
+    static_assert((2 * NI) % kDenseWaves == 0 && IPW >= 1, "copy instructions must split evenly");
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf[kStages][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf[kStages][Stage<SBS, D>::HALVES];
+
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int unit = (blockIdx.x % kNumXcd) * p.per_xcd + (int)(blockIdx.x / kNumXcd);
+    if (unit >= p.units) return;  // the whole workgroup
+    const int bg = unit / p.qtiles;
+    const int qt = p.qtiles - 1 - (unit - bg * p.qtiles);  // longest tiles first
+    const int b = bg / p.G;
+    const int g = bg % p.G;
+    const int q0 = qt * QWG;
+    const int q_last = min(q0 + QWG, p.M) - 1;
+    const int r = lane & 15;
+    const int q4 = lane >> 4;
+    const int h0 = g * p.gs;
+    const int q_in_tile = r / p.gs;
+    const int my_h = h0 + (r - q_in_tile * p.gs);
+
+    // Staging descriptors before the per-lane loads (keeps them scalar).
+    Stage<SBS, D> st;
+    {
+        const int bb = __builtin_amdgcn_readfirstlane(b), gg = __builtin_amdgcn_readfirstlane(g);
+        const size_t first = ((size_t)bb * p.N * p.G + gg) * D;
+        const size_t bytes = ((size_t)p.B * p.N * p.G * D - first) * 2;
+        st.init(p.K + first, p.V + first, (unsigned)(bytes < 0xFFFFFFFFu ? bytes : 0xFFFFFFFFu), p.G * D, p.N,
+                lane);
+    }
+
+    // This wavefront's tiles: tile nt covers queries mt[nt] .. mt[nt]+PACK-1.
+    bool live[NT];
+    int my_m[NT], mt[NT];
+    half8 qf[NT][DC];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        mt[nt] = q0 + (wave * NT + nt) * PACK;
+        const int m = mt[nt] + q_in_tile;
+        live[nt] = q_in_tile < PACK && m < p.M;
+        my_m[nt] = live[nt] ? m : q0;
+        const _Float16 *qrow = p.Q + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + (live[nt] ? my_h : h0)) * D;
+        const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const half8 x = __builtin_nontemporal_load((const half8 *)(qrow + c * 32 + q4 * 8));
+            qf[nt][c] = live[nt] ? x : zero8;
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // Q is in registers before the copies start counting
+
+    float m_run[NT], l_run[NT], alpha[NT];
+    float4v acc[NT][DC][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        m_run[nt] = -INFINITY;
+        l_run[nt] = 0.f;
+        alpha[nt] = 1.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            acc[nt][c][0] = float4v{0.f, 0.f, 0.f, 0.f};
+            acc[nt][c][1] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // Sub-blocks 0 .. nsub-1 cover keys 0 .. min(N, q_last + 1) - 1.
+    const int nkeys = min(p.N, q_last + 1);
+    const int nsub = (nkeys + SBS - 1) / SBS;
+    auto issue = [&](int s) {
+        const int slot = s % kStages;
+#pragma unroll
+        for (int k = 0; k < IPW; ++k) {
+            const int j = wave + k * kDenseWaves;  // this wavefront's share of the 2*NI instructions
+            if (j < NI)
+                st.issue_part(st.rk, kbuf[slot], s, j, lane);
+            else
+                st.issue_part(st.rv, vbuf[slot], s, j - NI, lane);
+        }
+    };
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nsub) issue(s);
+
+    half8 kf[KT][DC];
+    half4 vt[SBS / 32][DC][2][2];
+    half4 pf[NT][KT];
+    for (int s = 0; s < nsub; ++s) {
+        // Own share of sub-block s landed (later ones may still be in flight),
+        // then everyone's; the buffer of s-1 is free once all passed.
+        if (s + kStages - 2 < nsub)
+            __builtin_amdgcn_s_waitcnt(wait_vm(IPW * (kStages - 2)));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        lds_barrier();
+        if (s + kStages - 1 < nsub) issue(s + kStages - 1);
+
+        const int slot = s % kStages;
+        const int key0 = s * SBS;
+        Stage<SBS, D>::read(kf, kbuf[slot], r, q4);
+        bool on[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int tile_last = min(mt[nt] + PACK, p.M) - 1;
+            on[nt] = mt[nt] < p.M && key0 <= tile_last;  // uniform: some query of the tile sees a key here
+            if (!on[nt]) continue;
+            const bool causal = (key0 + SBS - 1 > mt[nt]) || (key0 + SBS > p.N);
+            score_block<SBS, D>(kf, qf[nt], key0, causal, true, live[nt], my_m[nt], p.N, p.scale_log2, m_run[nt],
+                                l_run[nt], alpha[nt], pf[nt], q4);
+        }
+        Stage<SBS, D>::read_vt(vt, vbuf[slot], lane);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            if (on[nt]) accumulate_block<SBS, D>(vt, pf[nt], alpha[nt], acc[nt]);
+    }
+
+    // Epilogue: total row sum over the 4 lanes of a column, normalise, store.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const float l = col_sum(l_run[nt]);
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        if (live[nt]) {
+            _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + my_h) * D;
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                const half4 lo = to_half4(acc[nt][c][0] * inv);
+                const half4 hi = to_half4(acc[nt][c][1] * inv);
+                __builtin_nontemporal_store(cat8(lo, hi), (half8 *)(orow + c * 32 + q4 * 8));
+            }
+            if (q4 == 0) {
+                const float lse = l > 0.f ? m_run[nt] * kLn2 + logf(l) : -INFINITY;
+                __builtin_nontemporal_store(lse, &p.LSE[((size_t)b * p.H + my_h) * p.M + my_m[nt]]);
+            }
+        }
+    }
+}
+
+template <int D, int PACK>
+hipError_t launch_dense(const DenseParams &p, hipStream_t stream) {
+    hipLaunchKernelGGL((nsa_dense_kernel<D, PACK>), dim3(p.per_xcd * kNumXcd), dim3(kWaveSize * kDenseWaves), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int nsa_dense_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N,
+                             int H, int G, int D, hipStream_t stream) {
+    if (!Q || !K || !V || !O || !LSE) return NSA_SEL_ERR_NULL;
+    if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1) return NSA_SEL_ERR_SHAPE;
+    if (H % G != 0) return NSA_SEL_ERR_SHAPE;
+    const int gs = H / G;
+    if ((D != 64 && D != 128) || gs > 16) return NSA_SEL_ERR_UNSUPPORTED;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15) return NSA_SEL_ERR_ALIGN;
+    if ((uintptr_t)LSE & 3) return NSA_SEL_ERR_ALIGN;
+    if ((int64_t)B * M * G > INT_MAX || (int64_t)N * G * D > INT_MAX) return NSA_SEL_ERR_RANGE;
+    const size_t q_bytes = (size_t)B * M * H * D * 2, kv_bytes = (size_t)B * N * G * D * 2;
+    const size_t lse_bytes = (size_t)B * H * M * 4;
+    const void *ins[3] = {Q, K, V};
+    const size_t in_bytes[3] = {q_bytes, kv_bytes, kv_bytes};
+    for (int i = 0; i < 3; ++i) {
+        if (ranges_overlap(O, q_bytes, ins[i], in_bytes[i]) || ranges_overlap(LSE, lse_bytes, ins[i], in_bytes[i]))
+            return NSA_SEL_ERR_ALIAS;
+    }
+    if (ranges_overlap(O, q_bytes, LSE, lse_bytes)) return NSA_SEL_ERR_ALIAS;
+
+    const int pack = (16 / gs) >= 4 ? 4 : (16 / gs) >= 2 ? 2 : 1;
+    const int qwg = kDenseWaves * kDenseTiles * pack;
+    DenseParams p;
+    p.Q = (const _Float16 *)Q;
+    p.K = (const _Float16 *)K;
+    p.V = (const _Float16 *)V;
+    p.O = (_Float16 *)O;
+    p.LSE = LSE;
+    p.B = B; p.M = M; p.N = N; p.H = H; p.G = G; p.gs = gs;
+    p.qtiles = (M + qwg - 1) / qwg;
+    p.units = B * G * p.qtiles;
+    p.per_xcd = (p.units + kNumXcd - 1) / kNumXcd;
+    p.scale_log2 = kLog2e / sqrtf((float)D);
+    hipError_t e;
+    if (D == 128)
+        e = pack == 4 ? launch_dense<128, 4>(p, stream) : pack == 2 ? launch_dense<128, 2>(p, stream)
+                                                                     : launch_dense<128, 1>(p, stream);
+    else
+        e = pack == 4 ? launch_dense<64, 4>(p, stream) : pack == 2 ? launch_dense<64, 2>(p, stream)
+                                                                    : launch_dense<64, 1>(p, stream);
+    return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
+}

@@ -334,6 +334,18 @@ struct Stage {
         }
     }
 
+    // Issues only instruction i (0 <= i < NI) of block t's copy, rows
+    // i*RPI .. i*RPI+RPI-1, so that several wavefronts can share one copy.
+    __device__ __forceinline__ void issue_part(__amdgpu_buffer_rsrc_t rs, _Float16 *buf_generic, int t, int i,
+                                               int lane) const {
+        lds_half *buf = (lds_half *)buf_generic;
+        const int row = i * RPI + lane / LPR;
+        int n = t * BS + row;
+        n = n < N ? n : N - 1;  // rows past the end are clamped (and masked later)
+        const unsigned off = (unsigned)(n - t * BS) * row_bytes + (unsigned)(((lane % LPR) ^ swz(row)) * 16);
+        copy(rs, buf, off, (unsigned)(t * BS) * row_bytes, i);
+    }
+
     // MFMA A-operand fragments of one staged block: lane l gets row
     // 16*kt + l%16, head-dim 32*c + 8*(l/16) .. +7.  The reads are issued
     // as one inline-asm batch that ends in its own lgkmcnt(0) wait: the
@@ -441,6 +453,145 @@ struct RegMerger {
 // s_waitcnt immediate for "at most n vector-memory ops outstanding"
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
 constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Workgroup barrier for LDS traffic between wavefronts: waits for this
+// wavefront's own LDS operations, then s_barrier.  Unlike __syncthreads() it
+// does not wait for outstanding global loads, so copies already issued stay
+// in flight across it.  The memory clobber keeps the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
+// Score and accumulate steps shared by the selection and dense kernels.
+
+__device__ __forceinline__ float4v mfma_16x16x32(half8 a, half8 b, float4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+
+__device__ __forceinline__ half4 to_half4(float4v v) {
+    half4 r;
+    r[0] = (_Float16)v[0];
+    r[1] = (_Float16)v[1];
+    r[2] = (_Float16)v[2];
+    r[3] = (_Float16)v[3];
+    return r;
+}
+
+__device__ __forceinline__ half8 cat8(half4 a, half4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max and sum over the four lanes l%16 + 16*j of an MFMA result (one column)
+// with the gfx950 row-swap permutes, which stay in VALU: permlane16_swap with
+// both operands x leaves rows (0, 0, 2, 2) in the first result and (1, 1, 3,
+// 3) in the second, permlane32_swap the low and the high half likewise.
+__device__ __forceinline__ float col_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Scores of one gathered block folded into the running softmax state:
+// S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, column l%16), then
+// the running max, the rescale factor of the accumulator and the block's
+// probabilities P^T (fp16), all in the log2 domain (x * log2(e) / sqrt(D)).
+//
+// causal: the block reaches past the smallest packed query or past N, so
+//   keys past the column's query (my_m) or past N are masked to -inf.
+// col_mask: some packed query did not select this block; for those columns
+//   (col_on false) the running state is left unchanged and P is zero.
+// The running max is only raised when a block's max exceeds it by more than
+// kLazyMax (P then stays below 2^kLazyMax, well inside fp16), so most blocks
+// need no rescale of the accumulator (alpha == 1 exactly).
+constexpr float kLazyMax = 8.0f;
+
+template <int BS, int D>
+__device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
+                                            int key0, bool causal, bool col_mask, bool col_on, int my_m,
+                                            int N, float scale_log2, float &m_run, float &l_run,
+                                            float &alpha, half4 (&pf)[BS / 16], int q4) {
+    constexpr int KT = BS / 16;
+    constexpr int DC = D / 32;
+    float4v s[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        s[kt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < DC; ++c) s[kt] = mfma_16x16x32(kf[kt][c], qf[c], s[kt]);
+    }
+    if (causal) {
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = key0 + kt * 16 + q4 * 4 + i;
+                if (key > my_m || key >= N) s[kt][i] = -INFINITY;
+            }
+    }
+    // Row max of the raw scores (the scale is positive), then over the 4
+    // lanes (l, l^16, l^32, l^48) that share a column.
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
+    mloc = col_max(mloc);
+    const float m_blk = mloc * scale_log2;
+    float m_new = (m_blk > m_run + kLazyMax) ? m_blk : m_run;
+    const bool off = col_mask && !col_on;
+    if (off) m_new = m_run;
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_use);
+    m_run = m_new;
+    // A column left out of this block gets P = exp2(-inf) = 0.
+    const float m_exp = off ? INFINITY : m_use;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        float4v pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -m_exp));
+            psum += pv[i];
+        }
+        pf[kt] = to_half4(pv);
+    }
+    l_run = l_run * alpha + psum;  // per-lane partial; lanes are summed at the end
+}
+
+// O^T = alpha * O^T + V^T * P^T over 32-key chunks.  acc[c][hh] holds O^T rows
+// d = 32*c + 8*(l/16) + 4*hh + i for head l%16.  The B operand is P^T straight
+// from the score layout; the A operand V^T comes from the transposing reads.
+template <int BS, int D>
+__device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 32][2][2],
+                                                 const half4 (&pf)[BS / 16], float alpha,
+                                                 float4v (&acc)[D / 32][2]) {
+    constexpr int DC = D / 32;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // wave-uniform: some column rescales
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            acc[c][0] *= alpha;
+            acc[c][1] *= alpha;
+        }
+    }
+#pragma unroll
+    for (int kc = 0; kc < BS / 32; ++kc) {
+        const half8 bp = cat8(pf[2 * kc], pf[2 * kc + 1]);
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                acc[c][hh] = mfma_16x16x32(cat8(vt[kc][c][hh][0], vt[kc][c][hh][1]), bp, acc[c][hh]);
+    }
+}
 
 // The queries of wavefront slot ws: m0 .. m0 + nq - 1 of one (b, g).  Slots
 // are numbered (b, g)-major, so a contiguous slot range walks consecutive

@@ -48,6 +48,8 @@ def _load():
         i64 = ctypes.c_int64
         lib.nsa_oracle_units.restype = ctypes.c_int
         lib.nsa_oracle_units.argtypes = [p, p, p, p] + [i64] * 8 + [p, i64, p, p, p, ctypes.c_int]
+        lib.nsa_oracle_dense_units.restype = ctypes.c_int
+        lib.nsa_oracle_dense_units.argtypes = [p, p, p] + [i64] * 6 + [p, i64, p, p, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -105,3 +107,29 @@ def oracle_full(q, k, v, idx, block_size: int, threads: int = 0):
     O = O.reshape(B, M, H, D)
     L = L.reshape(B, M, H).transpose(0, 2, 1).copy()
     return O, L
+
+
+def dense_units(q, k, v, units: np.ndarray, threads: int = 0):
+    """Dense causal attention (every key n <= m, n < N visible) for units
+    (b, m, g): O fp64 [U, H/G, D] and LSE fp64 [U, H/G].  The same fp64
+    two-pass computation as ``oracle_units`` without an index array."""
+    idx = np.zeros((q.shape[0], q.shape[1], k.shape[2], 1), np.int32)
+    B, M, N, H, G, D, _ = _check_inputs(q, k, v, idx)
+    units = np.ascontiguousarray(units, dtype=np.int64).reshape(-1, 3)
+    U = units.shape[0]
+    gs = H // G
+    O = np.empty((U, gs, D), dtype=np.float64)
+    L = np.empty((U, gs), dtype=np.float64)
+    rc = _load().nsa_oracle_dense_units(_ptr(q), _ptr(k), _ptr(v), B, M, N, H, G, D, _ptr(units), U, _ptr(O),
+                                        _ptr(L), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return O, L
+
+
+def dense_full(q, k, v, threads: int = 0):
+    """Whole-tensor dense causal attention: O fp64 [B, M, H, D], LSE fp64 [B, H, M]."""
+    B, M, H, D = q.shape
+    G = k.shape[2]
+    O, L = dense_units(q, k, v, all_units(B, M, G), threads)
+    return O.reshape(B, M, H, D), L.reshape(B, M, H).transpose(0, 2, 1).copy()

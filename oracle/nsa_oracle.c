@@ -88,24 +88,29 @@ static void one_unit(job_t *j, int64_t u, scratch_t *w) {
     const int64_t NB = (N + bs - 1) / bs;
     const double scale = 1.0 / sqrt((double)D);
 
-    /* Selected-block set (union over the row). */
-    memset(w->mark, 0, (size_t)NB);
-    const int32_t *row = j->idx + ((b * M + m) * G + g) * T;
-    int dup = 0;
-    for (int64_t i = 0; i < T; ++i) {
-        int64_t t = row[i];
-        if (t < 0 || t >= NB) continue;
-        if (w->mark[t]) dup = 1;
-        w->mark[t] = 1;
-    }
-    if (dup) j->dup_units++;
-
-    /* Visible selected keys, ascending. */
     int64_t nk = 0;
-    for (int64_t t = 0; t < NB; ++t) {
-        if (!w->mark[t]) continue;
-        for (int64_t n = t * bs; n < (t + 1) * bs && n < N; ++n)
-            if (n <= m) w->keys[nk++] = n;
+    if (j->idx) {
+        /* Selected-block set (union over the row). */
+        memset(w->mark, 0, (size_t)NB);
+        const int32_t *row = j->idx + ((b * M + m) * G + g) * T;
+        int dup = 0;
+        for (int64_t i = 0; i < T; ++i) {
+            int64_t t = row[i];
+            if (t < 0 || t >= NB) continue;
+            if (w->mark[t]) dup = 1;
+            w->mark[t] = 1;
+        }
+        if (dup) j->dup_units++;
+
+        /* Visible selected keys, ascending. */
+        for (int64_t t = 0; t < NB; ++t) {
+            if (!w->mark[t]) continue;
+            for (int64_t n = t * bs; n < (t + 1) * bs && n < N; ++n)
+                if (n <= m) w->keys[nk++] = n;
+        }
+    } else {
+        /* Dense attention: every causally visible key n <= m, n < N. */
+        for (int64_t n = 0; n <= m && n < N; ++n) w->keys[nk++] = n;
     }
 
     /* Head h = g*gs + i of query m, decoded. */
@@ -192,12 +197,12 @@ static void *worker(void *arg) {
  *   n_threads <= 0 uses every online host core.
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
-int nsa_oracle_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+static int run_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                      const int32_t *block_indices, int64_t B, int64_t M, int64_t N,
                      int64_t H, int64_t G, int64_t D, int64_t block_size, int64_t T,
                      const int64_t *units, int64_t n_units, double *O, double *LSE,
                      int64_t *n_dup, int n_threads) {
-    if (!Q || !K || !V || !block_indices || !units || !O || !LSE) return -1;
+    if (!Q || !K || !V || !units || !O || !LSE) return -1;
     if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1 || block_size < 1 || T < 1) return -1;
     if (H % G) return -1;
     for (int64_t u = 0; u < n_units; ++u) {
@@ -245,4 +250,26 @@ int nsa_oracle_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
     free(jobs);
     free(th);
     return rc;
+}
+
+int nsa_oracle_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                     const int32_t *block_indices, int64_t B, int64_t M, int64_t N,
+                     int64_t H, int64_t G, int64_t D, int64_t block_size, int64_t T,
+                     const int64_t *units, int64_t n_units, double *O, double *LSE,
+                     int64_t *n_dup, int n_threads) {
+    if (!block_indices) return -1;
+    return run_units(Q, K, V, block_indices, B, M, N, H, G, D, block_size, T, units, n_units, O, LSE, n_dup,
+                     n_threads);
+}
+
+/*
+ * Dense causal attention over a list of units: the same two-pass fp64
+ * computation with every key n <= m (n < N) visible -- the selection with all
+ * causal blocks selected, without an index array.  Arguments and outputs as
+ * for nsa_oracle_units.
+ */
+int nsa_oracle_dense_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t B, int64_t M,
+                           int64_t N, int64_t H, int64_t G, int64_t D, const int64_t *units, int64_t n_units,
+                           double *O, double *LSE, int n_threads) {
+    return run_units(Q, K, V, NULL, B, M, N, H, G, D, 1, 1, units, n_units, O, LSE, NULL, n_threads);
 }

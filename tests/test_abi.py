@@ -173,3 +173,50 @@ def test_probe_bad_sizes(probe_lib, over, code):
 @pytest.mark.parametrize("which,off", [("K", 8), ("V", 2), ("I", 2), ("S", 4)])
 def test_probe_misaligned(probe_lib, which, off):
     assert _probe_call(**{which: PADDR[which] + off}) == binding.NSA_SEL_ERR_ALIGN
+
+
+# --- dense causal attention (include/nsa_dense.h) ----------------------------
+
+DENSE_HEADER = os.path.join(ROOT, "include", "nsa_dense.h")
+DGOOD = dict(B=1, M=256, N=256, H=8, G=1, D=128)
+
+
+def test_dense_header_declares_the_binding_names():
+    text = re.sub(r"/\*.*?\*/", "", open(DENSE_HEADER).read(), flags=re.S)
+    assert sorted(set(re.findall(r"\b(nsa_\w+)\s*\(", text))) == sorted(binding.DENSE_EXPORTED)
+
+
+def test_dense_symbol_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in binding.DENSE_EXPORTED:
+        assert name in exported
+
+
+def _dense_call(**over):
+    args = dict(DGOOD)
+    ptrs = {k: ADDR[k] for k in ("Q", "K", "V", "O", "L")}
+    for k in list(over):
+        if k in ptrs:
+            ptrs[k] = over.pop(k)
+    args.update(over)
+    return binding.nsa_dense_fwd_raw(ptrs["Q"], ptrs["K"], ptrs["V"], ptrs["O"], ptrs["L"], args["B"], args["M"],
+                                     args["N"], args["H"], args["G"], args["D"], 0)
+
+
+@pytest.mark.parametrize("which", ["Q", "K", "V", "O", "L"])
+def test_dense_null_pointer(lib, which):
+    assert _dense_call(**{which: 0}) == binding.NSA_SEL_ERR_NULL
+
+
+@pytest.mark.parametrize("over,code", [(dict(M=0), binding.NSA_SEL_ERR_SHAPE), (dict(H=8, G=3), binding.NSA_SEL_ERR_SHAPE),
+                                       (dict(D=96), binding.NSA_SEL_ERR_UNSUPPORTED),
+                                       (dict(H=32, G=1), binding.NSA_SEL_ERR_UNSUPPORTED),
+                                       (dict(B=1 << 12, M=1 << 20, G=1, H=1), binding.NSA_SEL_ERR_RANGE),
+                                       (dict(Q=ADDR["Q"] + 8), binding.NSA_SEL_ERR_ALIGN),
+                                       (dict(L=ADDR["L"] + 2), binding.NSA_SEL_ERR_ALIGN),
+                                       (dict(O=ADDR["K"]), binding.NSA_SEL_ERR_ALIAS),
+                                       (dict(L=ADDR["O"] + 64), binding.NSA_SEL_ERR_ALIAS)])
+def test_dense_rejects_bad_arguments(lib, over, code):
+    assert _dense_call(**over) == code

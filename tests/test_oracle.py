@@ -129,6 +129,27 @@ def test_full_selection_is_causal_attention(oracle_mod, shape):
     assert np.abs(L - lse.numpy()).max() <= 1e-12
 
 
+@pytest.mark.parametrize("shape", [(1, 128, 128, 4, 2, 16), (2, 70, 90, 6, 3, 8), (1, 100, 64, 8, 1, 64)])
+def test_dense_entry_is_causal_attention(oracle_mod, shape):
+    """The oracle's dense entry (no index array) is causal attention with
+    key n visible iff n <= m and n < N: torch's scaled_dot_product_attention
+    with an explicit mask (fp64, CPU), also for M != N."""
+    B, M, N, H, G, D = shape
+    rng = np.random.default_rng(11)
+    q, k, v = _rand_inputs(rng, B, M, N, H, G, D)
+    O, L = oracle_mod.dense_full(q, k, v)
+    gs = H // G
+    qt = torch.from_numpy(q.astype(np.float64)).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(gs, dim=1)
+    vt = torch.from_numpy(v.astype(np.float64)).permute(0, 2, 1, 3).repeat_interleave(gs, dim=1)
+    mask = torch.arange(N)[None, :] <= torch.arange(M)[:, None]                  # [M, N]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask)
+    s = ((qt @ kt.transpose(-1, -2)) / math.sqrt(D)).masked_fill(~mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    assert np.abs(O - ref.permute(0, 2, 1, 3).numpy()).max() <= 1e-12
+    assert np.abs(L - lse.numpy()).max() <= 1e-12
+
+
 def test_generated_rows_that_cover_the_prefix(oracle_mod):
     """Rows of the 8k workload with m < T*bs select every causal block; on
     those rows the oracle equals causal attention (torch SDPA, fp64)."""
