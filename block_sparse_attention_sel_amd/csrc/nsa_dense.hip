@@ -52,11 +52,11 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
     constexpr int SBS = kDenseSbs;
     constexpr int DC = D / 32;
     constexpr int KT = SBS / 16;
-    constexpr int NI = Stage<SBS, D>::NI;              // copy instructions per K (or V) sub-block
+    constexpr int NI = Stage<SBS, D, 1>::NI;              // copy instructions per K (or V) sub-block
     constexpr int IPW = (2 * NI) / kDenseWaves;        // of which each wavefront issues
     static_assert((2 * NI) % kDenseWaves == 0 && IPW >= 1, "copy instructions must split evenly");
-    __shared__ __attribute__((aligned(16))) _Float16 kbuf[kStages][Stage<SBS, D>::HALVES];
-    __shared__ __attribute__((aligned(16))) _Float16 vbuf[kStages][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf[kStages][Stage<SBS, D, 1>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf[kStages][Stage<SBS, D, 1>::HALVES];
 
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
     const int my_h = h0 + (r - q_in_tile * p.gs);
 
     // Staging descriptors before the per-lane loads (keeps them scalar).
-    Stage<SBS, D> st;
+    Stage<SBS, D, 1> st;
     {
         const int bb = __builtin_amdgcn_readfirstlane(b), gg = __builtin_amdgcn_readfirstlane(g);
         const size_t first = ((size_t)bb * p.N * p.G + gg) * D;
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
 
         const int slot = s % kStages;
         const int key0 = s * SBS;
-        Stage<SBS, D>::read(kf, kbuf[slot], r, q4);
+        Stage<SBS, D, 1>::read(kf, kbuf[slot], r, q4);
         bool on[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -159,10 +159,10 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
             on[nt] = mt[nt] < p.M && key0 <= tile_last;  // uniform: some query of the tile sees a key here
             if (!on[nt]) continue;
             const bool causal = (key0 + SBS - 1 > mt[nt]) || (key0 + SBS > p.N);
-            score_block<SBS, D>(kf, qf[nt], key0, causal, true, live[nt], my_m[nt], p.N, p.scale_log2, m_run[nt],
+            score_block<SBS, D>(kf, qf[nt], key0, causal, true, live[nt], min(my_m[nt], p.N - 1), p.scale_log2, m_run[nt],
                                 l_run[nt], alpha[nt], pf[nt], q4);
         }
-        Stage<SBS, D>::read_vt(vt, vbuf[slot], lane);
+        Stage<SBS, D, 1>::read_vt(vt, vbuf[slot], lane);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             if (on[nt]) accumulate_block<SBS, D>(vt, pf[nt], alpha[nt], acc[nt]);

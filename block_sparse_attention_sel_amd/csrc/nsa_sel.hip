@@ -142,7 +142,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             const int first_m = m0 + nt * PACK;
             const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
             const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
-            score_block<SBS, D>(kf, qf[nt], key0, causal, true, col_on, my_m[nt], p.N, p.scale_log2, m_run[nt],
+            score_block<SBS, D>(kf, qf[nt], key0, causal, true, col_on, min(my_m[nt], p.N - 1), p.scale_log2, m_run[nt],
                                 l_run[nt], alpha[nt], pf[nt], q4);
         }
         if (has1)
