@@ -40,7 +40,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # Stream ids inside one seed.
-STREAM_Q, STREAM_K, STREAM_V, STREAM_IDX = 1, 2, 3, 4
+STREAM_Q, STREAM_K, STREAM_V, STREAM_IDX, STREAM_DO = 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -229,6 +229,11 @@ def make_inputs(cfg: Config, threads: int | None = None):
     v = normal_fp16((cfg.B, cfg.N, cfg.G, cfg.D), cfg.seed, STREAM_V, threads)
     idx = block_indices(cfg, threads)
     return q, k, v, idx
+
+
+def make_grad_output(cfg: Config, threads: int | None = None) -> np.ndarray:
+    """Upstream gradient dO, fp16 [B, M, H, D], N(0, 1), for the backward pass."""
+    return normal_fp16((cfg.B, cfg.M, cfg.H, cfg.D), cfg.seed, STREAM_DO, threads)
 
 
 def sample_units(cfg: Config, count: int, seed: int = 12345, tail: int = 2) -> np.ndarray:

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for NSA selection-attention forward.
+"""fp64 CPU oracle for NSA selection attention (forward and backward).
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by the
 bench's CPU-baseline leg, never by the GPU library or its binding.  It shares
@@ -50,6 +50,8 @@ def _load():
         lib.nsa_oracle_units.argtypes = [p, p, p, p] + [i64] * 8 + [p, i64, p, p, p, ctypes.c_int]
         lib.nsa_oracle_dense_units.restype = ctypes.c_int
         lib.nsa_oracle_dense_units.argtypes = [p, p, p] + [i64] * 6 + [p, i64, p, p, ctypes.c_int]
+        lib.nsa_oracle_bwd_units.restype = ctypes.c_int
+        lib.nsa_oracle_bwd_units.argtypes = ([p] * 5 + [i64] * 8 + [p, i64, p, i64, p, p, p, ctypes.c_int])
         _lib = lib
     return _lib
 
@@ -133,3 +135,49 @@ def dense_full(q, k, v, threads: int = 0):
     G = k.shape[2]
     O, L = dense_units(q, k, v, all_units(B, M, G), threads)
     return O.reshape(B, M, H, D), L.reshape(B, M, H).transpose(0, 2, 1).copy()
+
+
+def bwd_units(q, k, v, idx, do, block_size: int, units: np.ndarray, kblocks: np.ndarray | None = None,
+              threads: int = 0):
+    """Gradients of the selection attention of units (b, m, g) for the upstream
+    gradient ``do`` (fp16 [B, M, H, D]).
+
+    idx None means dense causal attention (every key n <= m visible).
+    Returns dQ fp64 [U, H/G, D] for the units, and dK, dV fp64 summed over the
+    units: [B, N, G, D] when ``kblocks`` is None, else [n_kblocks, bs, D] for
+    the key blocks (b, g, t) listed there (rows past N stay zero).  Only the
+    given units contribute, so a key block's dK/dV is complete when every unit
+    that selects it is listed."""
+    if idx is None:
+        idx_arr = np.zeros((q.shape[0], q.shape[1], k.shape[2], 1), np.int32)
+    else:
+        idx_arr = idx
+    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx_arr)
+    if do.dtype != np.float16 or not do.flags.c_contiguous or do.shape != q.shape:
+        raise ValueError("dO must be a C-contiguous float16 array shaped like Q")
+    units = np.ascontiguousarray(units, dtype=np.int64).reshape(-1, 3)
+    U = units.shape[0]
+    gs = H // G
+    dQ = np.empty((U, gs, D), dtype=np.float64)
+    if kblocks is None:
+        kb_ptr, nkb = None, 0
+        dK = np.zeros((B, N, G, D), dtype=np.float64)
+    else:
+        kblocks = np.ascontiguousarray(kblocks, dtype=np.int64).reshape(-1, 3)
+        kb_ptr, nkb = _ptr(kblocks), kblocks.shape[0]
+        dK = np.zeros((nkb, block_size, D), dtype=np.float64)
+    dV = np.zeros_like(dK)
+    rc = _load().nsa_oracle_bwd_units(_ptr(q), _ptr(k), _ptr(v), None if idx is None else _ptr(idx_arr), _ptr(do),
+                                      B, M, N, H, G, D, block_size, T, _ptr(units), U, kb_ptr, nkb,
+                                      _ptr(dQ), _ptr(dK), _ptr(dV), threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return dQ, dK, dV
+
+
+def bwd_full(q, k, v, idx, do, block_size: int, threads: int = 0):
+    """Whole-tensor gradients: dQ fp64 [B, M, H, D], dK and dV fp64 [B, N, G, D]."""
+    B, M, H, D = q.shape
+    G = k.shape[2]
+    dQ, dK, dV = bwd_units(q, k, v, idx, do, block_size, all_units(B, M, G), None, threads)
+    return dQ.reshape(B, M, H, D), dK, dV

@@ -81,7 +81,8 @@ typedef struct {
     double *mu, *z;       /* [gs] per-head max and normaliser     */
 } scratch_t;
 
-static void one_unit(job_t *j, int64_t u, scratch_t *w) {
+/* Returns the number of visible selected keys (w->keys[0 .. nk-1]). */
+static int64_t one_unit(job_t *j, int64_t u, scratch_t *w) {
     const int64_t b = j->units[3 * u], m = j->units[3 * u + 1], g = j->units[3 * u + 2];
     const int64_t N = j->N, M = j->M, H = j->H, G = j->G, D = j->D, bs = j->bs, T = j->T;
     const int64_t gs = H / G;
@@ -158,6 +159,7 @@ static void one_unit(job_t *j, int64_t u, scratch_t *w) {
         for (int64_t d = 0; d < D; ++d) o[d] /= w->z[i];
         j->LSE[u * gs + i] = w->mu[i] + log(w->z[i]);
     }
+    return nk;
 }
 
 static void *worker(void *arg) {
@@ -272,4 +274,187 @@ int nsa_oracle_dense_units(const uint16_t *Q, const uint16_t *K, const uint16_t 
                            int64_t N, int64_t H, int64_t G, int64_t D, const int64_t *units, int64_t n_units,
                            double *O, double *LSE, int n_threads) {
     return run_units(Q, K, V, NULL, B, M, N, H, G, D, 1, 1, units, n_units, O, LSE, NULL, n_threads);
+}
+
+/*
+ * Backward of the same operation, in fp64 (the reason the forward returns LSE:
+ * wave issue "[wave] NSA: selection attention forward kernel", section
+ * Requirements).  For a unit (b, m, g), head h of the group, with the visible
+ * selected keys n, scores s_n = q.k_n / sqrt(D), probabilities P_n and the
+ * upstream gradient dO_h:
+ *   dP_n = dO_h . v_n,   Delta_h = sum_n P_n dP_n  (= dO_h . O_h),
+ *   dS_n = P_n (dP_n - Delta_h),
+ *   dQ_h = sum_n dS_n k_n / sqrt(D),
+ *   dK_n += dS_n q_h / sqrt(D),   dV_n += P_n dO_h   (summed over every unit
+ *   and head that sees key n).
+ * These are the derivatives of softmax attention (chain rule through the
+ * softmax: dS = P * (dP - rowsum(P * dP))).
+ *
+ * kblocks: optional (b, g, t) triples; when given, dK/dV are accumulated only
+ * for the keys of those blocks, into dK/dV laid out [n_kblocks, bs, D];
+ * otherwise into [B, N, G, D].  dK/dV are accumulated (the caller zeroes
+ * them); dQ [n_units, H/G, D] is written.  Threads keep private partial sums
+ * that are added in thread order at the end.
+ */
+typedef struct {
+    job_t base;
+    const uint16_t *dO;
+    const int64_t *kblocks;
+    int64_t n_kblocks;
+    double *dQ;
+    double *dK, *dV;     /* this thread's partial sums */
+    int64_t kv_elems;
+} bjob_t;
+
+/* Position of key n of (b, g) in the dK/dV arrays, or -1 if filtered out. */
+static int64_t kv_pos(const bjob_t *j, int64_t b, int64_t g, int64_t n) {
+    const job_t *J = &j->base;
+    if (!j->kblocks) return ((b * J->N + n) * J->G + g) * J->D;
+    const int64_t t = n / J->bs;
+    for (int64_t i = 0; i < j->n_kblocks; ++i)
+        if (j->kblocks[3 * i] == b && j->kblocks[3 * i + 1] == g && j->kblocks[3 * i + 2] == t)
+            return (i * J->bs + (n - t * J->bs)) * J->D;
+    return -1;
+}
+
+static void *bworker(void *arg) {
+    bjob_t *j = (bjob_t *)arg;
+    job_t *J = &j->base;
+    const int64_t NB = (J->N + J->bs - 1) / J->bs;
+    const int64_t gs = J->H / J->G, D = J->D;
+    scratch_t w;
+    double *fwdO = (double *)malloc(sizeof(double) * (size_t)(gs * D));
+    double *fwdL = (double *)malloc(sizeof(double) * (size_t)gs);
+    double *dOd = (double *)malloc(sizeof(double) * (size_t)(gs * D));
+    double *dP = (double *)malloc(sizeof(double) * (size_t)(gs * J->N));
+    double *delta = (double *)malloc(sizeof(double) * (size_t)gs);
+    w.mark = (unsigned char *)malloc((size_t)NB);
+    w.keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)J->N);
+    w.score = (double *)malloc(sizeof(double) * (size_t)(gs * J->N));
+    w.qd = (double *)malloc(sizeof(double) * (size_t)(gs * D));
+    w.kd = (double *)malloc(sizeof(double) * (size_t)D);
+    w.mu = (double *)malloc(sizeof(double) * (size_t)gs);
+    w.z = (double *)malloc(sizeof(double) * (size_t)gs);
+    if (!fwdO || !fwdL || !dOd || !dP || !delta || !w.mark || !w.keys || !w.score || !w.qd || !w.kd || !w.mu || !w.z) {
+        J->error = 1;
+    } else {
+        const double scale = 1.0 / sqrt((double)D);
+        /* The forward pass of each unit is recomputed by one_unit into a
+           private O/LSE slot; the job's outputs are redirected there. */
+        job_t fj = *J;
+        fj.O = fwdO;
+        fj.LSE = fwdL;
+        for (int64_t u = J->thread_id; u < J->n_units; u += J->n_threads) {
+            const int64_t b = J->units[3 * u], m = J->units[3 * u + 1], g = J->units[3 * u + 2];
+            int64_t one[3] = {b, m, g};
+            fj.units = one;
+            /* Forward of the unit: scaled scores in w.score, visible keys in
+               w.keys, decoded queries in w.qd, O and LSE in fwdO / fwdL. */
+            const int64_t nk = one_unit(&fj, 0, &w);
+            for (int64_t i = 0; i < gs; ++i) {
+                const uint16_t *src = j->dO + ((b * J->M + m) * J->H + g * gs + i) * D;
+                for (int64_t d = 0; d < D; ++d) dOd[i * D + d] = g_half[src[d]];
+            }
+            /* dP and Delta. P_n = exp(s_n - LSE). */
+            for (int64_t i = 0; i < gs; ++i) delta[i] = 0.0;
+            for (int64_t s = 0; s < nk; ++s) {
+                const uint16_t *v = J->V + ((b * J->N + w.keys[s]) * J->G + g) * D;
+                for (int64_t d = 0; d < D; ++d) w.kd[d] = g_half[v[d]];
+                for (int64_t i = 0; i < gs; ++i) {
+                    double acc = 0.0;
+                    for (int64_t d = 0; d < D; ++d) acc += dOd[i * D + d] * w.kd[d];
+                    dP[i * J->N + s] = acc;
+                    delta[i] += exp(w.score[i * J->N + s] - fwdL[i]) * acc;
+                }
+            }
+            double *dq = j->dQ + u * gs * D;
+            for (int64_t e = 0; e < gs * D; ++e) dq[e] = 0.0;
+            for (int64_t s = 0; s < nk; ++s) {
+                const int64_t n = w.keys[s];
+                const uint16_t *k = J->K + ((b * J->N + n) * J->G + g) * D;
+                for (int64_t d = 0; d < D; ++d) w.kd[d] = g_half[k[d]];
+                const int64_t pos = kv_pos(j, b, g, n);
+                for (int64_t i = 0; i < gs; ++i) {
+                    const double P = exp(w.score[i * J->N + s] - fwdL[i]);
+                    const double dS = P * (dP[i * J->N + s] - delta[i]);
+                    for (int64_t d = 0; d < D; ++d) dq[i * D + d] += dS * w.kd[d] * scale;
+                    if (pos >= 0) {
+                        for (int64_t d = 0; d < D; ++d) {
+                            j->dK[pos + d] += dS * w.qd[i * D + d] * scale;
+                            j->dV[pos + d] += P * dOd[i * D + d];
+                        }
+                    }
+                }
+            }
+        }
+    }
+    free(fwdO); free(fwdL); free(dOd); free(dP); free(delta);
+    free(w.mark); free(w.keys); free(w.score); free(w.qd); free(w.kd); free(w.mu); free(w.z);
+    return NULL;
+}
+
+int nsa_oracle_bwd_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const int32_t *block_indices,
+                         const uint16_t *dO, int64_t B, int64_t M, int64_t N, int64_t H, int64_t G, int64_t D,
+                         int64_t block_size, int64_t T, const int64_t *units, int64_t n_units,
+                         const int64_t *kblocks, int64_t n_kblocks, double *dQ, double *dK, double *dV,
+                         int n_threads) {
+    if (!Q || !K || !V || !dO || !units || !dQ || !dK || !dV) return -1;
+    if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1 || block_size < 1 || T < 1) return -1;
+    if (H % G) return -1;
+    for (int64_t u = 0; u < n_units; ++u) {
+        if (units[3 * u] < 0 || units[3 * u] >= B || units[3 * u + 1] < 0 || units[3 * u + 1] >= M ||
+            units[3 * u + 2] < 0 || units[3 * u + 2] >= G)
+            return -1;
+    }
+    pthread_once(&g_half_once, fill_half_table);
+    if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (n_threads < 1) n_threads = 1;
+    if (n_units < n_threads) n_threads = n_units > 0 ? (int)n_units : 1;
+    const int64_t kv_elems = kblocks ? n_kblocks * block_size * D : B * N * G * D;
+    bjob_t *jobs = (bjob_t *)calloc((size_t)n_threads, sizeof(bjob_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    int rc = 0;
+    for (int i = 0; i < n_threads; ++i) {
+        bjob_t *j = &jobs[i];
+        job_t *J = &j->base;
+        J->Q = Q; J->K = K; J->V = V; J->idx = block_indices;
+        J->B = B; J->M = M; J->N = N; J->H = H; J->G = G; J->D = D;
+        J->bs = block_size; J->T = T;
+        J->units = units; J->n_units = n_units;
+        J->thread_id = i; J->n_threads = n_threads;
+        j->dO = dO; j->kblocks = kblocks; j->n_kblocks = n_kblocks; j->dQ = dQ; j->kv_elems = kv_elems;
+        j->dK = (double *)calloc((size_t)kv_elems, sizeof(double));
+        j->dV = (double *)calloc((size_t)kv_elems, sizeof(double));
+        if (!j->dK || !j->dV) rc = -1;
+    }
+    int started = 0;
+    if (rc == 0) {
+        for (int i = 0; i < n_threads; ++i) {
+            if (pthread_create(&th[i], NULL, bworker, &jobs[i]) != 0) {
+                rc = -1;
+                break;
+            }
+            started++;
+        }
+    }
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    for (int i = 0; i < started; ++i) {
+        if (jobs[i].base.error) rc = -1;
+        for (int64_t e = 0; rc == 0 && e < kv_elems; ++e) {
+            dK[e] += jobs[i].dK[e];
+            dV[e] += jobs[i].dV[e];
+        }
+    }
+    for (int i = 0; i < n_threads; ++i) {
+        free(jobs[i].dK);
+        free(jobs[i].dV);
+    }
+    free(jobs);
+    free(th);
+    return rc;
 }
