@@ -1,8 +1,9 @@
 """Thin ctypes binding of libnsa_sel.so and libnsa_gather_probe.so.
 
-``nsa_sel_fwd``, ``nsa_dense_fwd`` and ``nsa_sel_status_string`` mirror the C
-entry points one to one (pointers may be given as ints or as torch tensors);
-``sel_attn_fwd`` and ``dense_attn_fwd`` are conveniences that check torch
+``nsa_sel_fwd``, ``nsa_sel_bwd``, ``nsa_sel_bwd_workspace_size``,
+``nsa_dense_fwd`` and ``nsa_sel_status_string`` mirror the C entry points one
+to one (pointers may be given as ints or as torch tensors); ``sel_attn_fwd``,
+``sel_attn_bwd`` and ``dense_attn_fwd`` are conveniences that check torch
 tensors, allocate the outputs and call the entry point on the current stream.  ``nsa_gather_probe`` mirrors the
 measurement probe of include/nsa_gather_probe.h.  All arithmetic happens in the
 HIP kernels; when a library is missing every call into it raises.
@@ -26,9 +27,11 @@ NSA_SEL_ERR_ALIGN = 4
 NSA_SEL_ERR_RANGE = 5
 NSA_SEL_ERR_ALIAS = 6
 NSA_SEL_ERR_HIP = 7
+NSA_SEL_ERR_WORKSPACE = 8
 
 EXPORTED = ("nsa_sel_fwd", "nsa_sel_status_string")
 DENSE_EXPORTED = ("nsa_dense_fwd",)
+BWD_EXPORTED = ("nsa_sel_bwd", "nsa_sel_bwd_workspace_size")
 PROBE_EXPORTED = ("nsa_gather_probe",)
 
 _lib = None
@@ -55,6 +58,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nsa_sel_status_string.restype = ctypes.c_char_p
     lib.nsa_dense_fwd.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
     lib.nsa_dense_fwd.restype = ci
+    lib.nsa_sel_bwd_workspace_size.argtypes = [ci] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.nsa_sel_bwd_workspace_size.restype = ci
+    lib.nsa_sel_bwd.argtypes = [vp] * 11 + [ctypes.c_size_t] + [ci] * 8 + [vp]
+    lib.nsa_sel_bwd.restype = ci
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -111,6 +118,76 @@ def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, st
         stream = torch.cuda.current_stream(q.device).cuda_stream
     nsa_sel_fwd(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
     return out, lse
+
+
+def nsa_sel_bwd_workspace_size_raw(B, M, N, H, G, D, block_size, T):
+    """Calls the C entry point; returns (status, bytes)."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    rc = lib.nsa_sel_bwd_workspace_size(int(B), int(M), int(N), int(H), int(G), int(D), int(block_size), int(T),
+                                        ctypes.byref(n))
+    return rc, n.value
+
+
+def nsa_sel_bwd_workspace_size(B, M, N, H, G, D, block_size, T) -> int:
+    """Workspace bytes of nsa_sel_bwd; raises NsaSelError on a nonzero status."""
+    rc, n = nsa_sel_bwd_workspace_size_raw(B, M, N, H, G, D, block_size, T)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+    return n
+
+
+def nsa_sel_bwd_raw(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, B, M, N, H, G, D,
+                    block_size, T, stream=0) -> int:
+    """Calls the C entry point and returns its status code unchanged."""
+    lib = load_library()
+    return lib.nsa_sel_bwd(_addr(Q), _addr(K), _addr(V), _addr(block_indices), _addr(O), _addr(LSE), _addr(dO),
+                           _addr(dQ), _addr(dK), _addr(dV), _addr(workspace), int(workspace_bytes), int(B), int(M),
+                           int(N), int(H), int(G), int(D), int(block_size), int(T), ctypes.c_void_p(_addr(stream)))
+
+
+def nsa_sel_bwd(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, B, M, N, H, G, D,
+                block_size, T, stream=0) -> None:
+    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
+    rc = nsa_sel_bwd_raw(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, B, M, N, H, G,
+                         D, block_size, T, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def sel_attn_bwd(q, k, v, block_indices, out, lse, dout, block_size: int, workspace=None, stream=None):
+    """Gradients of sel_attn_fwd: q/out/dout [B,M,H,D] fp16, k/v [B,N,G,D]
+    fp16, block_indices [B,M,G,T] int32, lse [B,H,M] fp32, all contiguous CUDA
+    tensors.  workspace: optional uint8 CUDA tensor of at least
+    nsa_sel_bwd_workspace_size bytes.  Returns (dQ, dK, dV) in fp32."""
+    import torch
+
+    for name, t, dt in (("q", q, torch.float16), ("k", k, torch.float16), ("v", v, torch.float16),
+                        ("block_indices", block_indices, torch.int32), ("out", out, torch.float16),
+                        ("dout", dout, torch.float16)):
+        if not isinstance(t, torch.Tensor) or t.dtype != dt or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-d {dt} tensor")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 GPU tensor")
+    B, M, H, D = q.shape
+    _, N, G, _ = k.shape
+    T = block_indices.shape[3]
+    if ((k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape or tuple(block_indices.shape[:3]) != (B, M, G)
+            or out.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, H, M)):
+        raise ValueError("inconsistent shapes")
+    nbytes = nsa_sel_bwd_workspace_size(B, M, N, H, G, D, block_size, T)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty((B, M, H, D), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, N, G, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, N, G, D), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    nsa_sel_bwd(q, k, v, block_indices, out, lse, dout, dq, dk, dv, workspace, workspace.numel(), B, M, N, H, G, D,
+                block_size, T, stream)
+    return dq, dk, dv
 
 
 def nsa_dense_fwd_raw(Q, K, V, O, LSE, B, M, N, H, G, D, stream=0) -> int:

@@ -222,6 +222,8 @@ extern "C" const char *nsa_sel_status_string(int status) {
         case NSA_SEL_ERR_RANGE: return "nsa_sel: problem size exceeds the supported index range";
         case NSA_SEL_ERR_ALIAS: return "nsa_sel: an output buffer overlaps an input or the other output";
         case NSA_SEL_ERR_HIP: return "nsa_sel: the HIP runtime reported an error at kernel launch";
+        case NSA_SEL_ERR_WORKSPACE:
+            return "nsa_sel: the backward workspace is NULL, not 256-byte aligned or smaller than required";
         default: return "nsa_sel: unknown status";
     }
 }

@@ -1,0 +1,867 @@
+// NSA selection-attention backward for AMD MI355X (gfx950, CDNA4).
+//
+// Operation (include/nsa_sel_bwd.h): the gradients dQ, dK, dV of the
+// selection attention of nsa_sel_fwd, from the forward's O and LSE and the
+// upstream gradient dO.  Wave issue "[wave] NSA: selection attention forward
+// kernel", section Requirements, names this pass as what the returned LSE is
+// for: P = exp(S - LSE) is recomputed block by block without a softmax pass.
+//
+// The work splits by who owns each gradient:
+//  * dQ is a sum over the selected keys of one query, so it is computed
+//    query-major, exactly on the forward's slot layout: a wavefront carries
+//    a slot of consecutive queries of one (b, g), merges their index rows and
+//    stages each selected 32-key sub-block once.  Per sub-block it forms
+//    S^T = K Q^T and dP^T = V dO^T (v_mfma_f32_16x16x32_f16, keys on the MFMA
+//    rows), P^T = exp2(S^T log2(e)/sqrt(D) - LSE log2(e)), dS^T = P^T (dP^T -
+//    Delta), and accumulates dQ^T += K^T dS^T with K^T from the transposing
+//    LDS reads and dS^T straight from registers.  The same pass computes
+//    Delta = dO . O per row and stores (LSE log2(e), Delta) for the key pass.
+//  * dK and dV are sums over the queries that selected a key, so they are
+//    computed key-major.  The index rows are first inverted into a bitmap per
+//    key block (bit m of row (b, g, t) set when query m selects block t),
+//    without atomics on global memory; each key block's query list is cut
+//    into items of at most qc queries.  A workgroup takes one item: its
+//    wavefronts own 16 keys each, with their K and V fragments in registers,
+//    and stream the item's queries as 32-row tiles (row = query, head) of Q,
+//    dO and the row statistics, gathered global -> LDS with direct-to-LDS
+//    loads through a ring shared by the workgroup.  Per tile: S = Q K^T,
+//    dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS with the
+//    transposed row operands from ds_read_b64_tr_b16.
+//  * A key block cut into several items writes one partial sum per item; a
+//    last pass adds them in item order (and writes zeros for key blocks no
+//    query selected), so results do not depend on scheduling.
+#include "nsa_sel_common.h"
+#include "nsa_sel_bwd.h"
+
+#include <algorithm>
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// dQ pass (query-major).
+
+struct DqArgs {
+    const _Float16 *O;
+    const _Float16 *dO;
+    const float *LSE;
+    float *dQ;
+    float2 *rowstat;  // [B, H, M]: (LSE * log2 e, Delta)
+    float scale;      // 1 / sqrt(D)
+};
+
+// One 32-key sub-block of the dQ pass for one 16-column tile (lane l holds
+// column l%16, keys key0 + 16*kt + 4*(l/16) + i).
+//   causal: some key may lie past the column's last visible key lim
+//   col_on: the column's query selected the block (else P = 0)
+template <int SBS, int D>
+__device__ __forceinline__ void dq_block(const half8 (&kf)[SBS / 16][D / 32], const half8 (&vf)[SBS / 16][D / 32],
+                                         const half4 (&kt)[SBS / 32][D / 32][2][2], const half8 (&qf)[D / 32],
+                                         const half8 (&df)[D / 32], int key0, bool causal, bool col_on, int lim,
+                                         float scale_log2, float lse2, float delta, float4v (&acc)[D / 32][2],
+                                         int q4) {
+    constexpr int KT = SBS / 16;
+    constexpr int DC = D / 32;
+    float4v s[KT], dp[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        s[k] = float4v{0.f, 0.f, 0.f, 0.f};
+        dp[k] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            s[k] = mfma_16x16x32(kf[k][c], qf[c], s[k]);
+            dp[k] = mfma_16x16x32(vf[k][c], df[c], dp[k]);
+        }
+    }
+    // A column that did not select the block gets P = exp2(-inf) = 0.
+    const float m_exp = (col_on && lse2 != -INFINITY) ? lse2 : INFINITY;
+    half4 dsf[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        float4v ds;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float pv = fast_exp2(__builtin_fmaf(s[k][i], scale_log2, -m_exp));
+            if (causal && key0 + k * 16 + q4 * 4 + i > lim) pv = 0.f;
+            ds[i] = pv * (dp[k][i] - delta);
+        }
+        dsf[k] = to_half4(ds);
+    }
+#pragma unroll
+    for (int kc = 0; kc < SBS / 32; ++kc) {
+        const half8 bp = cat8(dsf[2 * kc], dsf[2 * kc + 1]);
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                acc[c][hh] = mfma_16x16x32(cat8(kt[kc][c][hh][0], kt[kc][c][hh][1]), bp, acc[c][hh]);
+    }
+}
+
+// One wavefront slot of the dQ pass: the forward's run_slot with the
+// gradient step in place of the online softmax.
+template <int BS, int SPLIT, int D, int PACK, int NT, class Merger>
+__device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws, int lane, _Float16 *kbuf,
+                                        _Float16 *vbuf) {
+    constexpr int SBS = BS / SPLIT;
+    constexpr int DC = D / 32;
+    constexpr int KT = SBS / 16;
+    constexpr int QW = PACK * NT;
+    const Slot sl = decode_slot(p, ws, QW);
+    const int b = sl.b, g = sl.g, m0 = sl.m0, nq = sl.nq;
+    const int r = lane & 15;
+    const int q4 = lane >> 4;
+    const int h0 = g * p.gs;
+    const int q_in_tile = r / p.gs;
+    const int my_h = h0 + (r - q_in_tile * p.gs);
+    bool live[NT];
+    int my_m[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int qi = nt * PACK + q_in_tile;
+        live[nt] = q_in_tile < PACK && qi < nq;
+        my_m[nt] = m0 + (live[nt] ? qi : 0);
+    }
+
+    Stage<SBS, D> st;
+    init_stage(st, p, b, g, lane);
+
+    // Q^T and dO^T fragments (B operands, lane l: column l%16, head dims
+    // 32*c + 8*(l/16) .. +7), Delta = dO . O per column, and LSE.
+    half8 qf[NT][DC], df[NT][DC];
+    float lse2[NT], delta[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const size_t row = ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + (live[nt] ? my_h : h0)) * D;
+        const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        float dot = 0.f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const half8 xq = __builtin_nontemporal_load((const half8 *)(p.Q + row + c * 32 + q4 * 8));
+            const half8 xd = __builtin_nontemporal_load((const half8 *)(x.dO + row + c * 32 + q4 * 8));
+            const half8 xo = __builtin_nontemporal_load((const half8 *)(x.O + row + c * 32 + q4 * 8));
+            qf[nt][c] = live[nt] ? xq : zero8;
+            df[nt][c] = live[nt] ? xd : zero8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dot = __builtin_fmaf((float)xd[e], (float)xo[e], dot);
+        }
+        delta[nt] = col_sum(live[nt] ? dot : 0.f);
+        const size_t li = ((size_t)b * p.H + (live[nt] ? my_h : h0)) * p.M + my_m[nt];
+        lse2[nt] = x.LSE[li] * kLog2e;
+        if (live[nt] && q4 == 0) x.rowstat[li] = make_float2(lse2[nt], delta[nt]);
+    }
+
+    Merger mg;
+    mg.init(p, b, g, m0, nq, lane);
+
+    float4v acc[NT][DC][2];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            acc[nt][c][0] = float4v{0.f, 0.f, 0.f, 0.f};
+            acc[nt][c][1] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
+
+    constexpr int NI = Stage<SBS, D>::NI;
+    const unsigned tile_bits = (1u << PACK) - 1u;
+
+    // Same pipeline as the forward: K(s1) is issued once K(s0)'s row and
+    // transposed fragments are in registers, V(s1) once V(s0)'s are.
+    half8 kf[KT][DC], vf[KT][DC];
+    half4 kt[SBS / 32][DC][2][2];
+    unsigned a0, a1;
+    const int t_first = mg.next(a0);
+    int s0 = t_first == kDone ? kDone : t_first * SPLIT;
+    if (s0 != kDone) {
+        st.issue(st.rk, kbuf, s0, lane);
+        st.issue(st.rv, vbuf, s0, lane);
+    }
+    while (s0 != kDone) {
+        int s1;
+        if ((s0 + 1) % SPLIT != 0) {
+            s1 = s0 + 1;
+            a1 = a0;
+        } else {
+            const int t1 = mg.next(a1);
+            s1 = t1 == kDone ? kDone : t1 * SPLIT;
+        }
+        const bool has1 = s1 != kDone;
+        __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K(s0) landed
+        Stage<SBS, D>::read(kf, kbuf, r, q4);
+        Stage<SBS, D>::read_vt(kt, kbuf, lane);
+        if (has1) st.issue(st.rk, kbuf, s1, lane);
+        if (has1)
+            __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(s0) landed
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        Stage<SBS, D>::read(vf, vbuf, r, q4);
+        if (has1) st.issue(st.rv, vbuf, s1, lane);
+        const int key0 = s0 * SBS;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const unsigned tb = (a0 >> (nt * PACK)) & tile_bits;
+            if (tb == 0) continue;
+            const int first_m = m0 + nt * PACK;
+            const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
+            const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
+            dq_block<SBS, D>(kf, vf, kt, qf[nt], df[nt], key0, causal, col_on, min(my_m[nt], p.N - 1),
+                             p.scale_log2, lse2[nt], delta[nt], acc[nt], q4);
+        }
+        s0 = s1;
+        a0 = a1;
+    }
+
+    // dQ = dS K / sqrt(D): lane l holds rows d = 32*c + 8*(l/16) + 4*hh + i
+    // of column l%16, i.e. 8 consecutive floats per c.
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (!live[nt]) continue;
+        float *dq = x.dQ + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + my_h) * D;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            __builtin_nontemporal_store(acc[nt][c][0] * x.scale, (float4v *)(dq + c * 32 + q4 * 8));
+            __builtin_nontemporal_store(acc[nt][c][1] * x.scale, (float4v *)(dq + c * 32 + q4 * 8 + 4));
+        }
+    }
+}
+
+template <int BS, int SPLIT, int D, int PACK, int MODE>
+__global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_bwd_dq_kernel(Params p, DqArgs x) {
+    constexpr int SBS = BS / SPLIT;
+    constexpr int WAVES = waves_per_wg(SBS);
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    const int ws = wave_slot<WAVES>(p, wave);
+    if (ws < 0) return;
+    if constexpr (MODE == 0)
+        dq_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>>(p, x, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+    else
+        dq_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, x, ws, lane, kbuf_all[wave],
+                                                                        vbuf_all[wave]);
+}
+
+struct DqKernel {
+    DqArgs x;
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
+        hipLaunchKernelGGL((nsa_sel_bwd_dq_kernel<BS, SPLIT, D, PACK, MODE>), grid, block, 0, stream, p, x);
+    }
+};
+
+// The dQ pass runs one tile per wavefront (mode 0 or 1).
+template <int BS, int D, int PACK>
+hipError_t dq_launch_mode(const DqKernel &f, const Params &p, int cus, hipStream_t stream) {
+    constexpr int SPLIT = BS / 32;
+    return p.mode == 1 ? launch_generations<DqKernel, BS, SPLIT, D, PACK, 1>(f, p, cus, stream)
+                       : launch_generations<DqKernel, BS, SPLIT, D, PACK, 0>(f, p, cus, stream);
+}
+
+template <int BS, int D>
+hipError_t dq_launch_pack(const DqKernel &f, const Params &p, int cus, hipStream_t stream) {
+    if (p.pack == 4) return dq_launch_mode<BS, D, 4>(f, p, cus, stream);
+    if (p.pack == 2) return dq_launch_mode<BS, D, 2>(f, p, cus, stream);
+    return dq_launch_mode<BS, D, 1>(f, p, cus, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Key-major passes: inverted index, dK/dV, reduction.
+
+constexpr int kBitQ = 256;     // queries per bitmap workgroup (8 words)
+constexpr int kBitWin = 512;   // key-block rows per LDS window of the bitmap pass
+constexpr int kRows = 32;      // (query, head) rows per tile of the dK/dV pass
+constexpr int kRing = 3;       // LDS ring depth of the dK/dV pass
+constexpr int kMaxQc = 2048;   // most queries per item
+
+struct Bw {
+    const _Float16 *Q, *K, *V, *dO;
+    const int32_t *idx;
+    float2 *rowstat;    // [B*H*M + 1]; the last entry is the padding row (+inf, 0)
+    unsigned *bits;     // [R][MW]
+    int *row_items;     // [R] items of key block row
+    int *row_first;     // [R] first item of the row
+    int *row_part;      // [R] first partial slot of a row with >= 2 items
+    int *starts;        // [R][kmax] first query of each item
+    int2 *items;        // [cap] (row, k)
+    int *n_items;       // [1]
+    float *part;        // [pcap][2][bs][D] partial dK, dV
+    float *dK, *dV;
+    int B, M, N, H, G, gs, T, bs, NB, MW, R, qc, kmax, cap, pcap, qpt;
+    int sentinel;       // B*H*M
+    float scale, scale_log2;
+};
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int o = 1; o < kWaveSize; o <<= 1) {
+        const int y = __shfl_up(x, o, kWaveSize);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Position of the r-th (0-based) set bit of a word holding more than r.
+__device__ __forceinline__ int nth_bit(unsigned word, int r) {
+    for (int i = 0; i < r; ++i) word &= word - 1u;
+    return __builtin_ctz(word);
+}
+
+// Bitmap of the selections: workgroup (b, g, chunk of 256 queries), one
+// thread per query, OR-ing its counted entries into LDS words (ds_or), then
+// writing rows t = 0 .. (last query of the chunk) / bs of its 8 words.  Words
+// of row t before query t*bs are never read, so nothing else needs clearing.
+__global__ __launch_bounds__(kBitQ) void nsa_sel_bwd_bitmap_kernel(Bw w) {
+    __shared__ unsigned win[kBitWin][kBitQ / 32];
+    const int chunks = (w.M + kBitQ - 1) / kBitQ;
+    const int bg = blockIdx.x / chunks, chunk = blockIdx.x - bg * chunks;
+    const int b = bg / w.G, g = bg - b * w.G;
+    const int tid = threadIdx.x;
+    const int m0 = chunk * kBitQ;
+    const int m = m0 + tid;
+    const bool live = m < w.M;
+    const int cmax = min((min(m0 + kBitQ, w.M) - 1) / w.bs, w.NB - 1);
+    const int cm = live ? m / w.bs : -1;
+    const int32_t *row = w.idx + ((size_t)(b * (size_t)w.M + (live ? m : m0)) * w.G + g) * w.T;
+    const int w0 = chunk * (kBitQ / 32);
+    for (int t0 = 0; t0 <= cmax; t0 += kBitWin) {
+        const int nrows = min(kBitWin, cmax + 1 - t0);
+        for (int e = tid; e < nrows * (kBitQ / 32); e += kBitQ) win[e / (kBitQ / 32)][e % (kBitQ / 32)] = 0u;
+        __syncthreads();
+        if (live) {
+            for (int j = 0; j < w.T; ++j) {
+                const int t = row[j];
+                if (t >= t0 && t < t0 + nrows && t <= cm) atomicOr(&win[t - t0][tid >> 5], 1u << (tid & 31));
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < nrows * (kBitQ / 32); e += kBitQ) {
+            const int tr = e / (kBitQ / 32), wi = e % (kBitQ / 32);
+            if (w0 + wi < w.MW) w.bits[((size_t)bg * w.NB + t0 + tr) * w.MW + w0 + wi] = win[tr][wi];
+        }
+        __syncthreads();
+    }
+}
+
+// Per key-block row: number of selecting queries, cut into items of qc; the
+// first query of item k is the one of rank k*qc.  One wavefront per row.
+__global__ __launch_bounds__(256) void nsa_sel_bwd_count_kernel(Bw w) {
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (row >= w.R) return;
+    const int t = row % w.NB;
+    const unsigned *bits = w.bits + (size_t)row * w.MW;
+    int total = 0;
+    for (int wb = t * w.bs / 32; wb < w.MW; wb += kWaveSize) {
+        const int wi = wb + lane;
+        const unsigned word = wi < w.MW ? bits[wi] : 0u;
+        const int pc = __popc(word);
+        const int incl = wave_incl_scan(pc, lane);
+        const int lo = total + incl - pc, hi = total + incl;
+        const int k = (lo + w.qc - 1) / w.qc;  // qc >= 32: at most one item starts in a word
+        if (pc > 0 && k * w.qc < hi && k < w.kmax)
+            w.starts[(size_t)row * w.kmax + k] = 32 * wi + nth_bit(word, k * w.qc - lo);
+        total += __shfl(incl, kWaveSize - 1, kWaveSize);
+    }
+    if (lane == 0) w.row_items[row] = (total + w.qc - 1) / w.qc;
+}
+
+// Exclusive scans of the item counts (item list) and of the counts of rows
+// with two or more items (partial slots); one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void nsa_sel_bwd_scan_kernel(Bw w) {
+    __shared__ int wsum[2][16];
+    const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid >> 6;
+    int carry_i = 0, carry_p = 0;
+    for (int base = 0; base < w.R; base += 1024) {
+        const int row = base + tid;
+        const int n = row < w.R ? w.row_items[row] : 0;
+        const int np = n >= 2 ? n : 0;
+        const int si = wave_incl_scan(n, lane), sp = wave_incl_scan(np, lane);
+        if (lane == kWaveSize - 1) {
+            wsum[0][wave] = si;
+            wsum[1][wave] = sp;
+        }
+        __syncthreads();
+        int off_i = carry_i, off_p = carry_p, tot_i = 0, tot_p = 0;
+        for (int v = 0; v < 16; ++v) {
+            const int a = wsum[0][v], c = wsum[1][v];
+            if (v < wave) {
+                off_i += a;
+                off_p += c;
+            }
+            tot_i += a;
+            tot_p += c;
+        }
+        off_i += si - n;
+        off_p += sp - np;
+        if (row < w.R) {
+            w.row_first[row] = off_i;
+            w.row_part[row] = off_p;
+            for (int k = 0; k < n; ++k)
+                if (off_i + k < w.cap) w.items[off_i + k] = make_int2(row, k);
+        }
+        carry_i += tot_i;
+        carry_p += tot_p;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        *w.n_items = min(carry_i, w.cap);
+        w.rowstat[w.sentinel] = make_float2(INFINITY, 0.f);
+    }
+}
+
+typedef __attribute__((address_space(3))) _Float16 lds_half_t;
+
+__device__ __forceinline__ unsigned lds_addr(const void *p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// LDS reads issued as inline asm with their own lgkmcnt wait: the compiler
+// would otherwise guard them with vmcnt(0), waiting for every copy in flight.
+__device__ __forceinline__ int lds_read_int(unsigned a) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+    return v;
+}
+
+template <int BS, int D>
+struct KvLds {
+    _Float16 q[kRing][kRows * D];
+    _Float16 d[kRing][kRows * D];
+    float st[kRing][BS / 16][2 * kRows];
+    int list[kMaxQc];
+    int nq;
+};
+
+// dK/dV of one item: key block (b, g, t), queries of rank k*qc .. k*qc+qc-1
+// among those that selected it.  Wavefront v owns keys t*BS + 16v .. +15.
+template <int BS, int D>
+__global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(Bw w) {
+    constexpr int WAVES = BS / 16;
+    constexpr int DC = D / 32;
+    using St = Stage<kRows, D>;
+    constexpr int NI = St::NI;  // copy instructions per tile and tensor
+    static_assert(NI % WAVES == 0, "copy instructions must split evenly");
+    constexpr int CPW = NI / WAVES;     // per wavefront, per tensor
+    constexpr int IPW = 2 * CPW + 1;    // per wavefront and tile, with the row statistics
+    __shared__ __attribute__((aligned(16))) KvLds<BS, D> L;
+
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_items = *w.n_items;
+    const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
+    const int loc = blockIdx.x / kNumXcd;
+    const int item = (blockIdx.x % kNumXcd) * per_xcd + loc;
+    if (loc >= per_xcd || item >= n_items) return;  // the whole workgroup
+    const int2 it = w.items[item];
+    const int row = it.x, k = it.y;
+    const int bg = row / w.NB, t = row - bg * w.NB;
+    const int b = bg / w.G, g = bg - b * w.G;
+    const int row_n = w.row_items[row];
+    const int m_lo = w.starts[(size_t)row * w.kmax + k];
+    const int m_hi = k + 1 < row_n ? w.starts[(size_t)row * w.kmax + k + 1] : w.M;
+
+    // The item's queries, ascending, into LDS (wavefront 0).
+    if (wave == 0) {
+        const unsigned *bits = w.bits + (size_t)row * w.MW;
+        const int wlo = m_lo >> 5, whi = (m_hi - 1) >> 5;
+        int cnt = 0;
+        for (int wb = wlo; wb <= whi; wb += kWaveSize) {
+            const int wi = wb + lane;
+            unsigned word = wi <= whi ? bits[wi] : 0u;
+            if (wi == wlo) word &= ~0u << (m_lo & 31);
+            if (wi == whi && (m_hi & 31)) word &= (1u << (m_hi & 31)) - 1u;
+            const int pc = __popc(word);
+            const int incl = wave_incl_scan(pc, lane);
+            int pos = cnt + incl - pc;
+            while (word) {
+                if (pos < kMaxQc) L.list[pos] = 32 * wi + __builtin_ctz(word);
+                ++pos;
+                word &= word - 1u;
+            }
+            cnt += __shfl(incl, kWaveSize - 1, kWaveSize);
+        }
+        if (lane == 0) L.nq = min(cnt, kMaxQc);
+    }
+    __syncthreads();
+    const int nq = L.nq;
+
+    // This wavefront's keys: K and V fragments as MFMA B operands (lane l:
+    // key key0 + l%16, head dims 32*c + 8*(l/16) .. +7); keys past N are
+    // clamped here and masked below.
+    const int r = lane & 15, q4 = lane >> 4;
+    const int key0 = t * BS + wave * 16;
+    const int my_key = key0 + r;
+    half8 kb[DC], vb[DC];
+    {
+        const size_t kr = ((size_t)(b * (size_t)w.N + min(my_key, w.N - 1)) * w.G + g) * D;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            kb[c] = *(const half8 *)(w.K + kr + c * 32 + q4 * 8);
+            vb[c] = *(const half8 *)(w.V + kr + c * 32 + q4 * 8);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // fragments in registers before the copies start counting
+
+    const int h0 = g * w.gs;
+    const int qpt = w.qpt;
+    const int ntiles = (nq + qpt - 1) / qpt;
+    const size_t qb = (size_t)b * w.M * w.H * D;
+    const unsigned q_bytes = (unsigned)((size_t)w.M * w.H * D * 2);
+    const __amdgpu_buffer_rsrc_t rq =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(w.Q + qb), (short)0, (int)q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(w.dO + qb), (short)0, (int)q_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)w.rowstat, (short)0, (int)((unsigned)(w.sentinel + 1) * 8u), 0x00020000);
+    const unsigned list_a = lds_addr(L.list);
+
+    // Row rr of tile i: query slot rr / gs, head rr % gs; rows past the
+    // item's queries (or past qpt * gs) are padding.
+    auto row_query = [&](int i, int rr, int &m, int &h) -> bool {
+        const int slot = rr / w.gs;
+        const int qi = i * qpt + slot;
+        const bool valid = slot < qpt && qi < nq;
+        m = lds_read_int(list_a + 4u * (unsigned)(valid ? qi : 0));
+        h = h0 + (valid ? rr - slot * w.gs : 0);
+        return valid;
+    };
+    auto issue = [&](int i) {
+        const int slot = i % kRing;
+#pragma unroll
+        for (int kk = 0; kk < CPW; ++kk) {
+            const int j = wave + kk * WAVES;
+            const int rr = j * St::RPI + lane / St::LPR;
+            int m, h;
+            row_query(i, rr, m, h);
+            const unsigned off = (unsigned)(((size_t)m * w.H + h) * D * 2) +
+                                 (unsigned)(((lane % St::LPR) ^ St::swz(rr)) * 16);
+            St::copy(rq, (lds_half_t *)L.q[slot], off, 0u, j);
+            St::copy(rd, (lds_half_t *)L.d[slot], off, 0u, j);
+        }
+        {
+            int m, h;
+            const bool valid = row_query(i, lane >> 1, m, h);
+            const unsigned e = valid ? (unsigned)(((size_t)b * w.H + h) * w.M + m) : (unsigned)w.sentinel;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)L.st[slot][wave],
+                                                     4, e * 8u + (unsigned)(lane & 1) * 4u, 0, 0, 0);
+        }
+    };
+
+    float4v dk[DC][2], dv[DC][2];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            dk[c][hh] = float4v{0.f, 0.f, 0.f, 0.f};
+            dv[c][hh] = float4v{0.f, 0.f, 0.f, 0.f};
+        }
+
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i)
+        if (i < ntiles) issue(i);
+
+    for (int i = 0; i < ntiles; ++i) {
+        // Own copies of tile i landed, then everyone's; the slot of tile i-1
+        // is free once all wavefronts passed the barrier.
+        if (i + kRing - 2 < ntiles)
+            __builtin_amdgcn_s_waitcnt(wait_vm(IPW * (kRing - 2)));
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        lds_barrier();
+        if (i + kRing - 1 < ntiles) issue(i + kRing - 1);
+        const int slot = i % kRing;
+
+        half8 qa[2][DC], da[2][DC];
+        St::read(qa, L.q[slot], r, q4);
+        St::read(da, L.d[slot], r, q4);
+        // S = Q K^T and dP = dO V^T: lane l holds rows 16*rt + 4*(l/16) + j
+        // of key my_key.
+        float4v s[2], dp[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            s[rt] = float4v{0.f, 0.f, 0.f, 0.f};
+            dp[rt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                s[rt] = mfma_16x16x32(qa[rt][c], kb[c], s[rt]);
+                dp[rt] = mfma_16x16x32(da[rt][c], vb[c], dp[rt]);
+            }
+        }
+        // Row statistics (LSE log2 e, Delta) of those 8 rows.
+        float4v sa[2][2];
+        {
+            const unsigned a = lds_addr(L.st[slot][wave]) + (unsigned)(q4 * 4 * 8);
+            asm volatile(
+                "ds_read_b128 %0, %4 offset:0\n"
+                "ds_read_b128 %1, %4 offset:16\n"
+                "ds_read_b128 %2, %4 offset:128\n"
+                "ds_read_b128 %3, %4 offset:144\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(sa[0][0]), "=&v"(sa[0][1]), "=&v"(sa[1][0]), "=&v"(sa[1][1])
+                : "v"(a)
+                : "memory");
+        }
+        // Keys past a row's query (or past N) occur only in tiles that start
+        // before the wavefront's last key.
+        const int m_first = __builtin_amdgcn_readfirstlane(lds_read_int(list_a + 4u * (unsigned)(i * qpt)));
+        const bool need_mask = m_first < key0 + 15 || key0 + 16 > w.N;
+        half4 pf[2], dsf[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            float4v pv, ds;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float lse2 = sa[rt][j >> 1][(j & 1) * 2];
+                const float delta = sa[rt][j >> 1][(j & 1) * 2 + 1];
+                float pj = fast_exp2(__builtin_fmaf(s[rt][j], w.scale_log2, -lse2));
+                if (need_mask) {
+                    int m, h;
+                    const bool valid = row_query(i, 16 * rt + 4 * q4 + j, m, h);
+                    if (!valid || my_key > min(m, w.N - 1)) pj = 0.f;
+                }
+                pv[j] = pj;
+                ds[j] = pj * (dp[rt][j] - delta);
+            }
+            pf[rt] = to_half4(pv);
+            dsf[rt] = to_half4(ds);
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS (rows of the tile on the MFMA k
+        // axis, in the order of the transposing reads).
+        half4 qt[1][DC][2][2], dt[1][DC][2][2];
+        St::read_vt(dt, L.d[slot], lane);
+        St::read_vt(qt, L.q[slot], lane);
+        const half8 bp = cat8(pf[0], pf[1]);
+        const half8 bds = cat8(dsf[0], dsf[1]);
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                dv[c][hh] = mfma_16x16x32(cat8(dt[0][c][hh][0], dt[0][c][hh][1]), bp, dv[c][hh]);
+                dk[c][hh] = mfma_16x16x32(cat8(qt[0][c][hh][0], qt[0][c][hh][1]), bds, dk[c][hh]);
+            }
+    }
+
+    // Lane l holds dK^T, dV^T rows d = 32*c + 8*(l/16) + 4*hh + i of key
+    // my_key: straight to the outputs when the item is the key block's only
+    // one, else to the item's partial slot.
+    if (my_key < w.N) {
+        float *pk, *pv;
+        if (row_n == 1) {
+            const size_t o = ((size_t)(b * (size_t)w.N + my_key) * w.G + g) * D;
+            pk = w.dK + o;
+            pv = w.dV + o;
+        } else {
+            const int psi = w.row_part[row] + k;  // < pcap by the plan's bound
+            const size_t ps = (size_t)(psi < w.pcap ? psi : w.pcap - 1);
+            pk = w.part + ((ps * 2 + 0) * BS + (my_key - t * BS)) * D;
+            pv = w.part + ((ps * 2 + 1) * BS + (my_key - t * BS)) * D;
+        }
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            __builtin_nontemporal_store(dk[c][0] * w.scale, (float4v *)(pk + c * 32 + q4 * 8));
+            __builtin_nontemporal_store(dk[c][1] * w.scale, (float4v *)(pk + c * 32 + q4 * 8 + 4));
+            __builtin_nontemporal_store(dv[c][0], (float4v *)(pv + c * 32 + q4 * 8));
+            __builtin_nontemporal_store(dv[c][1], (float4v *)(pv + c * 32 + q4 * 8 + 4));
+        }
+    }
+}
+
+// Key blocks with no item get zeros; those with several items the sum of
+// their partials in item order.  One workgroup per key block row.
+template <int BS, int D>
+__global__ __launch_bounds__(256) void nsa_sel_bwd_reduce_kernel(Bw w) {
+    const int row = blockIdx.x;
+    const int n = w.row_items[row];
+    if (n == 1) return;
+    const int bg = row / w.NB, t = row - bg * w.NB;
+    const int b = bg / w.G, g = bg - b * w.G;
+    const int p0 = n >= 2 ? w.row_part[row] : 0;
+    if (p0 + n > w.pcap) return;  // cannot happen: the plan bounds the partial slots
+    constexpr int V4 = BS * D / 4;  // float4 per tensor
+    for (int e = threadIdx.x; e < 2 * V4; e += 256) {
+        const int tensor = e / V4, f = e - tensor * V4;
+        const int key = f / (D / 4), d4 = f - key * (D / 4);
+        const int na = t * BS + key;
+        if (na >= w.N) continue;
+        float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < n; ++j)
+            acc += __builtin_nontemporal_load((const float4v *)(w.part + ((size_t)(p0 + j) * 2 + tensor) * BS * D) + f);
+        float *dst = (tensor ? w.dV : w.dK) + ((size_t)(b * (size_t)w.N + na) * w.G + g) * D;
+        __builtin_nontemporal_store(acc, (float4v *)dst + d4);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side planning.
+
+struct BwdPlan {
+    int NB, MW, R, qc, kmax, qpt;
+    int64_t cap, pcap;
+    size_t off_rowstat, off_bits, off_row_items, off_row_first, off_row_part, off_starts, off_items, off_nitems,
+        off_part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Sizes of the workspace for (B, M, N, H, G, D, bs, T); p must hold the
+// checked sizes.  Returns NSA_SEL_OK or NSA_SEL_ERR_RANGE.
+int bwd_plan(const Params &p, int D, int bs, BwdPlan &pl) {
+    pl.NB = p.NB;
+    pl.MW = (p.M + 31) / 32;
+    const int64_t R = (int64_t)p.B * p.G * p.NB;
+    if (R > INT_MAX) return NSA_SEL_ERR_RANGE;
+    pl.R = (int)R;
+    int qc = (8192 / p.gs) / 32 * 32;
+    qc = qc < 32 ? 32 : qc > kMaxQc ? kMaxQc : qc;
+    pl.qc = qc;
+    pl.kmax = (p.M + qc - 1) / qc;
+    pl.qpt = kRows / p.gs;
+    // Distinct (query, block) pairs per (b, g): query m counts at most
+    // min(T, m / bs + 1, NB) blocks.
+    int64_t pairs = 0;
+    for (int64_t c = 0; c * bs < p.M; ++c) {
+        const int64_t nqc = std::min<int64_t>(bs, p.M - c * bs);
+        pairs += nqc * std::min<int64_t>(std::min<int64_t>(p.T, c + 1), p.NB);
+    }
+    const int64_t bgs = (int64_t)p.B * p.G;
+    pl.cap = bgs * (p.NB + (pairs + qc - 1) / qc);
+    pl.pcap = bgs * ((2 * pairs + qc - 1) / qc) + 1;
+    if (pl.cap > INT_MAX || pl.pcap > INT_MAX || R * pl.kmax > INT_MAX) return NSA_SEL_ERR_RANGE;
+    const int64_t rows = (int64_t)p.B * p.H * p.M;
+    if (rows + 1 > (int64_t)1 << 28) return NSA_SEL_ERR_RANGE;          // rowstat byte offsets in 32 bits
+    if ((int64_t)p.M * p.H * D * 2 > (int64_t)UINT_MAX) return NSA_SEL_ERR_RANGE;  // Q / dO offsets of one batch
+    size_t o = 0;
+    pl.off_rowstat = o;
+    o = align256(o + (size_t)(rows + 1) * 8);
+    pl.off_bits = o;
+    o = align256(o + (size_t)R * pl.MW * 4);
+    pl.off_row_items = o;
+    o = align256(o + (size_t)R * 4);
+    pl.off_row_first = o;
+    o = align256(o + (size_t)R * 4);
+    pl.off_row_part = o;
+    o = align256(o + (size_t)R * 4);
+    pl.off_starts = o;
+    o = align256(o + (size_t)R * pl.kmax * 4);
+    pl.off_items = o;
+    o = align256(o + (size_t)pl.cap * 8);
+    pl.off_nitems = o;
+    o = align256(o + 4);
+    pl.off_part = o;
+    o = align256(o + (size_t)pl.pcap * 2 * bs * D * 4);
+    pl.total = o;
+    return NSA_SEL_OK;
+}
+
+template <int BS, int D>
+hipError_t launch_key_passes(const Bw &w, const BwdPlan &pl, hipStream_t stream) {
+    const int chunks = (w.M + kBitQ - 1) / kBitQ;
+    hipLaunchKernelGGL(nsa_sel_bwd_bitmap_kernel, dim3(w.B * w.G * chunks), dim3(kBitQ), 0, stream, w);
+    hipLaunchKernelGGL(nsa_sel_bwd_count_kernel, dim3((w.R + 3) / 4), dim3(256), 0, stream, w);
+    hipLaunchKernelGGL(nsa_sel_bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, w);
+    const int per_xcd = (int)((pl.cap + kNumXcd - 1) / kNumXcd);
+    hipLaunchKernelGGL((nsa_sel_bwd_dkv_kernel<BS, D>), dim3(per_xcd * kNumXcd), dim3(kWaveSize * (BS / 16)), 0,
+                       stream, w);
+    hipLaunchKernelGGL((nsa_sel_bwd_reduce_kernel<BS, D>), dim3(w.R), dim3(256), 0, stream, w);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" int nsa_sel_bwd_workspace_size(int B, int M, int N, int H, int G, int D, int block_size, int T,
+                                          size_t *bytes) {
+    if (!bytes) return NSA_SEL_ERR_NULL;
+    Params p;
+    const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
+    if (st != NSA_SEL_OK) return st;
+    BwdPlan pl;
+    const int st2 = bwd_plan(p, D, block_size, pl);
+    if (st2 != NSA_SEL_OK) return st2;
+    *bytes = pl.total;
+    return NSA_SEL_OK;
+}
+
+extern "C" int nsa_sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                           const void *O, const float *LSE, const void *dO, float *dQ, float *dK, float *dV,
+                           void *workspace, size_t workspace_bytes, int B, int M, int N, int H, int G, int D,
+                           int block_size, int T, hipStream_t stream) {
+    if (!Q || !K || !V || !block_indices || !O || !LSE || !dO || !dQ || !dK || !dV) return NSA_SEL_ERR_NULL;
+    Params p;
+    const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
+    if (st != NSA_SEL_OK) return st;
+    BwdPlan pl;
+    const int st2 = bwd_plan(p, D, block_size, pl);
+    if (st2 != NSA_SEL_OK) return st2;
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ |
+         (uintptr_t)dK | (uintptr_t)dV) & 15)
+        return NSA_SEL_ERR_ALIGN;
+    if (((uintptr_t)block_indices | (uintptr_t)LSE) & 3) return NSA_SEL_ERR_ALIGN;
+    if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < pl.total) return NSA_SEL_ERR_WORKSPACE;
+
+    const size_t q_bytes = (size_t)B * M * H * D * 2, kv_bytes = (size_t)B * N * G * D * 2;
+    const size_t idx_bytes = (size_t)B * M * G * T * 4, lse_bytes = (size_t)B * H * M * 4;
+    const void *ins[7] = {Q, K, V, block_indices, O, LSE, dO};
+    const size_t in_bytes[7] = {q_bytes, kv_bytes, kv_bytes, idx_bytes, q_bytes, lse_bytes, q_bytes};
+    void *outs[4] = {dQ, dK, dV, workspace};
+    const size_t out_bytes[4] = {q_bytes * 2, kv_bytes * 2, kv_bytes * 2, pl.total};
+    for (int o = 0; o < 4; ++o) {
+        for (int i = 0; i < 7; ++i)
+            if (ranges_overlap(outs[o], out_bytes[o], ins[i], in_bytes[i])) return NSA_SEL_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 4; ++o2)
+            if (ranges_overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return NSA_SEL_ERR_ALIAS;
+    }
+
+    const int cus = device_cus();
+    plan_slots(p, cus, 1);
+    p.Q = (const _Float16 *)Q;
+    p.K = (const _Float16 *)K;
+    p.V = (const _Float16 *)V;
+    p.idx = block_indices;
+    p.O = nullptr;
+    p.LSE = nullptr;
+    char *ws = (char *)workspace;
+    float2 *rowstat = (float2 *)(ws + pl.off_rowstat);
+    DqKernel f;
+    f.x.O = (const _Float16 *)O;
+    f.x.dO = (const _Float16 *)dO;
+    f.x.LSE = LSE;
+    f.x.dQ = dQ;
+    f.x.rowstat = rowstat;
+    f.x.scale = 1.0f / sqrtf((float)D);
+
+    Bw w;
+    w.Q = (const _Float16 *)Q;
+    w.K = (const _Float16 *)K;
+    w.V = (const _Float16 *)V;
+    w.dO = (const _Float16 *)dO;
+    w.idx = block_indices;
+    w.rowstat = rowstat;
+    w.bits = (unsigned *)(ws + pl.off_bits);
+    w.row_items = (int *)(ws + pl.off_row_items);
+    w.row_first = (int *)(ws + pl.off_row_first);
+    w.row_part = (int *)(ws + pl.off_row_part);
+    w.starts = (int *)(ws + pl.off_starts);
+    w.items = (int2 *)(ws + pl.off_items);
+    w.n_items = (int *)(ws + pl.off_nitems);
+    w.part = (float *)(ws + pl.off_part);
+    w.dK = dK;
+    w.dV = dV;
+    w.B = B; w.M = M; w.N = N; w.H = H; w.G = G; w.gs = p.gs; w.T = T; w.bs = block_size;
+    w.NB = pl.NB; w.MW = pl.MW; w.R = pl.R; w.qc = pl.qc; w.kmax = pl.kmax; w.cap = (int)pl.cap; w.pcap = (int)pl.pcap; w.qpt = pl.qpt;
+    w.sentinel = B * H * M;
+    w.scale = 1.0f / sqrtf((float)D);
+    w.scale_log2 = p.scale_log2;
+
+    hipError_t e;
+    if (block_size == 64)
+        e = (D == 128) ? dq_launch_pack<64, 128>(f, p, cus, stream) : dq_launch_pack<64, 64>(f, p, cus, stream);
+    else
+        e = (D == 128) ? dq_launch_pack<32, 128>(f, p, cus, stream) : dq_launch_pack<32, 64>(f, p, cus, stream);
+    if (e != hipSuccess) return NSA_SEL_ERR_HIP;
+    if (block_size == 64)
+        e = (D == 128) ? launch_key_passes<64, 128>(w, pl, stream) : launch_key_passes<64, 64>(w, pl, stream);
+    else
+        e = (D == 128) ? launch_key_passes<32, 128>(w, pl, stream) : launch_key_passes<32, 64>(w, pl, stream);
+    return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
+}

@@ -697,9 +697,11 @@ int check_sizes(int B, int M, int N, int H, int G, int D, int block_size, int T,
 // with streamed rows), and fewer while the grid would give a CU less than 8
 // wavefront slots.  Two tiles keep a wavefront within 256 registers, so two
 // wavefronts share each SIMD.
-void plan_slots(Params &p, int cus) {
+// max_mode caps the tiles per wavefront (the backward's dQ pass holds more
+// registers per tile than the forward and runs one).
+void plan_slots(Params &p, int cus, int max_mode = 2) {
     int mode = 0;
-    for (int nt = 2; nt >= 1; nt /= 2) {
+    for (int nt = max_mode; nt >= 1; nt /= 2) {
         if ((int64_t)p.pack * nt * p.T <= 128) {
             mode = nt;
             break;

@@ -40,7 +40,8 @@ enum {
     NSA_SEL_ERR_ALIGN = 4,       /* Q/K/V/O not 16-byte aligned, idx/LSE not 4-byte */
     NSA_SEL_ERR_RANGE = 5,       /* B*M*G units or a tensor size beyond the limits  */
     NSA_SEL_ERR_ALIAS = 6,       /* an output buffer overlaps an input or the other */
-    NSA_SEL_ERR_HIP = 7          /* the HIP runtime reported an error at launch     */
+    NSA_SEL_ERR_HIP = 7,         /* the HIP runtime reported an error at launch     */
+    NSA_SEL_ERR_WORKSPACE = 8    /* workspace NULL, misaligned or too small (bwd)   */
 };
 
 /*

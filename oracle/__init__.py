@@ -51,7 +51,7 @@ def _load():
         lib.nsa_oracle_dense_units.restype = ctypes.c_int
         lib.nsa_oracle_dense_units.argtypes = [p, p, p] + [i64] * 6 + [p, i64, p, p, ctypes.c_int]
         lib.nsa_oracle_bwd_units.restype = ctypes.c_int
-        lib.nsa_oracle_bwd_units.argtypes = ([p] * 5 + [i64] * 8 + [p, i64, p, i64, p, p, p, ctypes.c_int])
+        lib.nsa_oracle_bwd_units.argtypes = ([p] * 5 + [i64] * 8 + [p, i64, p, i64, p, p, p, p, p, p, ctypes.c_int])
         _lib = lib
     return _lib
 
@@ -138,7 +138,7 @@ def dense_full(q, k, v, threads: int = 0):
 
 
 def bwd_units(q, k, v, idx, do, block_size: int, units: np.ndarray, kblocks: np.ndarray | None = None,
-              threads: int = 0):
+              threads: int = 0, mags: bool = False):
     """Gradients of the selection attention of units (b, m, g) for the upstream
     gradient ``do`` (fp16 [B, M, H, D]).
 
@@ -147,7 +147,12 @@ def bwd_units(q, k, v, idx, do, block_size: int, units: np.ndarray, kblocks: np.
     units: [B, N, G, D] when ``kblocks`` is None, else [n_kblocks, bs, D] for
     the key blocks (b, g, t) listed there (rows past N stay zero).  Only the
     given units contribute, so a key block's dK/dV is complete when every unit
-    that selects it is listed."""
+    that selects it is listed.
+
+    mags=True also returns, laid out like dQ, dK, dV, the L2 norm over each
+    element's terms of the term magnitudes (dS taken as P (|dP| + sum_d |dO_d
+    O_d|)): the scale of the rounding error of a kernel that rounds P, dS and
+    the O that Delta is formed from."""
     if idx is None:
         idx_arr = np.zeros((q.shape[0], q.shape[1], k.shape[2], 1), np.int32)
     else:
@@ -167,17 +172,28 @@ def bwd_units(q, k, v, idx, do, block_size: int, units: np.ndarray, kblocks: np.
         kb_ptr, nkb = _ptr(kblocks), kblocks.shape[0]
         dK = np.zeros((nkb, block_size, D), dtype=np.float64)
     dV = np.zeros_like(dK)
+    if mags:
+        mQ, mK, mV = np.empty_like(dQ), np.zeros_like(dK), np.zeros_like(dK)
+        mp = (_ptr(mQ), _ptr(mK), _ptr(mV))
+    else:
+        mp = (None, None, None)
     rc = _load().nsa_oracle_bwd_units(_ptr(q), _ptr(k), _ptr(v), None if idx is None else _ptr(idx_arr), _ptr(do),
                                       B, M, N, H, G, D, block_size, T, _ptr(units), U, kb_ptr, nkb,
-                                      _ptr(dQ), _ptr(dK), _ptr(dV), threads)
+                                      _ptr(dQ), _ptr(dK), _ptr(dV), *mp, threads)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
+    if mags:
+        return dQ, dK, dV, mQ, mK, mV
     return dQ, dK, dV
 
 
-def bwd_full(q, k, v, idx, do, block_size: int, threads: int = 0):
-    """Whole-tensor gradients: dQ fp64 [B, M, H, D], dK and dV fp64 [B, N, G, D]."""
+def bwd_full(q, k, v, idx, do, block_size: int, threads: int = 0, mags: bool = False):
+    """Whole-tensor gradients: dQ fp64 [B, M, H, D], dK and dV fp64 [B, N, G, D]
+    (and with mags=True their term magnitudes, laid out alike)."""
     B, M, H, D = q.shape
     G = k.shape[2]
-    dQ, dK, dV = bwd_units(q, k, v, idx, do, block_size, all_units(B, M, G), None, threads)
-    return dQ.reshape(B, M, H, D), dK, dV
+    r = bwd_units(q, k, v, idx, do, block_size, all_units(B, M, G), None, threads, mags)
+    out = [r[0].reshape(B, M, H, D), r[1], r[2]]
+    if mags:
+        out += [r[3].reshape(B, M, H, D), r[4], r[5]]
+    return tuple(out)

@@ -303,6 +303,8 @@ typedef struct {
     int64_t n_kblocks;
     double *dQ;
     double *dK, *dV;     /* this thread's partial sums */
+    double *mQ;          /* optional: sums of squared term magnitudes of dQ */
+    double *mK, *mV;     /* this thread's partial sums of squared term magnitudes */
     int64_t kv_elems;
 } bjob_t;
 
@@ -328,6 +330,7 @@ static void *bworker(void *arg) {
     double *dOd = (double *)malloc(sizeof(double) * (size_t)(gs * D));
     double *dP = (double *)malloc(sizeof(double) * (size_t)(gs * J->N));
     double *delta = (double *)malloc(sizeof(double) * (size_t)gs);
+    double *adelta = (double *)malloc(sizeof(double) * (size_t)gs);
     w.mark = (unsigned char *)malloc((size_t)NB);
     w.keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)J->N);
     w.score = (double *)malloc(sizeof(double) * (size_t)(gs * J->N));
@@ -335,7 +338,7 @@ static void *bworker(void *arg) {
     w.kd = (double *)malloc(sizeof(double) * (size_t)D);
     w.mu = (double *)malloc(sizeof(double) * (size_t)gs);
     w.z = (double *)malloc(sizeof(double) * (size_t)gs);
-    if (!fwdO || !fwdL || !dOd || !dP || !delta || !w.mark || !w.keys || !w.score || !w.qd || !w.kd || !w.mu || !w.z) {
+    if (!fwdO || !fwdL || !dOd || !dP || !delta || !adelta || !w.mark || !w.keys || !w.score || !w.qd || !w.kd || !w.mu || !w.z) {
         J->error = 1;
     } else {
         const double scale = 1.0 / sqrt((double)D);
@@ -356,7 +359,11 @@ static void *bworker(void *arg) {
                 for (int64_t d = 0; d < D; ++d) dOd[i * D + d] = g_half[src[d]];
             }
             /* dP and Delta. P_n = exp(s_n - LSE). */
-            for (int64_t i = 0; i < gs; ++i) delta[i] = 0.0;
+            for (int64_t i = 0; i < gs; ++i) {
+                delta[i] = 0.0;
+                adelta[i] = 0.0;
+                for (int64_t d = 0; d < D; ++d) adelta[i] += fabs(dOd[i * D + d] * fwdO[i * D + d]);
+            }
             for (int64_t s = 0; s < nk; ++s) {
                 const uint16_t *v = J->V + ((b * J->N + w.keys[s]) * J->G + g) * D;
                 for (int64_t d = 0; d < D; ++d) w.kd[d] = g_half[v[d]];
@@ -368,7 +375,10 @@ static void *bworker(void *arg) {
                 }
             }
             double *dq = j->dQ + u * gs * D;
+            double *mq = j->mQ ? j->mQ + u * gs * D : NULL;
             for (int64_t e = 0; e < gs * D; ++e) dq[e] = 0.0;
+            if (mq)
+                for (int64_t e = 0; e < gs * D; ++e) mq[e] = 0.0;
             for (int64_t s = 0; s < nk; ++s) {
                 const int64_t n = w.keys[s];
                 const uint16_t *k = J->K + ((b * J->N + n) * J->G + g) * D;
@@ -377,28 +387,53 @@ static void *bworker(void *arg) {
                 for (int64_t i = 0; i < gs; ++i) {
                     const double P = exp(w.score[i * J->N + s] - fwdL[i]);
                     const double dS = P * (dP[i * J->N + s] - delta[i]);
+                    /* Size of dS before the cancellation of its two parts,
+                       with Delta taken as sum_d |dO_d O_d| (which also bounds
+                       the error of a Delta formed from a rounded O): the
+                       scale of the rounding errors a term can carry. */
+                    const double dSm = P * (fabs(dP[i * J->N + s]) + adelta[i]);
                     for (int64_t d = 0; d < D; ++d) dq[i * D + d] += dS * w.kd[d] * scale;
+                    if (mq)
+                        for (int64_t d = 0; d < D; ++d) {
+                            const double t = dSm * w.kd[d] * scale;
+                            mq[i * D + d] += t * t;
+                        }
                     if (pos >= 0) {
                         for (int64_t d = 0; d < D; ++d) {
                             j->dK[pos + d] += dS * w.qd[i * D + d] * scale;
                             j->dV[pos + d] += P * dOd[i * D + d];
                         }
+                        if (j->mK)
+                            for (int64_t d = 0; d < D; ++d) {
+                                const double tk = dSm * w.qd[i * D + d] * scale, tv = P * dOd[i * D + d];
+                                j->mK[pos + d] += tk * tk;
+                                j->mV[pos + d] += tv * tv;
+                            }
                     }
                 }
             }
         }
     }
-    free(fwdO); free(fwdL); free(dOd); free(dP); free(delta);
+    free(fwdO); free(fwdL); free(dOd); free(dP); free(delta); free(adelta);
     free(w.mark); free(w.keys); free(w.score); free(w.qd); free(w.kd); free(w.mu); free(w.z);
     return NULL;
 }
 
+/*
+ * mQ, mK, mV (optional, all or none): for every gradient element, the square
+ * root of the sum of the squared magnitudes of its terms, with dS taken as
+ * P (|dP| + sum_d |dO_d O_d|): the scale of the rounding error a kernel that
+ * rounds P, dS and O to a short format accumulates in that element.  Laid out as dQ, dK,
+ * dV; mK and mV are accumulated like dK and dV (as sums of squares) and the
+ * square root is taken at the end.
+ */
 int nsa_oracle_bwd_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const int32_t *block_indices,
                          const uint16_t *dO, int64_t B, int64_t M, int64_t N, int64_t H, int64_t G, int64_t D,
                          int64_t block_size, int64_t T, const int64_t *units, int64_t n_units,
                          const int64_t *kblocks, int64_t n_kblocks, double *dQ, double *dK, double *dV,
-                         int n_threads) {
+                         double *mQ, double *mK, double *mV, int n_threads) {
     if (!Q || !K || !V || !dO || !units || !dQ || !dK || !dV) return -1;
+    if ((mQ != NULL) != (mK != NULL) || (mK != NULL) != (mV != NULL)) return -1;
     if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1 || block_size < 1 || T < 1) return -1;
     if (H % G) return -1;
     for (int64_t u = 0; u < n_units; ++u) {
@@ -428,9 +463,15 @@ int nsa_oracle_bwd_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V
         J->units = units; J->n_units = n_units;
         J->thread_id = i; J->n_threads = n_threads;
         j->dO = dO; j->kblocks = kblocks; j->n_kblocks = n_kblocks; j->dQ = dQ; j->kv_elems = kv_elems;
+        j->mQ = mQ;
         j->dK = (double *)calloc((size_t)kv_elems, sizeof(double));
         j->dV = (double *)calloc((size_t)kv_elems, sizeof(double));
         if (!j->dK || !j->dV) rc = -1;
+        if (mK) {
+            j->mK = (double *)calloc((size_t)kv_elems, sizeof(double));
+            j->mV = (double *)calloc((size_t)kv_elems, sizeof(double));
+            if (!j->mK || !j->mV) rc = -1;
+        }
     }
     int started = 0;
     if (rc == 0) {
@@ -449,10 +490,24 @@ int nsa_oracle_bwd_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V
             dK[e] += jobs[i].dK[e];
             dV[e] += jobs[i].dV[e];
         }
+        if (mK)
+            for (int64_t e = 0; rc == 0 && e < kv_elems; ++e) {
+                mK[e] += jobs[i].mK[e];
+                mV[e] += jobs[i].mV[e];
+            }
+    }
+    if (mK && rc == 0) {
+        for (int64_t e = 0; e < kv_elems; ++e) {
+            mK[e] = sqrt(mK[e]);
+            mV[e] = sqrt(mV[e]);
+        }
+        for (int64_t e = 0; e < n_units * (H / G) * D; ++e) mQ[e] = sqrt(mQ[e]);
     }
     for (int i = 0; i < n_threads; ++i) {
         free(jobs[i].dK);
         free(jobs[i].dV);
+        free(jobs[i].mK);
+        free(jobs[i].mV);
     }
     free(jobs);
     free(th);

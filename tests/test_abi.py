@@ -51,7 +51,7 @@ def test_status_codes_match_header():
 
 
 def test_status_strings(lib):
-    for code in range(0, 8):
+    for code in range(0, 9):
         s = binding.nsa_sel_status_string(code)
         assert isinstance(s, str) and s
     assert binding.nsa_sel_status_string(0) == "ok"
@@ -220,3 +220,69 @@ def test_dense_null_pointer(lib, which):
                                        (dict(L=ADDR["O"] + 64), binding.NSA_SEL_ERR_ALIAS)])
 def test_dense_rejects_bad_arguments(lib, over, code):
     assert _dense_call(**over) == code
+
+
+# --- backward (include/nsa_sel_bwd.h) ------------------------------------------
+
+BWD_HEADER = os.path.join(ROOT, "include", "nsa_sel_bwd.h")
+BNAMES = ["Q", "K", "V", "I", "O", "L", "dO", "dQ", "dK", "dV", "W"]
+BADDR = {name: (i + 1) << 38 for i, name in enumerate(BNAMES)}
+
+
+def test_bwd_header_declares_the_binding_names():
+    text = re.sub(r"/\*.*?\*/", "", open(BWD_HEADER).read(), flags=re.S)
+    assert sorted(set(re.findall(r"\b(nsa_\w+)\s*\(", text))) == sorted(binding.BWD_EXPORTED)
+
+
+def test_bwd_symbols_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in binding.BWD_EXPORTED:
+        assert name in exported
+
+
+def test_bwd_workspace_size(lib):
+    n = binding.nsa_sel_bwd_workspace_size(**GOOD)
+    assert n > 0 and n % 256 == 0
+    # grows with the problem
+    assert binding.nsa_sel_bwd_workspace_size(**dict(GOOD, M=4096, N=4096)) > n
+    assert binding.nsa_sel_bwd_workspace_size_raw(**dict(GOOD, D=96))[0] == binding.NSA_SEL_ERR_UNSUPPORTED
+    assert binding.nsa_sel_bwd_workspace_size_raw(**dict(GOOD, M=0))[0] == binding.NSA_SEL_ERR_SHAPE
+    # one batch of Q beyond 2^32 - 1 bytes
+    rc, _ = binding.nsa_sel_bwd_workspace_size_raw(B=1, M=1 << 20, N=1024, H=16, G=1, D=128, block_size=64, T=4)
+    assert rc == binding.NSA_SEL_ERR_RANGE
+    assert lib.nsa_sel_bwd_workspace_size(1, 256, 256, 8, 1, 128, 64, 4, None) == binding.NSA_SEL_ERR_NULL
+
+
+def _bwd_call(**over):
+    args = dict(GOOD)
+    ptrs = dict(BADDR)
+    wsn = over.pop("wsn", None)
+    for k in list(over):
+        if k in ptrs:
+            ptrs[k] = over.pop(k)
+    args.update(over)
+    if wsn is None:
+        rc, wsn = binding.nsa_sel_bwd_workspace_size_raw(**args)
+    return binding.nsa_sel_bwd_raw(*(ptrs[k] for k in BNAMES), wsn, args["B"], args["M"], args["N"], args["H"],
+                                   args["G"], args["D"], args["block_size"], args["T"], 0)
+
+
+@pytest.mark.parametrize("which", BNAMES[:-1])
+def test_bwd_null_pointer(lib, which):
+    assert _bwd_call(**{which: 0}) == binding.NSA_SEL_ERR_NULL
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(M=0), binding.NSA_SEL_ERR_SHAPE), (dict(H=8, G=3), binding.NSA_SEL_ERR_SHAPE),
+    (dict(D=96), binding.NSA_SEL_ERR_UNSUPPORTED), (dict(block_size=128), binding.NSA_SEL_ERR_UNSUPPORTED),
+    (dict(Q=BADDR["Q"] + 8), binding.NSA_SEL_ERR_ALIGN), (dict(dO=BADDR["dO"] + 2), binding.NSA_SEL_ERR_ALIGN),
+    (dict(dK=BADDR["dK"] + 4), binding.NSA_SEL_ERR_ALIGN), (dict(L=BADDR["L"] + 2), binding.NSA_SEL_ERR_ALIGN),
+    (dict(W=0), binding.NSA_SEL_ERR_WORKSPACE), (dict(W=BADDR["W"] + 128), binding.NSA_SEL_ERR_WORKSPACE),
+    (dict(wsn=256), binding.NSA_SEL_ERR_WORKSPACE),
+    (dict(dQ=BADDR["O"]), binding.NSA_SEL_ERR_ALIAS), (dict(dV=BADDR["dK"] + 64), binding.NSA_SEL_ERR_ALIAS),
+    (dict(W=BADDR["dO"]), binding.NSA_SEL_ERR_ALIAS), (dict(dK=BADDR["W"] + 1024), binding.NSA_SEL_ERR_ALIAS),
+])
+def test_bwd_rejects_bad_arguments(lib, over, code):
+    assert _bwd_call(**over) == code

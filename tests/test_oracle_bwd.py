@@ -228,3 +228,43 @@ def test_rejects_bad_arguments(oracle_mod):
         oracle_mod.bwd_units(q, k, v, idx, do, 4, np.array([[0, 8, 0]]))
     with pytest.raises(ValueError):
         oracle_mod.bwd_units(q, k, v, idx, do[:, :4].copy(), 4, np.array([[0, 0, 0]]))
+
+
+def test_term_magnitudes(oracle_mod):
+    """The error-scale output: for each gradient element, the L2 norm over its
+    terms of |term| with dS taken as P (|dP| + sum_d |dO_d O_d|), checked
+    against dense masked matrices written here (numpy, fp64)."""
+    B, M, N, H, G, D, bs, T = 1, 40, 40, 4, 2, 8, 4, 3
+    rng = np.random.default_rng(31)
+    q, k, v, do = _rand(rng, B, M, N, H, G, D)
+    idx = _rand_idx(rng, B, M, N, G, bs, T)
+    mask = _mask(idx, M, N, bs)
+    gs = H // G
+    sc = 1.0 / math.sqrt(D)
+    wq = np.zeros((B, M, H, D))
+    wk = np.zeros((B, N, G, D))
+    wv = np.zeros((B, N, G, D))
+    for b in range(B):
+        for g in range(G):
+            K = k[b, :, g].astype(np.float64)
+            V = v[b, :, g].astype(np.float64)
+            for i in range(gs):
+                h = g * gs + i
+                Q = q[b, :, h].astype(np.float64)
+                dO = do[b, :, h].astype(np.float64)
+                s = np.where(mask[b, g], Q @ K.T * sc, -np.inf)
+                rows = mask[b, g].any(axis=1)
+                P = np.zeros((M, N))
+                P[rows] = np.exp(s[rows] - s[rows].max(axis=1, keepdims=True))
+                P[rows] /= P[rows].sum(axis=1, keepdims=True)
+                dP = dO @ V.T
+                O = P @ V
+                adelta = np.abs(dO * O).sum(axis=1)
+                dSm = P * (np.abs(dP) + adelta[:, None])
+                wq[b, :, h] = np.sqrt((dSm ** 2) @ (K ** 2)) * sc
+                wk[b, :, g] += (dSm ** 2).T @ (Q ** 2) * sc * sc
+                wv[b, :, g] += (P ** 2).T @ (dO ** 2)
+    _, _, _, mq, mk, mv = oracle_mod.bwd_full(q, k, v, idx, do, bs, mags=True)
+    np.testing.assert_allclose(mq, wq, rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(mk, np.sqrt(wk), rtol=1e-10, atol=1e-14)
+    np.testing.assert_allclose(mv, np.sqrt(wv), rtol=1e-10, atol=1e-14)
