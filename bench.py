@@ -7,12 +7,15 @@ roofline of the kernel (HBM-bound on gathered bytes), cold-cache timings, the
 gather-ceiling probe (the kernel's block-gather stream alone), the MFMA
 utilisation, the same kernel with every causal block selected (dense mode),
 the dense causal attention kernel on the same tensors (the reference point of
-the speed-up goal) and the fp64 CPU oracle timed on a bounded sample of the
+the speed-up goal), the backward pass (nsa_sel_bwd: dQ, dK, dV from the
+forward's O and LSE) and the fp64 CPU oracle timed on a bounded sample of the
 same workload.
 
 Work counts per launch (exact, from the index rows):
   gathered bytes  = sum over units of (counted blocks) * bs * D * 2 B * 2 (K and V)
   effective flops = sum over units of 4 * D * (H/G) * (visible selected keys)
+  backward flops  = sum over units of 10 * D * (H/G) * (visible selected keys)
+                    (five products per (row, key): S, dP, dQ, dK, dV)
 """
 
 from __future__ import annotations
@@ -29,7 +32,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from block_sparse_attention_sel_amd.inputs import CONFIGS, Config, block_indices, make_inputs  # noqa: E402
+from block_sparse_attention_sel_amd.inputs import (CONFIGS, Config, block_indices, make_grad_output,  # noqa: E402
+                                                   make_inputs)
 
 HBM_PEAK_GBPS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
@@ -222,6 +226,7 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the all-causal-blocks run")
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-dense-fa", action="store_true", help="skip the dense causal attention kernel")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10, help="cold-cache timed calls (0 = skip)")
     ap.add_argument("--no-probe", action="store_true", help="skip the gather-ceiling probe")
@@ -369,6 +374,32 @@ def main():
                            "eff_TFLOPs": round(f_flops / (f_ev * 1e-3) / 1e12, 2),
                            "mfma_frac": round(f_flops / (f_ev * 1e-3) / (FP16_PEAK_TFLOPS * 1e12), 4),
                            "ratio_dense_fa_over_selected": round(f_ev / ev_ms, 2)}
+
+    if not args.no_bwd:
+        # Gradients of the selection attention from this config's forward O
+        # and LSE (recomputed here: the dense runs above reuse O and L).
+        from block_sparse_attention_sel_amd.binding import nsa_sel_bwd, nsa_sel_bwd_workspace_size
+        print("[bench] backward (nsa_sel_bwd)", file=sys.stderr, flush=True)
+        launch()
+        tdo = torch.from_numpy(make_grad_output(cfg)).to(dev)
+        nbytes = nsa_sel_bwd_workspace_size(cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dq = torch.empty((cfg.B, cfg.M, cfg.H, cfg.D), dtype=torch.float32, device=dev)
+        dk = torch.empty((cfg.B, cfg.N, cfg.G, cfg.D), dtype=torch.float32, device=dev)
+        dv = torch.empty_like(dk)
+
+        def bwd():
+            nsa_sel_bwd(tq, tk, tv, ti, O, L, tdo, dq, dk, dv, ws, nbytes, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G,
+                        cfg.D, cfg.block_size, cfg.T, stream.cuda_stream)
+
+        _, b_ev, b_min = time_launches(torch, bwd, args.steps, args.warmup)
+        assert torch.isfinite(dq).all().item() and torch.isfinite(dk).all().item(), "non-finite gradients"
+        b_flops = 10.0 * cfg.D * cfg.gs * keys
+        out["backward"] = {"kernel": "nsa_sel_bwd", "ms": round(b_ev, 3), "ms_min": round(b_min, 3),
+                           "eff_TFLOPs": round(b_flops / (b_ev * 1e-3) / 1e12, 2),
+                           "effective_flops": b_flops, "ratio_bwd_over_fwd": round(b_ev / ev_ms, 2),
+                           "workspace_MiB": round(nbytes / 2 ** 20, 1)}
+        del tdo, ws, dq, dk, dv
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
