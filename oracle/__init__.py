@@ -50,6 +50,12 @@ def _load():
         lib.nsa_oracle_units.argtypes = [p, p, p, p] + [i64] * 8 + [p, i64, p, p, p, ctypes.c_int]
         lib.nsa_oracle_dense_units.restype = ctypes.c_int
         lib.nsa_oracle_dense_units.argtypes = [p, p, p] + [i64] * 6 + [p, i64, p, p, ctypes.c_int]
+        lib.nsa_oracle_bf16_to_double.restype = ctypes.c_double
+        lib.nsa_oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.nsa_oracle_units_t.restype = ctypes.c_int
+        lib.nsa_oracle_units_t.argtypes = [p, p, p, p] + [i64] * 8 + [p, i64, p, p, p, ctypes.c_int, ctypes.c_int]
+        lib.nsa_oracle_window_units.restype = ctypes.c_int
+        lib.nsa_oracle_window_units.argtypes = ([p, p, p] + [i64] * 8 + [p, i64, p, p, ctypes.c_int, ctypes.c_int])
         lib.nsa_oracle_bwd_units.restype = ctypes.c_int
         lib.nsa_oracle_bwd_units.argtypes = ([p] * 5 + [i64] * 8 + [p, i64, p, i64, p, p, p, p, p, p, ctypes.c_int])
         _lib = lib
@@ -60,12 +66,22 @@ def half_to_double(bits: int) -> float:
     return _load().nsa_oracle_half_to_double(bits)
 
 
+def bf16_to_double(bits: int) -> float:
+    return _load().nsa_oracle_bf16_to_double(bits)
+
+
+# Element types: fp16 arrays are numpy float16; bf16 arrays are numpy uint16
+# holding the bfloat16 bit patterns (numpy has no bfloat16 type).
+_ELEM = {"fp16": (np.float16, 0), "bf16": (np.uint16, 1)}
+
+
 def _ptr(a: np.ndarray) -> ctypes.c_void_p:
     return ctypes.c_void_p(a.ctypes.data)
 
 
-def _check_inputs(q, k, v, idx):
-    for name, a, dt in (("Q", q, np.float16), ("K", k, np.float16), ("V", v, np.float16),
+def _check_inputs(q, k, v, idx, dtype="fp16"):
+    et = _ELEM[dtype][0]
+    for name, a, dt in (("Q", q, et), ("K", k, et), ("V", v, et),
                         ("block_indices", idx, np.int32)):
         if a.dtype != dt or not a.flags.c_contiguous or a.ndim != 4:
             raise ValueError(f"{name} must be a C-contiguous 4-d {np.dtype(dt).name} array")
@@ -76,18 +92,19 @@ def _check_inputs(q, k, v, idx):
     return B, M, N, H, G, D, idx.shape[3]
 
 
-def oracle_units(q, k, v, idx, block_size: int, units: np.ndarray, threads: int = 0):
-    """O (fp64 [U, H/G, D]) and LSE (fp64 [U, H/G]) for units (b, m, g)."""
-    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx)
+def oracle_units(q, k, v, idx, block_size: int, units: np.ndarray, threads: int = 0, dtype: str = "fp16"):
+    """O (fp64 [U, H/G, D]) and LSE (fp64 [U, H/G]) for units (b, m, g).
+    dtype "bf16" takes Q, K, V as uint16 arrays of bfloat16 bit patterns."""
+    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx, dtype)
     units = np.ascontiguousarray(units, dtype=np.int64).reshape(-1, 3)
     U = units.shape[0]
     gs = H // G
     O = np.empty((U, gs, D), dtype=np.float64)
     L = np.empty((U, gs), dtype=np.float64)
     ndup = ctypes.c_int64(0)
-    rc = _load().nsa_oracle_units(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, M, N, H, G, D,
-                                  block_size, T, _ptr(units), U, _ptr(O), _ptr(L),
-                                  ctypes.byref(ndup), threads)
+    rc = _load().nsa_oracle_units_t(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), B, M, N, H, G, D,
+                                    block_size, T, _ptr(units), U, _ptr(O), _ptr(L),
+                                    ctypes.byref(ndup), _ELEM[dtype][1], threads)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     oracle_units.last_dup_units = ndup.value
@@ -102,10 +119,10 @@ def all_units(B: int, M: int, G: int) -> np.ndarray:
     return np.stack([b.ravel(), m.ravel(), g.ravel()], axis=1).astype(np.int64)
 
 
-def oracle_full(q, k, v, idx, block_size: int, threads: int = 0):
+def oracle_full(q, k, v, idx, block_size: int, threads: int = 0, dtype: str = "fp16"):
     """Whole-tensor oracle: O fp64 [B, M, H, D] and LSE fp64 [B, H, M]."""
-    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx)
-    O, L = oracle_units(q, k, v, idx, block_size, all_units(B, M, G), threads)
+    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx, dtype)
+    O, L = oracle_units(q, k, v, idx, block_size, all_units(B, M, G), threads, dtype)
     O = O.reshape(B, M, H, D)
     L = L.reshape(B, M, H).transpose(0, 2, 1).copy()
     return O, L
@@ -127,6 +144,32 @@ def dense_units(q, k, v, units: np.ndarray, threads: int = 0):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return O, L
+
+
+def window_units(q, k, v, left: int, right: int, units: np.ndarray, threads: int = 0, dtype: str = "fp16"):
+    """Sliding-window attention for units (b, m, g): keys n < N with
+    m - left <= n <= m + right (negative = unbounded on that side);
+    O fp64 [U, H/G, D], LSE fp64 [U, H/G]."""
+    idx = np.zeros((q.shape[0], q.shape[1], k.shape[2], 1), np.int32)
+    B, M, N, H, G, D, _ = _check_inputs(q, k, v, idx, dtype)
+    units = np.ascontiguousarray(units, dtype=np.int64).reshape(-1, 3)
+    U = units.shape[0]
+    gs = H // G
+    O = np.empty((U, gs, D), dtype=np.float64)
+    L = np.empty((U, gs), dtype=np.float64)
+    rc = _load().nsa_oracle_window_units(_ptr(q), _ptr(k), _ptr(v), B, M, N, H, G, D, left, right, _ptr(units), U,
+                                         _ptr(O), _ptr(L), _ELEM[dtype][1], threads)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return O, L
+
+
+def window_full(q, k, v, left: int, right: int, threads: int = 0, dtype: str = "fp16"):
+    """Whole-tensor sliding-window attention: O fp64 [B, M, H, D], LSE fp64 [B, H, M]."""
+    B, M, H, D = q.shape
+    G = k.shape[2]
+    O, L = window_units(q, k, v, left, right, all_units(B, M, G), threads, dtype)
+    return O.reshape(B, M, H, D), L.reshape(B, M, H).transpose(0, 2, 1).copy()
 
 
 def dense_full(q, k, v, threads: int = 0):

@@ -54,11 +54,32 @@ double nsa_oracle_half_to_double(uint16_t h) {
     return sign ? -v : v;
 }
 
-/* All 2^16 decoded values, filled once from nsa_oracle_half_to_double. */
+/* Exact decode of a bfloat16 bit pattern (the upper half of an IEEE 754
+   binary32: 1 sign bit, 8 exponent bits with bias 127, 7 fraction bits). */
+double nsa_oracle_bf16_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -133);                /* subnormal: f * 2^-126 / 2^7 */
+    } else if (e == 255) {
+        v = f ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(128 + f), e - 134);     /* (1 + f/2^7) * 2^(e-127) */
+    }
+    return sign ? -v : v;
+}
+
+/* All 2^16 decoded values of each element type, filled once. */
 static double g_half[65536];
+static double g_bf16[65536];
 static pthread_once_t g_half_once = PTHREAD_ONCE_INIT;
 static void fill_half_table(void) {
-    for (int i = 0; i < 65536; ++i) g_half[i] = nsa_oracle_half_to_double((uint16_t)i);
+    for (int i = 0; i < 65536; ++i) {
+        g_half[i] = nsa_oracle_half_to_double((uint16_t)i);
+        g_bf16[i] = nsa_oracle_bf16_to_double((uint16_t)i);
+    }
 }
 
 typedef struct {
@@ -71,6 +92,8 @@ typedef struct {
     int thread_id, n_threads;
     int64_t dup_units;   /* units whose valid entries repeat a block */
     int error;
+    const double *tab;   /* decode table of the element type (fp16 or bf16) */
+    int64_t left, right; /* window of the attention without index rows */
 } job_t;
 
 typedef struct {
@@ -110,21 +133,25 @@ static int64_t one_unit(job_t *j, int64_t u, scratch_t *w) {
                 if (n <= m) w->keys[nk++] = n;
         }
     } else {
-        /* Dense attention: every causally visible key n <= m, n < N. */
-        for (int64_t n = 0; n <= m && n < N; ++n) w->keys[nk++] = n;
+        /* Attention without index rows: every key n < N with
+           m - left <= n <= m + right (a negative bound is unbounded);
+           (left, right) = (-1, 0) is dense causal attention. */
+        const int64_t lo = j->left < 0 ? 0 : m - j->left;
+        const int64_t hi = j->right < 0 ? N - 1 : m + j->right;
+        for (int64_t n = lo < 0 ? 0 : lo; n <= hi && n < N; ++n) w->keys[nk++] = n;
     }
 
     /* Head h = g*gs + i of query m, decoded. */
     for (int64_t i = 0; i < gs; ++i) {
         const uint16_t *q = j->Q + ((b * M + m) * H + g * gs + i) * D;
-        for (int64_t d = 0; d < D; ++d) w->qd[i * D + d] = g_half[q[d]];
+        for (int64_t d = 0; d < D; ++d) w->qd[i * D + d] = j->tab[q[d]];
     }
 
     /* Pass 1: scores s = scale * q.k for every head and key, and their maxima. */
     for (int64_t i = 0; i < gs; ++i) w->mu[i] = -INFINITY;
     for (int64_t s = 0; s < nk; ++s) {
         const uint16_t *k = j->K + ((b * N + w->keys[s]) * G + g) * D;
-        for (int64_t d = 0; d < D; ++d) w->kd[d] = g_half[k[d]];
+        for (int64_t d = 0; d < D; ++d) w->kd[d] = j->tab[k[d]];
         for (int64_t i = 0; i < gs; ++i) {
             double acc = 0.0;
             for (int64_t d = 0; d < D; ++d) acc += w->qd[i * D + d] * w->kd[d];
@@ -142,7 +169,7 @@ static int64_t one_unit(job_t *j, int64_t u, scratch_t *w) {
     }
     for (int64_t s = 0; s < nk; ++s) {
         const uint16_t *v = j->V + ((b * N + w->keys[s]) * G + g) * D;
-        for (int64_t d = 0; d < D; ++d) w->kd[d] = g_half[v[d]];
+        for (int64_t d = 0; d < D; ++d) w->kd[d] = j->tab[v[d]];
         for (int64_t i = 0; i < gs; ++i) {
             const double e = exp(w->score[i * N + s] - w->mu[i]);
             double *o = j->O + (u * gs + i) * D;
@@ -203,7 +230,8 @@ static int run_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                      const int32_t *block_indices, int64_t B, int64_t M, int64_t N,
                      int64_t H, int64_t G, int64_t D, int64_t block_size, int64_t T,
                      const int64_t *units, int64_t n_units, double *O, double *LSE,
-                     int64_t *n_dup, int n_threads) {
+                     int64_t *n_dup, int elem, int64_t left, int64_t right, int n_threads) {
+    if (elem != 0 && elem != 1) return -1;
     if (!Q || !K || !V || !units || !O || !LSE) return -1;
     if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1 || block_size < 1 || T < 1) return -1;
     if (H % G) return -1;
@@ -232,6 +260,8 @@ static int run_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
         j->bs = block_size; j->T = T;
         j->units = units; j->n_units = n_units; j->O = O; j->LSE = LSE;
         j->thread_id = i; j->n_threads = n_threads;
+        j->tab = elem ? g_bf16 : g_half;
+        j->left = left; j->right = right;
     }
     int started = 0;
     for (int i = 0; i < n_threads; ++i) {
@@ -260,8 +290,19 @@ int nsa_oracle_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
                      const int64_t *units, int64_t n_units, double *O, double *LSE,
                      int64_t *n_dup, int n_threads) {
     if (!block_indices) return -1;
+    return run_units(Q, K, V, block_indices, B, M, N, H, G, D, block_size, T, units, n_units, O, LSE, n_dup, 0,
+                     -1, 0, n_threads);
+}
+
+/* As nsa_oracle_units for Q, K, V of element type elem: 0 = fp16, 1 = bf16. */
+int nsa_oracle_units_t(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
+                       const int32_t *block_indices, int64_t B, int64_t M, int64_t N,
+                       int64_t H, int64_t G, int64_t D, int64_t block_size, int64_t T,
+                       const int64_t *units, int64_t n_units, double *O, double *LSE,
+                       int64_t *n_dup, int elem, int n_threads) {
+    if (!block_indices) return -1;
     return run_units(Q, K, V, block_indices, B, M, N, H, G, D, block_size, T, units, n_units, O, LSE, n_dup,
-                     n_threads);
+                     elem, -1, 0, n_threads);
 }
 
 /*
@@ -273,7 +314,23 @@ int nsa_oracle_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V,
 int nsa_oracle_dense_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t B, int64_t M,
                            int64_t N, int64_t H, int64_t G, int64_t D, const int64_t *units, int64_t n_units,
                            double *O, double *LSE, int n_threads) {
-    return run_units(Q, K, V, NULL, B, M, N, H, G, D, 1, 1, units, n_units, O, LSE, NULL, n_threads);
+    return run_units(Q, K, V, NULL, B, M, N, H, G, D, 1, 1, units, n_units, O, LSE, NULL, 0, -1, 0, n_threads);
+}
+
+/*
+ * Sliding-window attention (the FlyDSL pull request "[Kernel][MI350] Add 8
+ * wave GQA sliding-window attention kernel", section What it does: query i
+ * attends to keys [i - LEFT, i + RIGHT]): every key n < N with
+ * m - left <= n <= m + right, a negative bound meaning unbounded on that side.
+ * (left, right) = (-1, 0) is dense causal attention.  elem: 0 = fp16,
+ * 1 = bf16.  A query whose window holds no key gets O = 0, LSE = -inf.
+ */
+int nsa_oracle_window_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V, int64_t B, int64_t M,
+                            int64_t N, int64_t H, int64_t G, int64_t D, int64_t left, int64_t right,
+                            const int64_t *units, int64_t n_units, double *O, double *LSE, int elem,
+                            int n_threads) {
+    return run_units(Q, K, V, NULL, B, M, N, H, G, D, 1, 1, units, n_units, O, LSE, NULL, elem, left, right,
+                     n_threads);
 }
 
 /*
@@ -356,7 +413,7 @@ static void *bworker(void *arg) {
             const int64_t nk = one_unit(&fj, 0, &w);
             for (int64_t i = 0; i < gs; ++i) {
                 const uint16_t *src = j->dO + ((b * J->M + m) * J->H + g * gs + i) * D;
-                for (int64_t d = 0; d < D; ++d) dOd[i * D + d] = g_half[src[d]];
+                for (int64_t d = 0; d < D; ++d) dOd[i * D + d] = J->tab[src[d]];
             }
             /* dP and Delta. P_n = exp(s_n - LSE). */
             for (int64_t i = 0; i < gs; ++i) {
@@ -366,7 +423,7 @@ static void *bworker(void *arg) {
             }
             for (int64_t s = 0; s < nk; ++s) {
                 const uint16_t *v = J->V + ((b * J->N + w.keys[s]) * J->G + g) * D;
-                for (int64_t d = 0; d < D; ++d) w.kd[d] = g_half[v[d]];
+                for (int64_t d = 0; d < D; ++d) w.kd[d] = J->tab[v[d]];
                 for (int64_t i = 0; i < gs; ++i) {
                     double acc = 0.0;
                     for (int64_t d = 0; d < D; ++d) acc += dOd[i * D + d] * w.kd[d];
@@ -382,7 +439,7 @@ static void *bworker(void *arg) {
             for (int64_t s = 0; s < nk; ++s) {
                 const int64_t n = w.keys[s];
                 const uint16_t *k = J->K + ((b * J->N + n) * J->G + g) * D;
-                for (int64_t d = 0; d < D; ++d) w.kd[d] = g_half[k[d]];
+                for (int64_t d = 0; d < D; ++d) w.kd[d] = J->tab[k[d]];
                 const int64_t pos = kv_pos(j, b, g, n);
                 for (int64_t i = 0; i < gs; ++i) {
                     const double P = exp(w.score[i * J->N + s] - fwdL[i]);
@@ -462,6 +519,8 @@ int nsa_oracle_bwd_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V
         J->bs = block_size; J->T = T;
         J->units = units; J->n_units = n_units;
         J->thread_id = i; J->n_threads = n_threads;
+        J->tab = g_half;
+        J->left = -1; J->right = 0;
         j->dO = dO; j->kblocks = kblocks; j->n_kblocks = n_kblocks; j->dQ = dQ; j->kv_elems = kv_elems;
         j->mQ = mQ;
         j->dK = (double *)calloc((size_t)kv_elems, sizeof(double));
