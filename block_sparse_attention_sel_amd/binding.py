@@ -1,10 +1,12 @@
 """Thin ctypes binding of libnsa_sel.so and libnsa_gather_probe.so.
 
-``nsa_sel_fwd``, ``nsa_sel_bwd``, ``nsa_sel_bwd_workspace_size``,
-``nsa_dense_fwd`` and ``nsa_sel_status_string`` mirror the C entry points one
-to one (pointers may be given as ints or as torch tensors); ``sel_attn_fwd``,
-``sel_attn_bwd`` and ``dense_attn_fwd`` are conveniences that check torch
-tensors, allocate the outputs and call the entry point on the current stream.  ``nsa_gather_probe`` mirrors the
+``nsa_sel_fwd``, ``nsa_sel_fwd_bf16``, ``nsa_sel_bwd``,
+``nsa_sel_bwd_workspace_size``, ``nsa_dense_fwd``, ``nsa_window_fwd``,
+``nsa_window_fwd_bf16`` and ``nsa_sel_status_string`` mirror the C entry points
+one to one (pointers may be given as ints or as torch tensors);
+``sel_attn_fwd``, ``sel_attn_bwd``, ``dense_attn_fwd`` and ``window_attn_fwd``
+are conveniences that check torch tensors, allocate the outputs and call the
+entry point on the current stream (the fp16 or bf16 one by the tensors' dtype).  ``nsa_gather_probe`` mirrors the
 measurement probe of include/nsa_gather_probe.h.  All arithmetic happens in the
 HIP kernels; when a library is missing every call into it raises.
 """
@@ -29,8 +31,8 @@ NSA_SEL_ERR_ALIAS = 6
 NSA_SEL_ERR_HIP = 7
 NSA_SEL_ERR_WORKSPACE = 8
 
-EXPORTED = ("nsa_sel_fwd", "nsa_sel_status_string")
-DENSE_EXPORTED = ("nsa_dense_fwd",)
+EXPORTED = ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_status_string")
+DENSE_EXPORTED = ("nsa_dense_fwd", "nsa_window_fwd", "nsa_window_fwd_bf16")
 BWD_EXPORTED = ("nsa_sel_bwd", "nsa_sel_bwd_workspace_size")
 PROBE_EXPORTED = ("nsa_gather_probe",)
 
@@ -52,12 +54,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(path)
     vp, ci = ctypes.c_void_p, ctypes.c_int
-    lib.nsa_sel_fwd.argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp]
-    lib.nsa_sel_fwd.restype = ci
+    for name in ("nsa_sel_fwd", "nsa_sel_fwd_bf16"):
+        getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp]
+        getattr(lib, name).restype = ci
     lib.nsa_sel_status_string.argtypes = [ci]
     lib.nsa_sel_status_string.restype = ctypes.c_char_p
     lib.nsa_dense_fwd.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
     lib.nsa_dense_fwd.restype = ci
+    for name in ("nsa_window_fwd", "nsa_window_fwd_bf16"):
+        getattr(lib, name).argtypes = [vp, vp, vp, vp, vp] + [ci] * 8 + [vp]
+        getattr(lib, name).restype = ci
     lib.nsa_sel_bwd_workspace_size.argtypes = [ci] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
     lib.nsa_sel_bwd_workspace_size.restype = ci
     lib.nsa_sel_bwd.argtypes = [vp] * 11 + [ctypes.c_size_t] + [ci] * 8 + [vp]
@@ -79,12 +85,15 @@ def nsa_sel_status_string(status: int) -> str:
     return load_library().nsa_sel_status_string(int(status)).decode()
 
 
-def nsa_sel_fwd_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> int:
-    """Calls the C entry point and returns its status code unchanged."""
+def nsa_sel_fwd_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0,
+                    bf16: bool = False) -> int:
+    """Calls the C entry point (nsa_sel_fwd, or nsa_sel_fwd_bf16 when bf16) and
+    returns its status code unchanged."""
     lib = load_library()
-    return lib.nsa_sel_fwd(_addr(Q), _addr(K), _addr(V), _addr(block_indices), _addr(O), _addr(LSE),
-                           int(B), int(M), int(N), int(H), int(G), int(D), int(block_size), int(T),
-                           ctypes.c_void_p(_addr(stream)))
+    fn = lib.nsa_sel_fwd_bf16 if bf16 else lib.nsa_sel_fwd
+    return fn(_addr(Q), _addr(K), _addr(V), _addr(block_indices), _addr(O), _addr(LSE),
+              int(B), int(M), int(N), int(H), int(G), int(D), int(block_size), int(T),
+              ctypes.c_void_p(_addr(stream)))
 
 
 def nsa_sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> None:
@@ -94,12 +103,21 @@ def nsa_sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T,
         raise NsaSelError(rc)
 
 
+def nsa_sel_fwd_bf16(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> None:
+    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
+    rc = nsa_sel_fwd_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, bf16=True)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
 def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, stream=None):
-    """q [B,M,H,D] fp16, k/v [B,N,G,D] fp16, block_indices [B,M,G,T] int32, all
-    contiguous CUDA tensors.  Returns (O [B,M,H,D] fp16, LSE [B,H,M] fp32)."""
+    """q [B,M,H,D], k/v [B,N,G,D] (all fp16 or all bf16), block_indices
+    [B,M,G,T] int32, all contiguous CUDA tensors.  Returns (O [B,M,H,D] in the
+    input dtype, LSE [B,H,M] fp32)."""
     import torch
 
-    for name, t, dt in (("q", q, torch.float16), ("k", k, torch.float16), ("v", v, torch.float16),
+    et = q.dtype if isinstance(q, torch.Tensor) and q.dtype in (torch.float16, torch.bfloat16) else torch.float16
+    for name, t, dt in (("q", q, et), ("k", k, et), ("v", v, et),
                         ("block_indices", block_indices, torch.int32)):
         if not isinstance(t, torch.Tensor) or t.dtype != dt or t.dim() != 4:
             raise TypeError(f"{name} must be a 4-d {dt} tensor")
@@ -111,12 +129,15 @@ def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, st
     if (k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape or tuple(block_indices.shape[:3]) != (B, M, G):
         raise ValueError("inconsistent shapes")
     if out is None:
-        out = torch.empty((B, M, H, D), dtype=torch.float16, device=q.device)
+        out = torch.empty((B, M, H, D), dtype=et, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    nsa_sel_fwd(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
+    if et == torch.bfloat16:
+        nsa_sel_fwd_bf16(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
+    else:
+        nsa_sel_fwd(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
     return out, lse
 
 
@@ -225,6 +246,55 @@ def dense_attn_fwd(q, k, v, out=None, lse=None, stream=None):
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
     nsa_dense_fwd(q, k, v, out, lse, B, M, N, H, G, D, stream)
+    return out, lse
+
+
+def nsa_window_fwd_raw(Q, K, V, O, LSE, B, M, N, H, G, D, left, right, stream=0, bf16: bool = False) -> int:
+    """Calls nsa_window_fwd (or nsa_window_fwd_bf16) and returns its status code unchanged."""
+    lib = load_library()
+    fn = lib.nsa_window_fwd_bf16 if bf16 else lib.nsa_window_fwd
+    return fn(_addr(Q), _addr(K), _addr(V), _addr(O), _addr(LSE), int(B), int(M), int(N), int(H), int(G), int(D),
+              int(left), int(right), ctypes.c_void_p(_addr(stream)))
+
+
+def nsa_window_fwd(Q, K, V, O, LSE, B, M, N, H, G, D, left, right, stream=0) -> None:
+    rc = nsa_window_fwd_raw(Q, K, V, O, LSE, B, M, N, H, G, D, left, right, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def nsa_window_fwd_bf16(Q, K, V, O, LSE, B, M, N, H, G, D, left, right, stream=0) -> None:
+    rc = nsa_window_fwd_raw(Q, K, V, O, LSE, B, M, N, H, G, D, left, right, stream, bf16=True)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def window_attn_fwd(q, k, v, left: int, right: int, out=None, lse=None, stream=None):
+    """Sliding-window GQA attention (keys m-left .. m+right, negative =
+    unbounded): q [B,M,H,D], k/v [B,N,G,D], all fp16 or all bf16 contiguous CUDA
+    tensors.  Returns (O [B,M,H,D] in the input dtype, LSE [B,H,M] fp32)."""
+    import torch
+
+    et = q.dtype if isinstance(q, torch.Tensor) and q.dtype in (torch.float16, torch.bfloat16) else torch.float16
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dtype != et or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-d {et} tensor")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, M, H, D = q.shape
+    _, N, G, _ = k.shape
+    if (k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape:
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty((B, M, H, D), dtype=et, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    if et == torch.bfloat16:
+        nsa_window_fwd_bf16(q, k, v, out, lse, B, M, N, H, G, D, left, right, stream)
+    else:
+        nsa_window_fwd(q, k, v, out, lse, B, M, N, H, G, D, left, right, stream)
     return out, lse
 
 

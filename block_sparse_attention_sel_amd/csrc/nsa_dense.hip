@@ -1,11 +1,16 @@
-// Dense causal GQA attention forward for AMD MI355X (gfx950): the baseline
-// the selection kernel is compared with (include/nsa_dense.h).
+// Dense and sliding-window GQA attention forward for AMD MI355X (gfx950):
+// the baseline the selection kernel is compared with, and the sliding-window
+// variant (include/nsa_dense.h).
 //
 // Operation: every causal key of the query (n <= m, n < N) for all H/G heads
 // of the group, one softmax, O and the natural-log LSE -- selection attention
 // with every block selected (wave issue "[wave] NSA: selection attention
 // forward kernel", section Performance target, names this dense attention as
-// the reference point).
+// the reference point).  The window variant keeps the keys
+// m - LEFT <= n <= m + RIGHT (the FlyDSL pull request "[Kernel][MI350] Add 8
+// wave GQA sliding-window attention kernel", section What it does), a
+// workgroup streaming only the key range its queries' windows cover; fp16 or
+// bf16 operands.
 //
 // MI355X mapping.  The per-step math is the selection kernel's (transposed
 // scores S^T = K Q^T on v_mfma_f32_16x16x32_f16 with P kept in registers as
@@ -42,10 +47,11 @@ struct DenseParams {
     int qtiles;   // query tiles per (b, g)
     int units;    // B * G * qtiles
     int per_xcd;  // ceil(units / 8)
+    int left, right;  // window: keys m - left .. m + right visible (negative = unbounded)
     float scale_log2;
 };
 
-template <int D, int PACK>
+template <int D, int PACK, bool BF16>
 __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(DenseParams p) {
     constexpr int NT = kDenseTiles;
     constexpr int QWG = kDenseWaves * NT * PACK;  // queries per workgroup
@@ -118,18 +124,28 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
         }
     }
 
-    // Sub-blocks 0 .. nsub-1 cover keys 0 .. min(N, q_last + 1) - 1.
-    const int nkeys = min(p.N, q_last + 1);
-    const int nsub = (nkeys + SBS - 1) / SBS;
+    // Keys any query of the workgroup sees: [k_lo, k_hi] (causal: 0 ..
+    // min(N, q_last + 1) - 1); sub-blocks s_begin .. s_begin + nsub - 1.
+    const int k_lo = p.left < 0 ? 0 : max(0, q0 - p.left);
+    const int k_hi = p.right < 0 ? p.N - 1 : min(p.N - 1, q_last + p.right);
+    const int s_begin = k_lo / SBS;
+    const int nsub = k_hi < k_lo ? 0 : k_hi / SBS - s_begin + 1;
+    // Each column's visible keys [c_lo[nt], c_hi[nt]].
+    int c_lo[NT], c_hi[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        c_lo[nt] = p.left < 0 ? INT_MIN : my_m[nt] - p.left;
+        c_hi[nt] = p.right < 0 ? p.N - 1 : min(my_m[nt] + p.right, p.N - 1);
+    }
     auto issue = [&](int s) {
         const int slot = s % kStages;
 #pragma unroll
         for (int k = 0; k < IPW; ++k) {
             const int j = wave + k * kDenseWaves;  // this wavefront's share of the 2*NI instructions
             if (j < NI)
-                st.issue_part(st.rk, kbuf[slot], s, j, lane);
+                st.issue_part(st.rk, kbuf[slot], s_begin + s, j, lane);
             else
-                st.issue_part(st.rv, vbuf[slot], s, j - NI, lane);
+                st.issue_part(st.rv, vbuf[slot], s_begin + s, j - NI, lane);
         }
     };
 #pragma unroll
@@ -150,22 +166,29 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
         if (s + kStages - 1 < nsub) issue(s + kStages - 1);
 
         const int slot = s % kStages;
-        const int key0 = s * SBS;
+        const int key0 = (s_begin + s) * SBS;
         Stage<SBS, D, 1>::read(kf, kbuf[slot], r, q4);
         bool on[NT];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
+            // Uniform over the tile: the union of its queries' windows is
+            // [t_lo, t_hi]; some key of the sub-block lies outside a column's
+            // window when it passes the smallest upper or the largest lower
+            // bound.
             const int tile_last = min(mt[nt] + PACK, p.M) - 1;
-            on[nt] = mt[nt] < p.M && key0 <= tile_last;  // uniform: some query of the tile sees a key here
+            const int t_lo = p.left < 0 ? 0 : mt[nt] - p.left;
+            const int t_hi = p.right < 0 ? p.N - 1 : min(p.N - 1, tile_last + p.right);
+            on[nt] = mt[nt] < p.M && key0 <= t_hi && key0 + SBS - 1 >= t_lo;
             if (!on[nt]) continue;
-            const bool causal = (key0 + SBS - 1 > mt[nt]) || (key0 + SBS > p.N);
-            score_block<SBS, D>(kf, qf[nt], key0, causal, true, live[nt], min(my_m[nt], p.N - 1), p.scale_log2, m_run[nt],
-                                l_run[nt], alpha[nt], pf[nt], q4);
+            const int min_hi = p.right < 0 ? p.N - 1 : min(p.N - 1, mt[nt] + p.right);
+            const bool masked = (key0 + SBS - 1 > min_hi) || (p.left >= 0 && key0 < tile_last - p.left);
+            score_block<SBS, D, BF16>(kf, qf[nt], key0, masked, true, live[nt], c_lo[nt], c_hi[nt], p.scale_log2,
+                                      m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
         }
         Stage<SBS, D, 1>::read_vt(vt, vbuf[slot], lane);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            if (on[nt]) accumulate_block<SBS, D>(vt, pf[nt], alpha[nt], acc[nt]);
+            if (on[nt]) accumulate_block<SBS, D, BF16>(vt, pf[nt], alpha[nt], acc[nt]);
     }
 
     // Epilogue: total row sum over the 4 lanes of a column, normalise, store.
@@ -177,8 +200,8 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
             _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + my_h) * D;
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
-                const half4 lo = to_half4(acc[nt][c][0] * inv);
-                const half4 hi = to_half4(acc[nt][c][1] * inv);
+                const half4 lo = pack4<BF16>(acc[nt][c][0] * inv);
+                const half4 hi = pack4<BF16>(acc[nt][c][1] * inv);
                 __builtin_nontemporal_store(cat8(lo, hi), (half8 *)(orow + c * 32 + q4 * 8));
             }
             if (q4 == 0) {
@@ -189,17 +212,28 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
     }
 }
 
-template <int D, int PACK>
+template <int D, int PACK, bool BF16>
 hipError_t launch_dense(const DenseParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((nsa_dense_kernel<D, PACK>), dim3(p.per_xcd * kNumXcd), dim3(kWaveSize * kDenseWaves), 0,
-                       stream, p);
+    hipLaunchKernelGGL((nsa_dense_kernel<D, PACK, BF16>), dim3(p.per_xcd * kNumXcd), dim3(kWaveSize * kDenseWaves),
+                       0, stream, p);
     return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_dense_dt(const DenseParams &p, int D, int pack, hipStream_t stream) {
+    if (D == 128)
+        return pack == 4 ? launch_dense<128, 4, BF16>(p, stream) : pack == 2 ? launch_dense<128, 2, BF16>(p, stream)
+                                                                                : launch_dense<128, 1, BF16>(p, stream);
+    return pack == 4 ? launch_dense<64, 4, BF16>(p, stream) : pack == 2 ? launch_dense<64, 2, BF16>(p, stream)
+                                                                         : launch_dense<64, 1, BF16>(p, stream);
 }
 
 }  // namespace
 
-extern "C" int nsa_dense_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N,
-                             int H, int G, int D, hipStream_t stream) {
+namespace {
+
+int window_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N, int H, int G,
+               int D, int left, int right, hipStream_t stream, bool bf16) {
     if (!Q || !K || !V || !O || !LSE) return NSA_SEL_ERR_NULL;
     if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1) return NSA_SEL_ERR_SHAPE;
     if (H % G != 0) return NSA_SEL_ERR_SHAPE;
@@ -207,7 +241,8 @@ extern "C" int nsa_dense_fwd(const void *Q, const void *K, const void *V, void *
     if ((D != 64 && D != 128) || gs > 16) return NSA_SEL_ERR_UNSUPPORTED;
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15) return NSA_SEL_ERR_ALIGN;
     if ((uintptr_t)LSE & 3) return NSA_SEL_ERR_ALIGN;
-    if ((int64_t)B * M * G > INT_MAX || (int64_t)N * G * D > INT_MAX) return NSA_SEL_ERR_RANGE;
+    if ((int64_t)B * M * G > INT_MAX || (int64_t)N * G * D > INT_MAX || (int64_t)M + N > INT_MAX)
+        return NSA_SEL_ERR_RANGE;
     const size_t q_bytes = (size_t)B * M * H * D * 2, kv_bytes = (size_t)B * N * G * D * 2;
     const size_t lse_bytes = (size_t)B * H * M * 4;
     const void *ins[3] = {Q, K, V};
@@ -230,13 +265,28 @@ extern "C" int nsa_dense_fwd(const void *Q, const void *K, const void *V, void *
     p.qtiles = (M + qwg - 1) / qwg;
     p.units = B * G * p.qtiles;
     p.per_xcd = (p.units + kNumXcd - 1) / kNumXcd;
+    // A bound that reaches past every query (left >= M) or every key
+    // (right >= N) is the same as none.
+    p.left = (left < 0 || left >= M) ? -1 : left;
+    p.right = (right < 0 || right >= N) ? -1 : right;
     p.scale_log2 = kLog2e / sqrtf((float)D);
-    hipError_t e;
-    if (D == 128)
-        e = pack == 4 ? launch_dense<128, 4>(p, stream) : pack == 2 ? launch_dense<128, 2>(p, stream)
-                                                                     : launch_dense<128, 1>(p, stream);
-    else
-        e = pack == 4 ? launch_dense<64, 4>(p, stream) : pack == 2 ? launch_dense<64, 2>(p, stream)
-                                                                    : launch_dense<64, 1>(p, stream);
+    const hipError_t e = bf16 ? launch_dense_dt<true>(p, D, pack, stream) : launch_dense_dt<false>(p, D, pack, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int nsa_dense_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N,
+                             int H, int G, int D, hipStream_t stream) {
+    return window_fwd(Q, K, V, O, LSE, B, M, N, H, G, D, -1, 0, stream, false);
+}
+
+extern "C" int nsa_window_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N,
+                              int H, int G, int D, int left, int right, hipStream_t stream) {
+    return window_fwd(Q, K, V, O, LSE, B, M, N, H, G, D, left, right, stream, false);
+}
+
+extern "C" int nsa_window_fwd_bf16(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M,
+                                   int N, int H, int G, int D, int left, int right, hipStream_t stream) {
+    return window_fwd(Q, K, V, O, LSE, B, M, N, H, G, D, left, right, stream, true);
 }

@@ -41,7 +41,7 @@ namespace {
 // SPLIT > 1 stages and computes each selected block as SPLIT consecutive
 // sub-blocks of SBS = BS / SPLIT keys: half the LDS per wavefront, so twice as
 // many wavefronts fit a CU.
-template <int BS, int SPLIT, int D, int PACK, int NT, class Merger>
+template <int BS, int SPLIT, int D, int PACK, int NT, class Merger, bool BF16>
 __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf) {
     constexpr int SBS = BS / SPLIT;
     constexpr int DC = D / 32;
@@ -142,8 +142,8 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             const int first_m = m0 + nt * PACK;
             const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
             const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
-            score_block<SBS, D>(kf, qf[nt], key0, causal, true, col_on, min(my_m[nt], p.N - 1), p.scale_log2, m_run[nt],
-                                l_run[nt], alpha[nt], pf[nt], q4);
+            score_block<SBS, D, BF16>(kf, qf[nt], key0, causal, true, col_on, INT_MIN, min(my_m[nt], p.N - 1),
+                                      p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
         }
         if (has1)
             __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(s0) landed; K(s1) may be pending
@@ -154,7 +154,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (((a0 >> (nt * PACK)) & tile_bits) == 0) continue;
-            accumulate_block<SBS, D>(vt, pf[nt], alpha[nt], acc[nt]);
+            accumulate_block<SBS, D, BF16>(vt, pf[nt], alpha[nt], acc[nt]);
         }
         s0 = s1;
         a0 = a1;
@@ -169,8 +169,8 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             _Float16 *orow = p.O + ((size_t)(b * (size_t)p.M + my_m[nt]) * p.H + my_h) * D;
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
-                const half4 lo = to_half4(acc[nt][c][0] * inv);
-                const half4 hi = to_half4(acc[nt][c][1] * inv);
+                const half4 lo = pack4<BF16>(acc[nt][c][0] * inv);
+                const half4 hi = pack4<BF16>(acc[nt][c][1] * inv);
                 __builtin_nontemporal_store(cat8(lo, hi), (half8 *)(orow + c * 32 + q4 * 8));
             }
             if (q4 == 0) {
@@ -184,7 +184,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
 
 // MODE 0: rows streamed through cursors (any T), one tile.  MODE 1/2: rows
 // held in registers, NT = MODE tiles.
-template <int BS, int SPLIT, int D, int PACK, int MODE>
+template <int BS, int SPLIT, int D, int PACK, int MODE, bool BF16>
 __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_fwd_kernel(Params p) {
     constexpr int SBS = BS / SPLIT;
     constexpr int WAVES = waves_per_wg(SBS);
@@ -195,16 +195,17 @@ __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_
     const int ws = wave_slot<WAVES>(p, wave);
     if (ws < 0) return;
     if constexpr (MODE == 0)
-        run_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+        run_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>, BF16>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
     else
-        run_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, ws, lane, kbuf_all[wave],
-                                                                         vbuf_all[wave]);
+        run_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>, BF16>(p, ws, lane, kbuf_all[wave],
+                                                                               vbuf_all[wave]);
 }
 
+template <bool BF16>
 struct FwdKernel {
     template <int BS, int SPLIT, int D, int PACK, int MODE>
     void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
-        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE, BF16>), grid, block, 0, stream, p);
     }
 };
 
@@ -228,9 +229,10 @@ extern "C" const char *nsa_sel_status_string(int status) {
     }
 }
 
-extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
-                           void *O, float *LSE, int B, int M, int N, int H, int G, int D,
-                           int block_size, int T, hipStream_t stream) {
+namespace {
+
+int sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices, void *O, float *LSE, int B,
+            int M, int N, int H, int G, int D, int block_size, int T, hipStream_t stream, bool bf16) {
     if (!Q || !K || !V || !block_indices || !O || !LSE) return NSA_SEL_ERR_NULL;
     Params p;
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
@@ -257,6 +259,21 @@ extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const in
     p.idx = block_indices;
     p.O = (_Float16 *)O;
     p.LSE = LSE;
-    const hipError_t e = launch_all(FwdKernel{}, p, block_size, D, cus, stream);
+    const hipError_t e = bf16 ? launch_all(FwdKernel<true>{}, p, block_size, D, cus, stream)
+                              : launch_all(FwdKernel<false>{}, p, block_size, D, cus, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int nsa_sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                           void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                           int block_size, int T, hipStream_t stream) {
+    return sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, false);
+}
+
+extern "C" int nsa_sel_fwd_bf16(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                                void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                                int block_size, int T, hipStream_t stream) {
+    return sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, true);
 }

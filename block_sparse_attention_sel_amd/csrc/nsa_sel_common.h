@@ -21,8 +21,13 @@
 
 namespace {
 
+// Fragments are held as 16-bit containers (half8 / half4) whatever the
+// element type: the staging, the LDS reads and the transposes only move bits;
+// the MFMA and the float -> 16-bit packing are the type-specific steps.
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
@@ -490,6 +495,31 @@ __device__ __forceinline__ half8 cat8(half4 a, half4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Element-type-generic steps: BF16 selects bfloat16 operands (MFMA bf16,
+// round-to-nearest-even packing), else fp16.
+template <bool BF16>
+__device__ __forceinline__ float4v mfma16(half8 a, half8 b, float4v c) {
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                        c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ half4 pack4(float4v v) {
+    if constexpr (BF16) {
+        bf16x4 r;
+        r[0] = (__bf16)v[0];
+        r[1] = (__bf16)v[1];
+        r[2] = (__bf16)v[2];
+        r[3] = (__bf16)v[3];
+        return __builtin_bit_cast(half4, r);
+    } else {
+        return to_half4(v);
+    }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Max and sum over the four lanes l%16 + 16*j of an MFMA result (one column)
@@ -514,9 +544,11 @@ __device__ __forceinline__ float col_sum(float x) {
 // the running max, the rescale factor of the accumulator and the block's
 // probabilities P^T (fp16), all in the log2 domain (x * log2(e) / sqrt(D)).
 //
-// causal: the block reaches past the smallest packed query or past N, so
-//   keys past the column's last visible key lim = min(its query, N - 1) are
-//   masked to -inf (one comparison per key; the caller forms lim once).
+// causal: the block reaches past the smallest packed query or past N (or,
+//   for a sliding window, before some column's first visible key), so keys
+//   outside the column's visible range [lo, lim] are masked to -inf (the
+//   caller forms lo and lim once; lim = min(its query, N - 1) for causal
+//   attention, lo = INT_MIN when there is no lower bound).
 // col_mask: some packed query did not select this block; for those columns
 //   (col_on false) the running state is left unchanged and P is zero.
 // The running max is only raised when a block's max exceeds it by more than
@@ -524,9 +556,9 @@ __device__ __forceinline__ float col_sum(float x) {
 // need no rescale of the accumulator (alpha == 1 exactly).
 constexpr float kLazyMax = 8.0f;
 
-template <int BS, int D>
+template <int BS, int D, bool BF16 = false>
 __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
-                                            int key0, bool causal, bool col_mask, bool col_on, int lim,
+                                            int key0, bool causal, bool col_mask, bool col_on, int lo, int lim,
                                             float scale_log2, float &m_run, float &l_run,
                                             float &alpha, half4 (&pf)[BS / 16], int q4) {
     constexpr int KT = BS / 16;
@@ -536,7 +568,7 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
     for (int kt = 0; kt < KT; ++kt) {
         s[kt] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < DC; ++c) s[kt] = mfma_16x16x32(kf[kt][c], qf[c], s[kt]);
+        for (int c = 0; c < DC; ++c) s[kt] = mfma16<BF16>(kf[kt][c], qf[c], s[kt]);
     }
     if (causal) {
 #pragma unroll
@@ -544,7 +576,7 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = key0 + kt * 16 + q4 * 4 + i;
-                if (key > lim) s[kt][i] = -INFINITY;
+                if (key > lim || key < lo) s[kt][i] = -INFINITY;
             }
     }
     // Row max of the raw scores (the scale is positive), then over the 4
@@ -571,7 +603,7 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
             pv[i] = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -m_exp));
             psum += pv[i];
         }
-        pf[kt] = to_half4(pv);
+        pf[kt] = pack4<BF16>(pv);
     }
     l_run = l_run * alpha + psum;  // per-lane partial; lanes are summed at the end
 }
@@ -579,7 +611,7 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
 // O^T = alpha * O^T + V^T * P^T over 32-key chunks.  acc[c][hh] holds O^T rows
 // d = 32*c + 8*(l/16) + 4*hh + i for head l%16.  The B operand is P^T straight
 // from the score layout; the A operand V^T comes from the transposing reads.
-template <int BS, int D>
+template <int BS, int D, bool BF16 = false>
 __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 32][2][2],
                                                  const half4 (&pf)[BS / 16], float alpha,
                                                  float4v (&acc)[D / 32][2]) {
@@ -598,7 +630,7 @@ __device__ __forceinline__ void accumulate_block(const half4 (&vt)[BS / 32][D / 
         for (int c = 0; c < DC; ++c)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
-                acc[c][hh] = mfma_16x16x32(cat8(vt[kc][c][hh][0], vt[kc][c][hh][1]), bp, acc[c][hh]);
+                acc[c][hh] = mfma16<BF16>(cat8(vt[kc][c][hh][0], vt[kc][c][hh][1]), bp, acc[c][hh]);
     }
 }
 

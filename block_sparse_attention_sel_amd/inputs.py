@@ -110,6 +110,35 @@ def normal_fp16(shape, seed: int, stream: int, threads: int | None = None) -> np
     return out.reshape(shape)
 
 
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even.
+    Finite inputs only."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + (0x7FFF + ((u >> 16) & 1))) >> 16).astype(np.uint16)
+
+
+def normal_bf16(shape, seed: int, stream: int, threads: int | None = None) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of the same N(0,1) float32 draws as
+    normal_fp16(shape, seed, stream), rounded to bf16 instead of fp16."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    nchunks = -(-n // CHUNK)
+
+    def fill(i):
+        lo = i * CHUNK
+        hi = min(n, lo + CHUNK)
+        key = np.array([seed, (stream << 32) + i], dtype=np.uint64)
+        rng = np.random.Generator(np.random.Philox(key=key))
+        out[lo:hi] = to_bf16_bits(rng.standard_normal(hi - lo, dtype=np.float32))
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(threads or _threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
 def _rng(seed: int, stream: int, sub: int = 0) -> np.random.Generator:
     key = np.array([seed, (stream << 32) + sub], dtype=np.uint64)
     return np.random.Generator(np.random.Philox(key=key))
@@ -227,6 +256,16 @@ def make_inputs(cfg: Config, threads: int | None = None):
     q = normal_fp16((cfg.B, cfg.M, cfg.H, cfg.D), cfg.seed, STREAM_Q, threads)
     k = normal_fp16((cfg.B, cfg.N, cfg.G, cfg.D), cfg.seed, STREAM_K, threads)
     v = normal_fp16((cfg.B, cfg.N, cfg.G, cfg.D), cfg.seed, STREAM_V, threads)
+    idx = block_indices(cfg, threads)
+    return q, k, v, idx
+
+
+def make_inputs_bf16(cfg: Config, threads: int | None = None):
+    """(Q, K, V, block_indices) with Q, K, V as bfloat16 bit patterns (uint16):
+    the same draws and index rows as make_inputs, rounded to bf16."""
+    q = normal_bf16((cfg.B, cfg.M, cfg.H, cfg.D), cfg.seed, STREAM_Q, threads)
+    k = normal_bf16((cfg.B, cfg.N, cfg.G, cfg.D), cfg.seed, STREAM_K, threads)
+    v = normal_bf16((cfg.B, cfg.N, cfg.G, cfg.D), cfg.seed, STREAM_V, threads)
     idx = block_indices(cfg, threads)
     return q, k, v, idx
 

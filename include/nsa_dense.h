@@ -1,6 +1,7 @@
 /*
  * nsa_dense.h -- dense causal GQA attention forward, the baseline the NSA
- * selection kernel (nsa_sel.h) is measured against.
+ * selection kernel (nsa_sel.h) is measured against, and its sliding-window
+ * variant (fp16 and bf16).
  *
  * Operation: the attention that selection attention replaces.  Wave issue
  * "[wave] NSA: selection attention forward kernel", section Performance
@@ -52,6 +53,35 @@ extern "C" {
  */
 int nsa_dense_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N, int H,
                   int G, int D, hipStream_t stream);
+
+/*
+ * nsa_window_fwd -- sliding-window GQA attention forward, fp16.
+ *
+ * Operation: the FlyDSL pull request "[Kernel][MI350] Add 8 wave GQA
+ * sliding-window attention kernel" (section What it does) describes a kernel
+ * for windows (LEFT, RIGHT): query i attends to the keys [i - LEFT, i + RIGHT].
+ * Here query m of (b, h) attends to the keys n < N with
+ * m - left <= n <= m + right; a negative bound leaves that side unbounded, so
+ * (left, right) = (-1, 0) is nsa_dense_fwd and (-1, -1) full (non-causal)
+ * attention.  Scores, scale, GQA mapping, O and LSE as for nsa_dense_fwd; a
+ * query whose window holds no key gets O = 0 and LSE = -inf.
+ *
+ * Arguments and behaviour as nsa_dense_fwd (same checks and status codes;
+ * NSA_SEL_ERR_RANGE also when M + N exceeds INT_MAX).  A workgroup streams
+ * only the keys its queries' windows cover, so the work is proportional to
+ * the window.
+ */
+int nsa_window_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N, int H,
+                   int G, int D, int left, int right, hipStream_t stream);
+
+/*
+ * nsa_window_fwd_bf16 -- nsa_window_fwd with bfloat16 Q, K, V and O (the
+ * dtype of the FlyDSL kernel, section Summary: bf16 I/O).  Products take bf16
+ * operands (P is rounded to bf16 for the PV product) and accumulate in fp32;
+ * LSE stays fp32.
+ */
+int nsa_window_fwd_bf16(const void *Q, const void *K, const void *V, void *O, float *LSE, int B, int M, int N,
+                        int H, int G, int D, int left, int right, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-/* Status codes returned by nsa_sel_fwd. */
+/* Status codes returned by the entry points of this library. */
 enum {
     NSA_SEL_OK = 0,
     NSA_SEL_ERR_NULL = 1,        /* a pointer argument is NULL                      */
@@ -74,6 +74,17 @@ enum {
 int nsa_sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
                 void *O, float *LSE, int B, int M, int N, int H, int G, int D,
                 int block_size, int T, hipStream_t stream);
+
+/*
+ * nsa_sel_fwd_bf16 -- nsa_sel_fwd with bfloat16 Q, K, V and O (bf16 I/O, the
+ * dtype of the FlyDSL pull request "[Kernel][MI350] Add 8 wave GQA
+ * sliding-window attention kernel", section Summary).  Same arguments, checks
+ * and behaviour; products take bf16 operands (P is rounded to bf16 for the PV
+ * product) and accumulate in fp32; LSE stays fp32.
+ */
+int nsa_sel_fwd_bf16(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                     void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                     int block_size, int T, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *nsa_sel_status_string(int status);

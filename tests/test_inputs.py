@@ -113,3 +113,18 @@ def test_sample_units_cover_edges_and_are_unique():
     assert np.unique(key).size == key.size
     assert (u[:, 1] == 0).sum() == cfg.G and (u[:, 1] == cfg.M - 1).sum() == cfg.G
     assert np.all((u >= 0) & (u < np.array([cfg.B, cfg.M, cfg.G])))
+
+
+def test_bf16_rounding_matches_torch():
+    import torch
+    from block_sparse_attention_sel_amd.inputs import normal_bf16, normal_fp16, to_bf16_bits
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(1 << 16) * np.exp(rng.uniform(-20, 20, 1 << 16))).astype(np.float32)
+    x[:4] = [0.0, -0.0, 1.0, -3.5]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(to_bf16_bits(x), want)
+    # same draws as the fp16 generator: the two roundings of one float32 agree to bf16 precision
+    a = normal_bf16((3, 1000), 5, 1)
+    b = normal_fp16((3, 1000), 5, 1).astype(np.float32)
+    af = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.all(np.abs(af - b) <= 2.0 ** -8 * np.abs(b) + 2.0 ** -14)

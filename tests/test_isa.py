@@ -70,5 +70,5 @@ def test_no_scalar_spills_on_the_register_merger_path(kernels):
     # registers per lane) keeps some cursor state in VGPR lanes.
     _, meta = kernels
     for name, text in meta.items():
-        if not re.search(r"ELi0EEEvNS_6ParamsE(P|NS_6DqArgsE|$)", name):
+        if not re.search(r"ELi0E(Lb[01]E)?EEvNS_6ParamsE(P|NS_6DqArgsE|$)", name):
             assert _spills(text, "sgpr_spill_count") == 0, name
