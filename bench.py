@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from block_sparse_attention_sel_amd.inputs import (CONFIGS, Config, block_indices, make_grad_output,  # noqa: E402
-                                                   make_inputs)
+                                                   make_inputs, make_inputs_bf16)
 
 HBM_PEAK_GBPS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
@@ -227,6 +227,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=3)
     ap.add_argument("--no-dense-fa", action="store_true", help="skip the dense causal attention kernel")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
+    ap.add_argument("--no-window", action="store_true", help="skip the sliding-window kernel runs")
+    ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 selection forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10, help="cold-cache timed calls (0 = skip)")
     ap.add_argument("--no-probe", action="store_true", help="skip the gather-ceiling probe")
@@ -400,6 +402,57 @@ def main():
                            "effective_flops": b_flops, "ratio_bwd_over_fwd": round(b_ev / ev_ms, 2),
                            "workspace_MiB": round(nbytes / 2 ** 20, 1)}
         del tdo, ws, dq, dk, dv
+
+    if not args.no_bf16:
+        # The selection forward with bf16 Q, K, V, O (same draws, rounded to bf16).
+        import torch as _t
+        from block_sparse_attention_sel_amd.binding import nsa_sel_fwd_bf16
+        print("[bench] bf16 selection forward", file=sys.stderr, flush=True)
+        qb, kb, vb, _ = make_inputs_bf16(cfg)
+        bq, bk, bv = (_t.from_numpy(a.view(np.int16)).view(_t.bfloat16).to(dev) for a in (qb, kb, vb))
+        del qb, kb, vb
+        Ob = torch.empty((cfg.B, cfg.M, cfg.H, cfg.D), dtype=torch.bfloat16, device=dev)
+
+        def sel_bf16():
+            nsa_sel_fwd_bf16(bq, bk, bv, ti, Ob, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
+                             stream.cuda_stream)
+
+        _, s_ev, s_min = time_launches(torch, sel_bf16, args.steps, args.warmup)
+        out["bf16"] = {"kernel": "nsa_sel_fwd_bf16", "ms": round(s_ev, 4), "ms_min": round(s_min, 4),
+                       "eff_TFLOPs": round(flops / (s_ev * 1e-3) / 1e12, 3),
+                       "ratio_bf16_over_fp16": round(s_ev / ev_ms, 3)}
+        if args.no_window:
+            del bq, bk, bv, Ob
+
+    if not args.no_window:
+        # Sliding-window attention (keys m - LEFT .. m) on the same tensors at
+        # the FlyDSL page's windows.  Flops: 4 * D * (H/G) per visible
+        # (query, key) pair; the page's TF column counts half of that.
+        from block_sparse_attention_sel_amd.binding import nsa_window_fwd, nsa_window_fwd_bf16
+        runs = []
+        m = np.arange(cfg.M, dtype=np.int64)
+        for left in (512, 8192):
+            pairs = int(np.minimum(np.minimum(m, left) + 1, np.maximum(cfg.N - np.maximum(m - left, 0), 0)).sum())
+            wflops = 4.0 * cfg.D * cfg.H * pairs * cfg.B
+            for dt in ("fp16", "bf16"):
+                if dt == "bf16" and args.no_bf16:
+                    continue
+                print(f"[bench] window ({left}, 0) {dt}", file=sys.stderr, flush=True)
+                if dt == "fp16":
+                    def win(left=left):
+                        nsa_window_fwd(tq, tk, tv, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, left, 0,
+                                       stream.cuda_stream)
+                else:
+                    def win(left=left):
+                        nsa_window_fwd_bf16(bq, bk, bv, Ob, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, left, 0,
+                                            stream.cuda_stream)
+                _, w_ev, w_min = time_launches(torch, win, args.steps, args.warmup)
+                runs.append({"window": [left, 0], "dtype": dt, "ms": round(w_ev, 4), "ms_min": round(w_min, 4),
+                             "eff_TFLOPs": round(wflops / (w_ev * 1e-3) / 1e12, 2),
+                             "page_convention_TFLOPs": round(wflops / 2 / (w_ev * 1e-3) / 1e12, 2)})
+        out["window"] = {"kernel": "nsa_window_fwd / nsa_window_fwd_bf16", "runs": runs}
+        if not args.no_bf16:
+            del bq, bk, bv, Ob
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
