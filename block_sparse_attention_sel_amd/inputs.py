@@ -40,7 +40,7 @@ import numpy as np
 CHUNK = 1 << 22
 
 # Stream ids inside one seed.
-STREAM_Q, STREAM_K, STREAM_V, STREAM_IDX, STREAM_DO = 1, 2, 3, 4, 5
+STREAM_Q, STREAM_K, STREAM_V, STREAM_IDX, STREAM_DO, STREAM_SCORES = 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -268,6 +268,29 @@ def make_inputs_bf16(cfg: Config, threads: int | None = None):
     v = normal_bf16((cfg.B, cfg.N, cfg.G, cfg.D), cfg.seed, STREAM_V, threads)
     idx = block_indices(cfg, threads)
     return q, k, v, idx
+
+
+def block_scores(cfg: Config, threads: int | None = None) -> np.ndarray:
+    """Block importance scores for top-k selection, fp32 [B, M, G, NB], N(0, 1)
+    (the same chunked Philox scheme as the other tensors, stream 6)."""
+    shape = (cfg.B, cfg.M, cfg.G, cfg.NB)
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    nchunks = -(-n // CHUNK)
+
+    def fill(i):
+        lo = i * CHUNK
+        hi = min(n, lo + CHUNK)
+        key = np.array([cfg.seed, (STREAM_SCORES << 32) + i], dtype=np.uint64)
+        rng = np.random.Generator(np.random.Philox(key=key))
+        out[lo:hi] = rng.standard_normal(hi - lo, dtype=np.float32)
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(threads or _threads()) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
 
 
 def make_grad_output(cfg: Config, threads: int | None = None) -> np.ndarray:

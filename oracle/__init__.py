@@ -58,6 +58,8 @@ def _load():
         lib.nsa_oracle_window_units.argtypes = ([p, p, p] + [i64] * 8 + [p, i64, p, p, ctypes.c_int, ctypes.c_int])
         lib.nsa_oracle_bwd_units.restype = ctypes.c_int
         lib.nsa_oracle_bwd_units.argtypes = ([p] * 5 + [i64] * 8 + [p, i64, p, i64, p, p, p, p, p, p, ctypes.c_int])
+        lib.nsa_oracle_topk.restype = ctypes.c_int
+        lib.nsa_oracle_topk.argtypes = [p] + [i64] * 6 + [p]
         _lib = lib
     return _lib
 
@@ -240,3 +242,17 @@ def bwd_full(q, k, v, idx, do, block_size: int, threads: int = 0, mags: bool = F
     if mags:
         out += [r[3].reshape(B, M, H, D), r[4], r[5]]
     return tuple(out)
+
+
+def topk_blocks(scores: np.ndarray, block_size: int, T: int) -> np.ndarray:
+    """Top-k block selection: scores fp32 [B, M, G, NB] -> block_indices int32
+    [B, M, G, T].  Per row, the T highest-scoring blocks among t = 0 ..
+    min(m // block_size, NB - 1) (ties: smaller t first; NaN counts as -inf),
+    written in ascending order, padded with -1."""
+    if scores.dtype != np.float32 or scores.ndim != 4 or not scores.flags.c_contiguous:
+        raise ValueError("scores must be a C-contiguous 4-d float32 array")
+    B, M, G, NB = scores.shape
+    out = np.empty((B, M, G, T), dtype=np.int32)
+    if _load().nsa_oracle_topk(_ptr(scores), B, M, G, NB, block_size, T, _ptr(out)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out

@@ -572,3 +572,64 @@ int nsa_oracle_bwd_units(const uint16_t *Q, const uint16_t *K, const uint16_t *V
     free(th);
     return rc;
 }
+
+/*
+ * Top-k block selection: the step that produces block_indices (wave issue
+ * "[wave] NSA: selection attention forward kernel", section Depends on, names
+ * a top-k kernel; the pages give no algorithm for it).  Plain reading: for
+ * every row (b, m, g) of scores [B, M, G, NB] (one importance score per key
+ * block), the candidates are the blocks a query may select, t = 0 .. min(m/bs,
+ * NB - 1); the T candidates with the highest scores are chosen, ordered by
+ * score descending and, among equal scores, by block index ascending (a NaN
+ * score counts as -inf; -0 equals +0).  The row is written in ascending block
+ * order and padded with -1 (fewer than T candidates: all of them).
+ */
+typedef struct {
+    double key;
+    int64_t t;
+} cand_t;
+
+static int cand_cmp(const void *a, const void *b) {
+    const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+    if (x->key > y->key) return -1;
+    if (x->key < y->key) return 1;
+    return (x->t > y->t) - (x->t < y->t);
+}
+
+static int i64_cmp(const void *a, const void *b) {
+    const int64_t x = *(const int64_t *)a, y = *(const int64_t *)b;
+    return (x > y) - (x < y);
+}
+
+int nsa_oracle_topk(const float *scores, int64_t B, int64_t M, int64_t G, int64_t NB, int64_t block_size,
+                    int64_t T, int32_t *out) {
+    if (!scores || !out || B < 1 || M < 1 || G < 1 || NB < 1 || block_size < 1 || T < 1) return -1;
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)NB);
+    int64_t *sel = (int64_t *)malloc(sizeof(int64_t) * (size_t)NB);
+    if (!c || !sel) {
+        free(c);
+        free(sel);
+        return -1;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t m = 0; m < M; ++m)
+            for (int64_t g = 0; g < G; ++g) {
+                const float *row = scores + ((b * M + m) * G + g) * NB;
+                const int64_t last = (m / block_size < NB - 1) ? m / block_size : NB - 1;
+                const int64_t nc = last + 1;
+                for (int64_t t = 0; t < nc; ++t) {
+                    const double v = (double)row[t];
+                    c[t].key = isnan(v) ? -INFINITY : v;   /* -0.0 == +0.0 under > and < */
+                    c[t].t = t;
+                }
+                qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
+                const int64_t k = nc < T ? nc : T;
+                for (int64_t i = 0; i < k; ++i) sel[i] = c[i].t;
+                qsort(sel, (size_t)k, sizeof(int64_t), i64_cmp);
+                int32_t *o = out + ((b * M + m) * G + g) * T;
+                for (int64_t i = 0; i < T; ++i) o[i] = i < k ? (int32_t)sel[i] : -1;
+            }
+    free(c);
+    free(sel);
+    return 0;
+}
