@@ -2,10 +2,10 @@
 
 ``nsa_sel_fwd``, ``nsa_sel_fwd_bf16``, ``nsa_sel_bwd``,
 ``nsa_sel_bwd_workspace_size``, ``nsa_dense_fwd``, ``nsa_window_fwd``,
-``nsa_window_fwd_bf16`` and ``nsa_sel_status_string`` mirror the C entry points
-one to one (pointers may be given as ints or as torch tensors);
-``sel_attn_fwd``, ``sel_attn_bwd``, ``dense_attn_fwd`` and ``window_attn_fwd``
-are conveniences that check torch tensors, allocate the outputs and call the
+``nsa_window_fwd_bf16``, ``nsa_topk_blocks`` and ``nsa_sel_status_string``
+mirror the C entry points one to one (pointers may be given as ints or as torch tensors);
+``sel_attn_fwd``, ``sel_attn_bwd``, ``dense_attn_fwd``, ``window_attn_fwd`` and
+``topk_blocks`` are conveniences that check torch tensors, allocate the outputs and call the
 entry point on the current stream (the fp16 or bf16 one by the tensors' dtype).  ``nsa_gather_probe`` mirrors the
 measurement probe of include/nsa_gather_probe.h.  All arithmetic happens in the
 HIP kernels; when a library is missing every call into it raises.
@@ -34,6 +34,7 @@ NSA_SEL_ERR_WORKSPACE = 8
 EXPORTED = ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_status_string")
 DENSE_EXPORTED = ("nsa_dense_fwd", "nsa_window_fwd", "nsa_window_fwd_bf16")
 BWD_EXPORTED = ("nsa_sel_bwd", "nsa_sel_bwd_workspace_size")
+TOPK_EXPORTED = ("nsa_topk_blocks",)
 PROBE_EXPORTED = ("nsa_gather_probe",)
 
 _lib = None
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nsa_sel_bwd_workspace_size.restype = ci
     lib.nsa_sel_bwd.argtypes = [vp] * 11 + [ctypes.c_size_t] + [ci] * 8 + [vp]
     lib.nsa_sel_bwd.restype = ci
+    lib.nsa_topk_blocks.argtypes = [vp, vp] + [ci] * 6 + [vp]
+    lib.nsa_topk_blocks.restype = ci
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -296,6 +299,38 @@ def window_attn_fwd(q, k, v, left: int, right: int, out=None, lse=None, stream=N
     else:
         nsa_window_fwd(q, k, v, out, lse, B, M, N, H, G, D, left, right, stream)
     return out, lse
+
+
+def nsa_topk_blocks_raw(scores, block_indices, B, M, G, NB, block_size, T, stream=0) -> int:
+    """Calls the C entry point and returns its status code unchanged."""
+    lib = load_library()
+    return lib.nsa_topk_blocks(_addr(scores), _addr(block_indices), int(B), int(M), int(G), int(NB),
+                               int(block_size), int(T), ctypes.c_void_p(_addr(stream)))
+
+
+def nsa_topk_blocks(scores, block_indices, B, M, G, NB, block_size, T, stream=0) -> None:
+    rc = nsa_topk_blocks_raw(scores, block_indices, B, M, G, NB, block_size, T, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def topk_blocks(scores, block_size: int, T: int, out=None, stream=None):
+    """scores [B, M, G, NB] fp32 contiguous CUDA tensor -> block_indices
+    [B, M, G, T] int32: per row the T highest-scoring causal blocks, ascending,
+    padded with -1 (include/nsa_topk.h)."""
+    import torch
+
+    if not isinstance(scores, torch.Tensor) or scores.dtype != torch.float32 or scores.dim() != 4:
+        raise TypeError("scores must be a 4-d float32 tensor")
+    if not scores.is_cuda or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous GPU tensor")
+    B, M, G, NB = scores.shape
+    if out is None:
+        out = torch.empty((B, M, G, T), dtype=torch.int32, device=scores.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(scores.device).cuda_stream
+    nsa_topk_blocks(scores, out, B, M, G, NB, block_size, T, stream)
+    return out
 
 
 def load_probe_library(path: str = PROBE_LIB_PATH) -> ctypes.CDLL:

@@ -1,8 +1,9 @@
 """Builds the HIP libraries (gfx950) in-tree with hipcc:
 
 - libnsa_sel.so: the selection-attention forward (include/nsa_sel.h), its
-  backward (include/nsa_sel_bwd.h) and the dense causal attention forward it
-  is compared with (include/nsa_dense.h);
+  backward (include/nsa_sel_bwd.h), the top-k block selection that produces
+  its index rows (include/nsa_topk.h) and the dense / sliding-window attention
+  forward it is compared with (include/nsa_dense.h);
 - libnsa_gather_probe.so: the gather-ceiling probe (include/nsa_gather_probe.h),
   a measurement aid that replays the forward kernel's block gathers.
 """
@@ -18,6 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 SRC = os.path.join(CSRC, "nsa_sel.hip")
 DENSE_SRC = os.path.join(CSRC, "nsa_dense.hip")
 BWD_SRC = os.path.join(CSRC, "nsa_sel_bwd.hip")
+TOPK_SRC = os.path.join(CSRC, "nsa_topk.hip")
 LIB = os.path.join(PKG, "libnsa_sel.so")
 PROBE_SRC = os.path.join(CSRC, "gather_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libnsa_gather_probe.so")
@@ -37,7 +39,7 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(extra_flags=(), out: str = LIB, srcs=(SRC, DENSE_SRC, BWD_SRC)) -> str:
+def build(extra_flags=(), out: str = LIB, srcs=(SRC, DENSE_SRC, BWD_SRC, TOPK_SRC)) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = out + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]

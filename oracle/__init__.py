@@ -60,6 +60,8 @@ def _load():
         lib.nsa_oracle_bwd_units.argtypes = ([p] * 5 + [i64] * 8 + [p, i64, p, i64, p, p, p, p, p, p, ctypes.c_int])
         lib.nsa_oracle_topk.restype = ctypes.c_int
         lib.nsa_oracle_topk.argtypes = [p] + [i64] * 6 + [p]
+        lib.nsa_oracle_topk_rows.restype = ctypes.c_int
+        lib.nsa_oracle_topk_rows.argtypes = [p, p] + [i64] * 4 + [p]
         _lib = lib
     return _lib
 
@@ -254,5 +256,17 @@ def topk_blocks(scores: np.ndarray, block_size: int, T: int) -> np.ndarray:
     B, M, G, NB = scores.shape
     out = np.empty((B, M, G, T), dtype=np.int32)
     if _load().nsa_oracle_topk(_ptr(scores), B, M, G, NB, block_size, T, _ptr(out)) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def topk_rows(scores_rows: np.ndarray, ms: np.ndarray, block_size: int, T: int) -> np.ndarray:
+    """topk_blocks for explicit rows: scores fp32 [R, NB] of queries at
+    positions ms [R] -> int32 [R, T]."""
+    scores_rows = np.ascontiguousarray(scores_rows, dtype=np.float32)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    R, NB = scores_rows.shape
+    out = np.empty((R, T), dtype=np.int32)
+    if _load().nsa_oracle_topk_rows(_ptr(scores_rows), _ptr(ms), R, NB, block_size, T, _ptr(out)) != 0:
         raise ValueError("oracle rejected its arguments")
     return out

@@ -601,6 +601,20 @@ static int i64_cmp(const void *a, const void *b) {
     return (x > y) - (x < y);
 }
 
+/* One row: the T best of candidates 0 .. nc-1 into o[0 .. T-1]. */
+static void select_row(const float *row, int64_t nc, int64_t T, cand_t *c, int64_t *sel, int32_t *o) {
+    for (int64_t t = 0; t < nc; ++t) {
+        const double v = (double)row[t];
+        c[t].key = isnan(v) ? -INFINITY : v;   /* -0.0 == +0.0 under > and < */
+        c[t].t = t;
+    }
+    qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
+    const int64_t k = nc < T ? nc : T;
+    for (int64_t i = 0; i < k; ++i) sel[i] = c[i].t;
+    qsort(sel, (size_t)k, sizeof(int64_t), i64_cmp);
+    for (int64_t i = 0; i < T; ++i) o[i] = i < k ? (int32_t)sel[i] : -1;
+}
+
 int nsa_oracle_topk(const float *scores, int64_t B, int64_t M, int64_t G, int64_t NB, int64_t block_size,
                     int64_t T, int32_t *out) {
     if (!scores || !out || B < 1 || M < 1 || G < 1 || NB < 1 || block_size < 1 || T < 1) return -1;
@@ -614,21 +628,36 @@ int nsa_oracle_topk(const float *scores, int64_t B, int64_t M, int64_t G, int64_
     for (int64_t b = 0; b < B; ++b)
         for (int64_t m = 0; m < M; ++m)
             for (int64_t g = 0; g < G; ++g) {
-                const float *row = scores + ((b * M + m) * G + g) * NB;
                 const int64_t last = (m / block_size < NB - 1) ? m / block_size : NB - 1;
-                const int64_t nc = last + 1;
-                for (int64_t t = 0; t < nc; ++t) {
-                    const double v = (double)row[t];
-                    c[t].key = isnan(v) ? -INFINITY : v;   /* -0.0 == +0.0 under > and < */
-                    c[t].t = t;
-                }
-                qsort(c, (size_t)nc, sizeof(cand_t), cand_cmp);
-                const int64_t k = nc < T ? nc : T;
-                for (int64_t i = 0; i < k; ++i) sel[i] = c[i].t;
-                qsort(sel, (size_t)k, sizeof(int64_t), i64_cmp);
-                int32_t *o = out + ((b * M + m) * G + g) * T;
-                for (int64_t i = 0; i < T; ++i) o[i] = i < k ? (int32_t)sel[i] : -1;
+                select_row(scores + ((b * M + m) * G + g) * NB, last + 1, T, c, sel,
+                           out + ((b * M + m) * G + g) * T);
             }
+    free(c);
+    free(sel);
+    return 0;
+}
+
+/* The same selection for R explicit rows: scores [R, NB], query positions
+   ms [R], output [R, T]. */
+int nsa_oracle_topk_rows(const float *scores, const int64_t *ms, int64_t R, int64_t NB, int64_t block_size,
+                         int64_t T, int32_t *out) {
+    if (!scores || !ms || !out || R < 0 || NB < 1 || block_size < 1 || T < 1) return -1;
+    cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)NB);
+    int64_t *sel = (int64_t *)malloc(sizeof(int64_t) * (size_t)NB);
+    if (!c || !sel) {
+        free(c);
+        free(sel);
+        return -1;
+    }
+    for (int64_t r = 0; r < R; ++r) {
+        if (ms[r] < 0) {
+            free(c);
+            free(sel);
+            return -1;
+        }
+        const int64_t last = (ms[r] / block_size < NB - 1) ? ms[r] / block_size : NB - 1;
+        select_row(scores + r * NB, last + 1, T, c, sel, out + r * T);
+    }
     free(c);
     free(sel);
     return 0;

@@ -286,3 +286,37 @@ def test_bwd_null_pointer(lib, which):
 ])
 def test_bwd_rejects_bad_arguments(lib, over, code):
     assert _bwd_call(**over) == code
+
+
+# --- top-k selection (include/nsa_topk.h) ---------------------------------------
+
+TOPK_HEADER = os.path.join(ROOT, "include", "nsa_topk.h")
+
+
+def test_topk_header_declares_the_binding_names():
+    text = re.sub(r"/\*.*?\*/", "", open(TOPK_HEADER).read(), flags=re.S)
+    assert sorted(set(re.findall(r"\b(nsa_\w+)\s*\(", text))) == sorted(binding.TOPK_EXPORTED)
+
+
+def test_topk_symbol_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in binding.TOPK_EXPORTED:
+        assert name in exported
+
+
+def _topk_call(S=1 << 36, I=2 << 36, B=1, M=256, G=2, NB=4, bs=64, T=4):
+    return binding.nsa_topk_blocks_raw(S, I, B, M, G, NB, bs, T, 0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(S=0), binding.NSA_SEL_ERR_NULL), (dict(I=0), binding.NSA_SEL_ERR_NULL),
+    (dict(M=0), binding.NSA_SEL_ERR_SHAPE), (dict(T=0), binding.NSA_SEL_ERR_SHAPE),
+    (dict(bs=0), binding.NSA_SEL_ERR_SHAPE), (dict(NB=0), binding.NSA_SEL_ERR_SHAPE),
+    (dict(NB=4097), binding.NSA_SEL_ERR_UNSUPPORTED), (dict(S=(1 << 36) + 2), binding.NSA_SEL_ERR_ALIGN),
+    (dict(I=(2 << 36) + 1), binding.NSA_SEL_ERR_ALIGN), (dict(B=1 << 12, M=1 << 20), binding.NSA_SEL_ERR_RANGE),
+    (dict(I=(1 << 36) + 64), binding.NSA_SEL_ERR_ALIAS),
+])
+def test_topk_rejects_bad_arguments(lib, over, code):
+    assert _topk_call(**over) == code

@@ -14,7 +14,7 @@ import pytest
 from block_sparse_attention_sel_amd import build as hip_build
 
 SOURCES = {"forward": hip_build.SRC, "probe": hip_build.PROBE_SRC, "dense": hip_build.DENSE_SRC,
-           "backward": hip_build.BWD_SRC}
+           "backward": hip_build.BWD_SRC, "topk": hip_build.TOPK_SRC}
 
 
 def _device_asm(src: str) -> str:

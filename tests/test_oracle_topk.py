@@ -97,3 +97,13 @@ def test_rejects_bad_arguments(oracle_mod):
         oracle_mod.topk_blocks(np.zeros((1, 4, 1, 2), np.float64), 2, 1)
     with pytest.raises(ValueError):
         oracle_mod.topk_blocks(np.zeros((1, 4, 1, 2), np.float32), 2, 0)
+
+
+def test_rows_entry_is_the_same_selection(oracle_mod):
+    rng = np.random.default_rng(8)
+    B, M, G, NB, bs, T = 1, 90, 2, 12, 8, 4
+    scores = _special_scores(rng, (B, M, G, NB))
+    full = oracle_mod.topk_blocks(scores, bs, T)
+    ms = np.repeat(np.arange(M), G)
+    rows = oracle_mod.topk_rows(scores.reshape(-1, NB), ms, bs, T)
+    assert np.array_equal(rows.reshape(B, M, G, T), full)
