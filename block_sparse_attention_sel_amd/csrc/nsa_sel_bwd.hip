@@ -8,9 +8,10 @@
 //
 // The work splits by who owns each gradient:
 //  * dQ is a sum over the selected keys of one query, so it is computed
-//    query-major, exactly on the forward's slot layout: a wavefront carries
-//    a slot of consecutive queries of one (b, g), merges their index rows and
-//    stages each selected 32-key sub-block once.  Per sub-block it forms
+//    query-major, exactly on the forward's slot layout and plan (one or two
+//    16-column tiles per wavefront): a wavefront carries a slot of
+//    consecutive queries of one (b, g), merges their index rows and stages
+//    each selected 32-key sub-block once.  Per sub-block it forms
 //    S^T = K Q^T and dP^T = V dO^T (v_mfma_f32_16x16x32_f16, keys on the MFMA
 //    rows), P^T = exp2(S^T log2(e)/sqrt(D) - LSE log2(e)), dS^T = P^T (dP^T -
 //    Delta), and accumulates dQ^T += K^T dS^T with K^T from the transposing
@@ -50,27 +51,35 @@ struct DqArgs {
 };
 
 // One 32-key sub-block of the dQ pass for one 16-column tile (lane l holds
-// column l%16, keys key0 + 16*kt + 4*(l/16) + i).
+// column l%16, keys key0 + 16*kt + 4*(l/16) + i), in two steps so that the K
+// row fragments are dead before the V fragments are read: dq_scores forms
+// S^T = K Q^T; dq_grad forms dP^T = V dO^T, P^T, dS^T and dQ^T += K^T dS^T.
 //   causal: some key may lie past the column's last visible key lim
 //   col_on: the column's query selected the block (else P = 0)
 template <int SBS, int D>
-__device__ __forceinline__ void dq_block(const half8 (&kf)[SBS / 16][D / 32], const half8 (&vf)[SBS / 16][D / 32],
-                                         const half4 (&kt)[SBS / 32][D / 32][2][2], const half8 (&qf)[D / 32],
-                                         const half8 (&df)[D / 32], int key0, bool causal, bool col_on, int lim,
-                                         float scale_log2, float lse2, float delta, float4v (&acc)[D / 32][2],
-                                         int q4) {
+__device__ __forceinline__ void dq_scores(const half8 (&kf)[SBS / 16][D / 32], const half8 (&qf)[D / 32],
+                                          float4v (&s)[SBS / 16]) {
+#pragma unroll
+    for (int k = 0; k < SBS / 16; ++k) {
+        s[k] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) s[k] = mfma_16x16x32(kf[k][c], qf[c], s[k]);
+    }
+}
+
+template <int SBS, int D>
+__device__ __forceinline__ void dq_grad(const half8 (&vf)[SBS / 16][D / 32], const half4 (&kt)[SBS / 32][D / 32][2][2],
+                                        const half8 (&df)[D / 32], const float4v (&s)[SBS / 16], int key0,
+                                        bool causal, bool col_on, int lim, float scale_log2, float lse2, float delta,
+                                        float4v (&acc)[D / 32][2], int q4) {
     constexpr int KT = SBS / 16;
     constexpr int DC = D / 32;
-    float4v s[KT], dp[KT];
+    float4v dp[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
-        s[k] = float4v{0.f, 0.f, 0.f, 0.f};
         dp[k] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            s[k] = mfma_16x16x32(kf[k][c], qf[c], s[k]);
-            dp[k] = mfma_16x16x32(vf[k][c], df[c], dp[k]);
-        }
+        for (int c = 0; c < DC; ++c) dp[k] = mfma_16x16x32(vf[k][c], df[c], dp[k]);
     }
     // A column that did not select the block gets P = exp2(-inf) = 0.
     const float m_exp = (col_on && lse2 != -INFINITY) ? lse2 : INFINITY;
@@ -190,6 +199,10 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
         Stage<SBS, D>::read(kf, kbuf, r, q4);
         Stage<SBS, D>::read_vt(kt, kbuf, lane);
         if (has1) st.issue(st.rk, kbuf, s1, lane);
+        float4v sc[NT][KT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            if ((a0 >> (nt * PACK)) & tile_bits) dq_scores<SBS, D>(kf, qf[nt], sc[nt]);
         if (has1)
             __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(s0) landed
         else
@@ -204,8 +217,8 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
             const int first_m = m0 + nt * PACK;
             const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
             const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
-            dq_block<SBS, D>(kf, vf, kt, qf[nt], df[nt], key0, causal, col_on, min(my_m[nt], p.N - 1),
-                             p.scale_log2, lse2[nt], delta[nt], acc[nt], q4);
+            dq_grad<SBS, D>(vf, kt, df[nt], sc[nt], key0, causal, col_on, min(my_m[nt], p.N - 1), p.scale_log2,
+                            lse2[nt], delta[nt], acc[nt], q4);
         }
         s0 = s1;
         a0 = a1;
@@ -225,8 +238,13 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
     }
 }
 
+// Two wavefronts per SIMD even with two tiles per wavefront: the compiler then
+// spills about 23 VGPRs of the two-tile kernel (D = 128), which measured 10%
+// faster over the whole backward than one tile per wavefront (189 VGPRs) and
+// than two tiles at one wavefront per SIMD (274 VGPRs).
 template <int BS, int SPLIT, int D, int PACK, int MODE>
-__global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_bwd_dq_kernel(Params p, DqArgs x) {
+__global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void nsa_sel_bwd_dq_kernel(Params p, DqArgs x) {
     constexpr int SBS = BS / SPLIT;
     constexpr int WAVES = waves_per_wg(SBS);
     const int lane = threadIdx.x & (kWaveSize - 1);
@@ -250,12 +268,14 @@ struct DqKernel {
     }
 };
 
-// The dQ pass runs one tile per wavefront (mode 0 or 1).
 template <int BS, int D, int PACK>
 hipError_t dq_launch_mode(const DqKernel &f, const Params &p, int cus, hipStream_t stream) {
     constexpr int SPLIT = BS / 32;
-    return p.mode == 1 ? launch_generations<DqKernel, BS, SPLIT, D, PACK, 1>(f, p, cus, stream)
-                       : launch_generations<DqKernel, BS, SPLIT, D, PACK, 0>(f, p, cus, stream);
+    switch (p.mode) {
+        case 2: return launch_generations<DqKernel, BS, SPLIT, D, PACK, 2>(f, p, cus, stream);
+        case 1: return launch_generations<DqKernel, BS, SPLIT, D, PACK, 1>(f, p, cus, stream);
+        default: return launch_generations<DqKernel, BS, SPLIT, D, PACK, 0>(f, p, cus, stream);
+    }
 }
 
 template <int BS, int D>
@@ -271,7 +291,7 @@ hipError_t dq_launch_pack(const DqKernel &f, const Params &p, int cus, hipStream
 constexpr int kBitQ = 256;     // queries per bitmap workgroup (8 words)
 constexpr int kBitWin = 512;   // key-block rows per LDS window of the bitmap pass
 constexpr int kRows = 32;      // (query, head) rows per tile of the dK/dV pass
-constexpr int kRing = 3;       // LDS ring depth of the dK/dV pass
+constexpr int kRing = 4;       // LDS ring depth of the dK/dV pass (two workgroups still fit a CU)
 constexpr int kMaxQc = 2048;   // most queries per item
 
 struct Bw {
@@ -424,6 +444,65 @@ __device__ __forceinline__ int lds_read_int(unsigned a) {
     return v;
 }
 
+// The dK/dV pass's LDS reads of one tile at D = 128, as two batches with one
+// wait each: (1) the Q and dO row fragments (MFMA A operands, the layout of
+// Stage::read) and the 8 rows' statistics of this lane, (2) the transposed
+// dO^T and Q^T fragments (the layout of Stage::read_vt).  aq/ad are the
+// lane's addresses of head-dim chunk c in the Q and dO tiles (row part
+// included), ast the lane's statistics address; tq/td the transposing-read
+// addresses.
+__device__ __forceinline__ void tile_rows128(half8 (&qa)[2][4], half8 (&da)[2][4], float4v (&sa)[2][2],
+                                             const unsigned (&aq)[4], const unsigned (&ad)[4], unsigned ast) {
+    asm volatile(
+        "ds_read_b128 %0, %20 offset:0\n" "ds_read_b128 %1, %21 offset:0\n" "ds_read_b128 %2, %22 offset:0\n"
+        "ds_read_b128 %3, %23 offset:0\n" "ds_read_b128 %4, %20 offset:4096\n" "ds_read_b128 %5, %21 offset:4096\n"
+        "ds_read_b128 %6, %22 offset:4096\n" "ds_read_b128 %7, %23 offset:4096\n" "ds_read_b128 %8, %24 offset:0\n"
+        "ds_read_b128 %9, %25 offset:0\n" "ds_read_b128 %10, %26 offset:0\n" "ds_read_b128 %11, %27 offset:0\n"
+        "ds_read_b128 %12, %24 offset:4096\n" "ds_read_b128 %13, %25 offset:4096\n"
+        "ds_read_b128 %14, %26 offset:4096\n" "ds_read_b128 %15, %27 offset:4096\n"
+        "ds_read_b128 %16, %28 offset:0\n" "ds_read_b128 %17, %28 offset:16\n" "ds_read_b128 %18, %28 offset:128\n"
+        "ds_read_b128 %19, %28 offset:144\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(qa[0][0]), "=&v"(qa[0][1]), "=&v"(qa[0][2]), "=&v"(qa[0][3]), "=&v"(qa[1][0]), "=&v"(qa[1][1]),
+          "=&v"(qa[1][2]), "=&v"(qa[1][3]), "=&v"(da[0][0]), "=&v"(da[0][1]), "=&v"(da[0][2]), "=&v"(da[0][3]),
+          "=&v"(da[1][0]), "=&v"(da[1][1]), "=&v"(da[1][2]), "=&v"(da[1][3]), "=&v"(sa[0][0]), "=&v"(sa[0][1]),
+          "=&v"(sa[1][0]), "=&v"(sa[1][1])
+        : "v"(aq[0]), "v"(aq[1]), "v"(aq[2]), "v"(aq[3]), "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ast)
+        : "memory");
+}
+
+__device__ __forceinline__ void tile_tr128(half4 (&dt)[1][4][2][2], half4 (&qt)[1][4][2][2], const unsigned (&td)[4],
+                                           const unsigned (&tq)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %32 offset:0\n" "ds_read_b64_tr_b16 %1, %32 offset:4096\n"
+        "ds_read_b64_tr_b16 %2, %32 offset:8\n" "ds_read_b64_tr_b16 %3, %32 offset:4104\n"
+        "ds_read_b64_tr_b16 %4, %33 offset:0\n" "ds_read_b64_tr_b16 %5, %33 offset:4096\n"
+        "ds_read_b64_tr_b16 %6, %33 offset:8\n" "ds_read_b64_tr_b16 %7, %33 offset:4104\n"
+        "ds_read_b64_tr_b16 %8, %34 offset:0\n" "ds_read_b64_tr_b16 %9, %34 offset:4096\n"
+        "ds_read_b64_tr_b16 %10, %34 offset:8\n" "ds_read_b64_tr_b16 %11, %34 offset:4104\n"
+        "ds_read_b64_tr_b16 %12, %35 offset:0\n" "ds_read_b64_tr_b16 %13, %35 offset:4096\n"
+        "ds_read_b64_tr_b16 %14, %35 offset:8\n" "ds_read_b64_tr_b16 %15, %35 offset:4104\n"
+        "ds_read_b64_tr_b16 %16, %36 offset:0\n" "ds_read_b64_tr_b16 %17, %36 offset:4096\n"
+        "ds_read_b64_tr_b16 %18, %36 offset:8\n" "ds_read_b64_tr_b16 %19, %36 offset:4104\n"
+        "ds_read_b64_tr_b16 %20, %37 offset:0\n" "ds_read_b64_tr_b16 %21, %37 offset:4096\n"
+        "ds_read_b64_tr_b16 %22, %37 offset:8\n" "ds_read_b64_tr_b16 %23, %37 offset:4104\n"
+        "ds_read_b64_tr_b16 %24, %38 offset:0\n" "ds_read_b64_tr_b16 %25, %38 offset:4096\n"
+        "ds_read_b64_tr_b16 %26, %38 offset:8\n" "ds_read_b64_tr_b16 %27, %38 offset:4104\n"
+        "ds_read_b64_tr_b16 %28, %39 offset:0\n" "ds_read_b64_tr_b16 %29, %39 offset:4096\n"
+        "ds_read_b64_tr_b16 %30, %39 offset:8\n" "ds_read_b64_tr_b16 %31, %39 offset:4104\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(dt[0][0][0][0]), "=&v"(dt[0][0][0][1]), "=&v"(dt[0][0][1][0]), "=&v"(dt[0][0][1][1]),
+          "=&v"(dt[0][1][0][0]), "=&v"(dt[0][1][0][1]), "=&v"(dt[0][1][1][0]), "=&v"(dt[0][1][1][1]),
+          "=&v"(dt[0][2][0][0]), "=&v"(dt[0][2][0][1]), "=&v"(dt[0][2][1][0]), "=&v"(dt[0][2][1][1]),
+          "=&v"(dt[0][3][0][0]), "=&v"(dt[0][3][0][1]), "=&v"(dt[0][3][1][0]), "=&v"(dt[0][3][1][1]),
+          "=&v"(qt[0][0][0][0]), "=&v"(qt[0][0][0][1]), "=&v"(qt[0][0][1][0]), "=&v"(qt[0][0][1][1]),
+          "=&v"(qt[0][1][0][0]), "=&v"(qt[0][1][0][1]), "=&v"(qt[0][1][1][0]), "=&v"(qt[0][1][1][1]),
+          "=&v"(qt[0][2][0][0]), "=&v"(qt[0][2][0][1]), "=&v"(qt[0][2][1][0]), "=&v"(qt[0][2][1][1]),
+          "=&v"(qt[0][3][0][0]), "=&v"(qt[0][3][0][1]), "=&v"(qt[0][3][1][0]), "=&v"(qt[0][3][1][1])
+        : "v"(td[0]), "v"(td[1]), "v"(td[2]), "v"(td[3]), "v"(tq[0]), "v"(tq[1]), "v"(tq[2]), "v"(tq[3])
+        : "memory");
+}
+
 template <int BS, int D>
 struct KvLds {
     _Float16 q[kRing][kRows * D];
@@ -439,7 +518,7 @@ template <int BS, int D>
 __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(Bw w) {
     constexpr int WAVES = BS / 16;
     constexpr int DC = D / 32;
-    using St = Stage<kRows, D>;
+    using St = Stage<kRows, D, 1>;
     constexpr int NI = St::NI;  // copy instructions per tile and tensor
     static_assert(NI % WAVES == 0, "copy instructions must split evenly");
     constexpr int CPW = NI / WAVES;     // per wavefront, per tensor
@@ -503,6 +582,17 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));  // fragments in registers before the copies start counting
 
+    // Rows whose query precedes the key block's last key need the causal
+    // mask; they are queries of the block itself (at most BS - 1), hence
+    // among the first 64 of the ascending list.  A tile needs the mask when
+    // it starts before them or the wavefront's keys reach past N.
+    int n_early;
+    {
+        const int mv = lane < nq ? lds_read_int(lds_addr(L.list) + 4u * (unsigned)lane) : INT_MAX;
+        n_early = __builtin_popcountll(__ballot(mv < t * BS + BS - 1));
+    }
+    const bool tail_keys = key0 + 16 > w.N;
+
     const int h0 = g * w.gs;
     const int qpt = w.qpt;
     const int ntiles = (nq + qpt - 1) / qpt;
@@ -528,25 +618,53 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
     };
     auto issue = [&](int i) {
         const int slot = i % kRing;
+        // The rows' queries: CPW copy rows and one statistics row per lane,
+        // read from the list with one LDS wait.
+        unsigned la[5];
+        int rrs[5], hs[5], ms[5];
+        bool vs[5];
+#pragma unroll
+        for (int kk = 0; kk < 5; ++kk) {
+            const int rr = kk < CPW ? (wave + kk * WAVES) * St::RPI + lane / St::LPR : lane >> 1;
+            const int sl = rr / w.gs;
+            const int qi = i * qpt + sl;
+            vs[kk] = kk <= CPW && sl < qpt && qi < nq;
+            la[kk] = list_a + 4u * (unsigned)(vs[kk] ? qi : 0);
+            hs[kk] = h0 + (vs[kk] ? rr - sl * w.gs : 0);
+            rrs[kk] = rr;
+        }
+        asm volatile("ds_read_b32 %0, %5\n\tds_read_b32 %1, %6\n\tds_read_b32 %2, %7\n\tds_read_b32 %3, %8\n\t"
+                     "ds_read_b32 %4, %9\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(ms[0]), "=&v"(ms[1]), "=&v"(ms[2]), "=&v"(ms[3]), "=&v"(ms[4])
+                     : "v"(la[0]), "v"(la[1]), "v"(la[2]), "v"(la[3]), "v"(la[4])
+                     : "memory");
 #pragma unroll
         for (int kk = 0; kk < CPW; ++kk) {
             const int j = wave + kk * WAVES;
-            const int rr = j * St::RPI + lane / St::LPR;
-            int m, h;
-            row_query(i, rr, m, h);
-            const unsigned off = (unsigned)(((size_t)m * w.H + h) * D * 2) +
-                                 (unsigned)(((lane % St::LPR) ^ St::swz(rr)) * 16);
+            const unsigned off = (unsigned)(((size_t)ms[kk] * w.H + hs[kk]) * D * 2) +
+                                 (unsigned)(((lane % St::LPR) ^ St::swz(rrs[kk])) * 16);
             St::copy(rq, (lds_half_t *)L.q[slot], off, 0u, j);
             St::copy(rd, (lds_half_t *)L.d[slot], off, 0u, j);
         }
         {
-            int m, h;
-            const bool valid = row_query(i, lane >> 1, m, h);
+            const int m = ms[CPW], h = hs[CPW];
+            const bool valid = vs[CPW];
             const unsigned e = valid ? (unsigned)(((size_t)b * w.H + h) * w.M + m) : (unsigned)w.sentinel;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)L.st[slot][wave],
                                                      4, e * 8u + (unsigned)(lane & 1) * 4u, 0, 0, 0);
         }
     };
+
+    // The lane's LDS byte offsets within a staged tile: row fragments (row r,
+    // head-dim chunk c) and transposing reads (row 4*(l/16) + (l/4)%4, piece
+    // 4*c + l%4), with the staging swizzle.
+    unsigned row_off[DC], tr_off[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+        row_off[c] = (unsigned)(r * D + ((c * 4 + q4) ^ St::swz(r)) * 8) * 2u;
+        const int trow = 4 * q4 + ((lane >> 2) & 3);
+        tr_off[c] = (unsigned)(trow * D * 2 + ((4 * c + (lane & 3)) ^ St::swz(trow)) * 16);
+    }
 
     float4v dk[DC][2], dv[DC][2];
 #pragma unroll
@@ -573,8 +691,30 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
         const int slot = i % kRing;
 
         half8 qa[2][DC], da[2][DC];
-        St::read(qa, L.q[slot], r, q4);
-        St::read(da, L.d[slot], r, q4);
+        float4v sa[2][2];  // (LSE log2 e, Delta) of rows 16*rt + 4*(l/16) + j
+        const unsigned st_a = lds_addr(L.st[slot][wave]) + (unsigned)(q4 * 4 * 8);
+        if constexpr (D == 128) {
+            const unsigned qb = lds_addr(L.q[slot]), db = lds_addr(L.d[slot]);
+            unsigned aq[4], ad[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                aq[c] = qb + row_off[c];
+                ad[c] = db + row_off[c];
+            }
+            tile_rows128(qa, da, sa, aq, ad, st_a);
+        } else {
+            St::read(qa, L.q[slot], r, q4);
+            St::read(da, L.d[slot], r, q4);
+            asm volatile(
+                "ds_read_b128 %0, %4 offset:0\n"
+                "ds_read_b128 %1, %4 offset:16\n"
+                "ds_read_b128 %2, %4 offset:128\n"
+                "ds_read_b128 %3, %4 offset:144\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(sa[0][0]), "=&v"(sa[0][1]), "=&v"(sa[1][0]), "=&v"(sa[1][1])
+                : "v"(st_a)
+                : "memory");
+        }
         // S = Q K^T and dP = dO V^T: lane l holds rows 16*rt + 4*(l/16) + j
         // of key my_key.
         float4v s[2], dp[2];
@@ -588,24 +728,7 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
                 dp[rt] = mfma_16x16x32(da[rt][c], vb[c], dp[rt]);
             }
         }
-        // Row statistics (LSE log2 e, Delta) of those 8 rows.
-        float4v sa[2][2];
-        {
-            const unsigned a = lds_addr(L.st[slot][wave]) + (unsigned)(q4 * 4 * 8);
-            asm volatile(
-                "ds_read_b128 %0, %4 offset:0\n"
-                "ds_read_b128 %1, %4 offset:16\n"
-                "ds_read_b128 %2, %4 offset:128\n"
-                "ds_read_b128 %3, %4 offset:144\n"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(sa[0][0]), "=&v"(sa[0][1]), "=&v"(sa[1][0]), "=&v"(sa[1][1])
-                : "v"(a)
-                : "memory");
-        }
-        // Keys past a row's query (or past N) occur only in tiles that start
-        // before the wavefront's last key.
-        const int m_first = __builtin_amdgcn_readfirstlane(lds_read_int(list_a + 4u * (unsigned)(i * qpt)));
-        const bool need_mask = m_first < key0 + 15 || key0 + 16 > w.N;
+        const bool need_mask = tail_keys || i * qpt < n_early;
         half4 pf[2], dsf[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -629,8 +752,19 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
         // dV^T += dO^T P and dK^T += Q^T dS (rows of the tile on the MFMA k
         // axis, in the order of the transposing reads).
         half4 qt[1][DC][2][2], dt[1][DC][2][2];
-        St::read_vt(dt, L.d[slot], lane);
-        St::read_vt(qt, L.q[slot], lane);
+        if constexpr (D == 128) {
+            const unsigned qb = lds_addr(L.q[slot]), db = lds_addr(L.d[slot]);
+            unsigned td[4], tq[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                td[c] = db + tr_off[c];
+                tq[c] = qb + tr_off[c];
+            }
+            tile_tr128(dt, qt, td, tq);
+        } else {
+            St::read_vt(dt, L.d[slot], lane);
+            St::read_vt(qt, L.q[slot], lane);
+        }
         const half8 bp = cat8(pf[0], pf[1]);
         const half8 bds = cat8(dsf[0], dsf[1]);
 #pragma unroll
@@ -813,7 +947,7 @@ extern "C" int nsa_sel_bwd(const void *Q, const void *K, const void *V, const in
     }
 
     const int cus = device_cus();
-    plan_slots(p, cus, 1);
+    plan_slots(p, cus);
     p.Q = (const _Float16 *)Q;
     p.K = (const _Float16 *)K;
     p.V = (const _Float16 *)V;

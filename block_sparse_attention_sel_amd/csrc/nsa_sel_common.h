@@ -666,8 +666,8 @@ __device__ __forceinline__ int wave_slot(const Params &p, int wave) {
 // through readfirstlane keeps the descriptors in scalar registers (without
 // it the compiler may place them in vector registers and wrap every copy in a
 // loop over distinct descriptor values).
-template <int SBS, int D>
-__device__ __forceinline__ void init_stage(Stage<SBS, D> &st, const Params &p, int b, int g, int lane) {
+template <int SBS, int D, int SWZ>
+__device__ __forceinline__ void init_stage(Stage<SBS, D, SWZ> &st, const Params &p, int b, int g, int lane) {
     b = __builtin_amdgcn_readfirstlane(b);
     g = __builtin_amdgcn_readfirstlane(g);
     const _Float16 *Kg = p.K + ((size_t)b * p.N * p.G + g) * D;
@@ -729,8 +729,7 @@ int check_sizes(int B, int M, int N, int H, int G, int D, int block_size, int T,
 // with streamed rows), and fewer while the grid would give a CU less than 8
 // wavefront slots.  Two tiles keep a wavefront within 256 registers, so two
 // wavefronts share each SIMD.
-// max_mode caps the tiles per wavefront (the backward's dQ pass holds more
-// registers per tile than the forward and runs one).
+// max_mode caps the tiles per wavefront.
 void plan_slots(Params &p, int cus, int max_mode = 2) {
     int mode = 0;
     for (int nt = max_mode; nt >= 1; nt /= 2) {

@@ -57,11 +57,18 @@ def _spills(text, key):
     return int(m.group(1))
 
 
+# Spills taken on purpose: the backward's dQ kernel with two tiles per
+# wavefront at D = 128 is held to two wavefronts per SIMD (256 VGPRs), which
+# spills a few registers and measured faster than every spill-free layout.
+ALLOWED_SPILLS = {r"nsa_sel_bwd_dq_kernelILi(32|64)ELi[12]ELi128ELi\d+ELi2E": 32}
+
+
 def test_no_vector_register_spills(kernels):
     _, meta = kernels
     assert meta
     for name, text in meta.items():
-        assert _spills(text, "vgpr_spill_count") == 0, name
+        limit = max([v for k, v in ALLOWED_SPILLS.items() if re.search(k, name)], default=0)
+        assert _spills(text, "vgpr_spill_count") <= limit, name
 
 
 def test_no_scalar_spills_on_the_register_merger_path(kernels):
