@@ -32,8 +32,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from block_sparse_attention_sel_amd.inputs import (CONFIGS, Config, block_indices, make_grad_output,  # noqa: E402
-                                                   make_inputs, make_inputs_bf16)
+from block_sparse_attention_sel_amd.inputs import (CONFIGS, Config, block_indices, block_scores,  # noqa: E402
+                                                   make_grad_output, make_inputs, make_inputs_bf16)
 
 HBM_PEAK_GBPS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
@@ -229,6 +229,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window kernel runs")
     ap.add_argument("--no-bf16", action="store_true", help="skip the bf16 selection forward")
+    ap.add_argument("--no-topk", action="store_true", help="skip the top-k block selection")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10, help="cold-cache timed calls (0 = skip)")
     ap.add_argument("--no-probe", action="store_true", help="skip the gather-ceiling probe")
@@ -453,6 +454,28 @@ def main():
         out["window"] = {"kernel": "nsa_window_fwd / nsa_window_fwd_bf16", "runs": runs}
         if not args.no_bf16:
             del bq, bk, bv, Ob
+
+    if not args.no_topk:
+        # Top-k block selection over N(0, 1) block scores [B, M, G, NB]; bytes
+        # are the causal candidates read (rows with more candidates than T)
+        # plus the index rows written.
+        from block_sparse_attention_sel_amd.binding import nsa_topk_blocks
+        print("[bench] top-k block selection", file=sys.stderr, flush=True)
+        tsc = torch.from_numpy(block_scores(cfg)).to(dev)
+        tout = torch.empty((cfg.B, cfg.M, cfg.G, cfg.T), dtype=torch.int32, device=dev)
+
+        def topk():
+            nsa_topk_blocks(tsc, tout, cfg.B, cfg.M, cfg.G, cfg.NB, cfg.block_size, cfg.T, stream.cuda_stream)
+
+        _, k_ev, k_min = time_launches(torch, topk, args.steps, args.warmup)
+        nc = np.minimum(np.arange(cfg.M, dtype=np.int64) // cfg.block_size, cfg.NB - 1) + 1
+        read = int(np.where(nc > cfg.T, nc, 0).sum()) * 4 * cfg.B * cfg.G
+        written = cfg.B * cfg.M * cfg.G * cfg.T * 4
+        out["topk"] = {"kernel": "nsa_topk_blocks", "ms": round(k_ev, 4), "ms_min": round(k_min, 4),
+                       "bytes": read + written,
+                       "GBps": round((read + written) / (k_ev * 1e-3) / 1e9, 1),
+                       "hbm_frac": round((read + written) / (k_ev * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del tsc, tout
 
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
