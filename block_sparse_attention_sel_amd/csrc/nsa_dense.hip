@@ -21,9 +21,11 @@
 // through a ring of kStages LDS buffers:
 //   * each wavefront copies its share of every sub-block (1/8 of the K and V
 //     copy instructions, 128-bit direct-to-LDS, coalesced rows);
-//   * per sub-block: wait for the own share, one LDS barrier (all shares in,
-//     the oldest buffer free), issue the copies kStages-1 sub-blocks ahead,
-//     then read K fragments, score the active tiles, read V^T, accumulate;
+//   * per group of 4 sub-blocks: wait for the own shares, one LDS barrier
+//     (all shares in, the other half of the ring free), issue the next
+//     group's copies; then per sub-block read K fragments, score the active
+//     tiles, read V^T, accumulate (fewer barriers let the two wavefronts of a
+//     SIMD drift out of phase, so one's softmax overlaps the other's MFMAs);
 //   * query tiles run longest first, and each XCD takes a contiguous range of
 //     (b, g, tile) units, so the workgroups resident on an XCD sweep the same
 //     group's keys.
@@ -34,7 +36,8 @@ namespace {
 
 constexpr int kDenseWaves = 8;   // wavefronts per workgroup (two per SIMD)
 constexpr int kDenseTiles = 2;   // 16-column tiles per wavefront
-constexpr int kStages = 4;       // LDS ring of 32-key sub-blocks
+constexpr int kStages = 8;       // LDS ring of 32-key sub-blocks (128 KiB at D = 128)
+constexpr int kGroup = 4;        // sub-blocks per LDS barrier: the ring holds two groups
 constexpr int kDenseSbs = 32;
 
 struct DenseParams {
@@ -149,21 +152,24 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
         }
     };
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
+    for (int s = 0; s < kGroup; ++s)
         if (s < nsub) issue(s);
 
     half8 kf[KT][DC];
     half4 vt[SBS / 32][DC][2][2];
     half4 pf[NT][KT];
     for (int s = 0; s < nsub; ++s) {
-        // Own share of sub-block s landed (later ones may still be in flight),
-        // then everyone's; the buffer of s-1 is free once all passed.
-        if (s + kStages - 2 < nsub)
-            __builtin_amdgcn_s_waitcnt(wait_vm(IPW * (kStages - 2)));
-        else
+        // Once per group of kGroup sub-blocks: this wavefront's copies of the
+        // group landed, then everyone's (one LDS barrier); the other half of
+        // the ring, read during the previous group, is refilled with the next
+        // group while this one is computed.
+        if (s % kGroup == 0) {
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
-        lds_barrier();
-        if (s + kStages - 1 < nsub) issue(s + kStages - 1);
+            lds_barrier();
+#pragma unroll
+            for (int k = 0; k < kGroup; ++k)
+                if (s + kGroup + k < nsub) issue(s + kGroup + k);
+        }
 
         const int slot = s % kStages;
         const int key0 = (s_begin + s) * SBS;
