@@ -53,6 +53,7 @@ SHAPES = [
     (1, 600, 1, 600, 1, 40),        # bs = 1, large T
     (1, 300, 1, 4096, 16, 3),       # the largest NB; most of the row is past the causal limit
     (1, 200, 2, 1, 64, 2),          # NB = 1
+    (1, 900, 1, 900, 1, 90),        # T > 64: more keys than one register at the threshold
 ]
 
 
@@ -60,9 +61,13 @@ SHAPES = [
 def test_topk_exact(torch_cuda, oracle_mod, shape):
     B, M, G, NB, bs, T = shape
     rng = np.random.default_rng(sum(shape))
-    for kind in ("normal", "special"):
-        scores = rng.standard_normal((B, M, G, NB)).astype(np.float32) if kind == "normal" else _special(
-            rng, (B, M, G, NB))
+    for kind in ("normal", "special", "binary"):
+        if kind == "normal":
+            scores = rng.standard_normal((B, M, G, NB)).astype(np.float32)
+        elif kind == "special":
+            scores = _special(rng, (B, M, G, NB))
+        else:  # two values: hundreds of keys tie at the T-th place
+            scores = rng.integers(0, 2, size=(B, M, G, NB)).astype(np.float32)
         got = _gpu_topk(torch_cuda, scores, bs, T)
         want = oracle_mod.topk_blocks(scores, bs, T)
         bad = np.argwhere((got != want).any(axis=3))
