@@ -23,9 +23,13 @@
 //     copy instructions, 128-bit direct-to-LDS, coalesced rows);
 //   * per group of 4 sub-blocks: wait for the own shares, one LDS barrier
 //     (all shares in, the other half of the ring free), issue the next
-//     group's copies; then per sub-block read K fragments, score the active
-//     tiles, read V^T, accumulate (fewer barriers let the two wavefronts of a
-//     SIMD drift out of phase, so one's softmax overlaps the other's MFMAs);
+//     group's copies (fewer barriers let the two wavefronts of a SIMD drift
+//     out of phase, so one's softmax overlaps the other's MFMAs);
+//   * runs of sub-blocks that no column masks are software-pipelined: the
+//     step for sub-block s issues the PV products of s and the QK products of
+//     s + 1 (both tiles) and then the softmax of s + 1, in one straight-line
+//     block, so the softmax of the first tile runs beside the second tile's
+//     QK products; sub-blocks at a window edge take a per-tile masked step;
 //   * query tiles run longest first, and each XCD takes a contiguous range of
 //     (b, g, tile) units, so the workgroups resident on an XCD sweep the same
 //     group's keys.
@@ -53,6 +57,74 @@ struct DenseParams {
     int left, right;  // window: keys m - left .. m + right visible (negative = unbounded)
     float scale_log2;
 };
+
+// S^T = K Q^T of one 16-column tile over a staged sub-block (no masking).
+template <int SBS, int D, bool BF16>
+__device__ __forceinline__ void qk_tile(const half8 (&kf)[SBS / 16][D / 32], const half8 (&qf)[D / 32],
+                                        float4v (&s)[SBS / 16]) {
+#pragma unroll
+    for (int kt = 0; kt < SBS / 16; ++kt) {
+        s[kt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) s[kt] = mfma16<BF16>(kf[kt][c], qf[c], s[kt]);
+    }
+}
+
+// The softmax step of score_block for a sub-block that no column masks and
+// every column takes: the same arithmetic, on scores computed beforehand, so
+// that one tile's softmax can be scheduled beside another tile's MFMAs.
+template <int KT, bool BF16>
+__device__ __forceinline__ void softmax_open(const float4v (&s)[KT], float scale_log2, float &m_run, float &l_run,
+                                             float &alpha, half4 (&pf)[KT]) {
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
+    mloc = col_max(mloc);
+    const float m_blk = mloc * scale_log2;
+    const float m_new = (m_blk > m_run + kLazyMax) ? m_blk : m_run;
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+        float4v pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            pv[i] = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -m_use));
+            psum += pv[i];
+        }
+        pf[kt] = pack4<BF16>(pv);
+    }
+    l_run = l_run * alpha + psum;
+}
+
+// accumulate_block split in two, so that the (rare) rescale branch can sit
+// outside the straight-line step: the rescale by alpha, then PV.
+template <int D>
+__device__ __forceinline__ void rescale_acc(float4v (&acc)[D / 32][2], float alpha) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {  // wave-uniform: some column rescales
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+            acc[c][0] *= alpha;
+            acc[c][1] *= alpha;
+        }
+    }
+}
+
+template <int SBS, int D, bool BF16>
+__device__ __forceinline__ void pv_tile(const half4 (&vt)[SBS / 32][D / 32][2][2], const half4 (&pf)[SBS / 16],
+                                        float4v (&acc)[D / 32][2]) {
+#pragma unroll
+    for (int kc = 0; kc < SBS / 32; ++kc) {
+        const half8 bp = cat8(pf[2 * kc], pf[2 * kc + 1]);
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                acc[c][hh] = mfma16<BF16>(cat8(vt[kc][c][hh][0], vt[kc][c][hh][1]), bp, acc[c][hh]);
+    }
+}
 
 template <int D, int PACK, bool BF16>
 __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(DenseParams p) {
@@ -158,43 +230,123 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
     half8 kf[KT][DC];
     half4 vt[SBS / 32][DC][2][2];
     half4 pf[NT][KT];
-    for (int s = 0; s < nsub; ++s) {
-        // Once per group of kGroup sub-blocks: this wavefront's copies of the
-        // group landed, then everyone's (one LDS barrier); the other half of
-        // the ring, read during the previous group, is refilled with the next
-        // group while this one is computed.
-        if (s % kGroup == 0) {
+    float4v sc[NT][KT];
+
+    // Group barriers are passed lazily, in order, before the first read of a
+    // sub-block of the group: this wavefront's copies of the group landed,
+    // then everyone's (one LDS barrier), and everyone is done with the other
+    // half of the ring, which is refilled with the next group.  Every
+    // wavefront reads every sub-block, so all pass the same barriers.
+    int bar_next = 0;
+    auto ensure = [&](int t) {
+        while (bar_next <= t / kGroup) {
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
             lds_barrier();
+            const int first = (bar_next + 1) * kGroup;
 #pragma unroll
             for (int k = 0; k < kGroup; ++k)
-                if (s + kGroup + k < nsub) issue(s + kGroup + k);
+                if (first + k < nsub) issue(first + k);
+            ++bar_next;
         }
-
-        const int slot = s % kStages;
+    };
+    // Per tile and sub-block (uniform over the tile): on = some key of the
+    // sub-block lies in the union [t_lo, t_hi] of its queries' windows;
+    // masked = some key lies outside some column's window (past the smallest
+    // upper or before the largest lower bound).
+    auto classify = [&](int s, bool (&on)[NT], bool (&masked)[NT]) {
         const int key0 = (s_begin + s) * SBS;
-        Stage<SBS, D, 1>::read(kf, kbuf[slot], r, q4);
-        bool on[NT];
+        bool open = true;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            // Uniform over the tile: the union of its queries' windows is
-            // [t_lo, t_hi]; some key of the sub-block lies outside a column's
-            // window when it passes the smallest upper or the largest lower
-            // bound.
             const int tile_last = min(mt[nt] + PACK, p.M) - 1;
             const int t_lo = p.left < 0 ? 0 : mt[nt] - p.left;
             const int t_hi = p.right < 0 ? p.N - 1 : min(p.N - 1, tile_last + p.right);
             on[nt] = mt[nt] < p.M && key0 <= t_hi && key0 + SBS - 1 >= t_lo;
-            if (!on[nt]) continue;
             const int min_hi = p.right < 0 ? p.N - 1 : min(p.N - 1, mt[nt] + p.right);
-            const bool masked = (key0 + SBS - 1 > min_hi) || (p.left >= 0 && key0 < tile_last - p.left);
-            score_block<SBS, D, BF16>(kf, qf[nt], key0, masked, true, live[nt], c_lo[nt], c_hi[nt], p.scale_log2,
-                                      m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
+            masked[nt] = (key0 + SBS - 1 > min_hi) || (p.left >= 0 && key0 < tile_last - p.left);
+            open = open && on[nt] && !masked[nt];
         }
-        Stage<SBS, D, 1>::read_vt(vt, vbuf[slot], lane);
+        return open;  // every tile takes the whole sub-block unmasked
+    };
+
+    int s = 0;
+    while (s < nsub) {
+        bool on[NT], masked[NT];
+        if (!classify(s, on, masked)) {
+            // A sub-block at a window edge: per tile, with masks.
+            ensure(s);
+            const int slot = s % kStages;
+            const int key0 = (s_begin + s) * SBS;
+            Stage<SBS, D, 1>::read(kf, kbuf[slot], r, q4);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                if (!on[nt]) continue;
+                score_block<SBS, D, BF16>(kf, qf[nt], key0, masked[nt], true, live[nt], c_lo[nt], c_hi[nt],
+                                          p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
+            }
+            Stage<SBS, D, 1>::read_vt(vt, vbuf[slot], lane);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                if (on[nt]) accumulate_block<SBS, D, BF16>(vt, pf[nt], alpha[nt], acc[nt]);
+            ++s;
+            continue;
+        }
+        // A run of open sub-blocks, software-pipelined: the step for s issues
+        // the QK products of s + 1 and the PV products of s beside the
+        // softmax of s + 1, in one straight-line block; the rescale of the
+        // accumulators (rare: the running max moves lazily) stays outside it.
+        // Padding columns (fewer than 16 heads x queries in a tile) score
+        // zero and carry finite values that are never stored; MFMA columns
+        // do not mix.
+        ensure(s);
+        Stage<SBS, D, 1>::read(kf, kbuf[s % kStages], r, q4);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) qk_tile<SBS, D, BF16>(kf, qf[nt], sc[nt]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-            if (on[nt]) accumulate_block<SBS, D, BF16>(vt, pf[nt], alpha[nt], acc[nt]);
+            softmax_open<KT, BF16>(sc[nt], p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt]);
+        for (;;) {
+            // V^T of s before the group barrier that may come with s + 1 (it
+            // frees the half of the ring that holds s).
+            Stage<SBS, D, 1>::read_vt(vt, vbuf[s % kStages], lane);
+            bool on1[NT], masked1[NT];
+            const bool next = s + 1 < nsub && classify(s + 1, on1, masked1);
+            if (next) ensure(s + 1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) rescale_acc<D>(acc[nt], alpha[nt]);
+            // Straight-line from here.  The K fragments of s + 1 are read once
+            // the PV products of s are issued (the V^T fragments are then
+            // dead, and the read's latency hides under the products).  Past
+            // the run's last sub-block the slot read may hold anything; the
+            // QK products and the softmax on it are dropped, which is cheaper
+            // than a branch that would split the block.
+            float m1[NT], l1[NT], a1[NT];
+            half4 pn[NT][KT];
+            // Raised wave priority while the products are issued: of the two
+            // wavefronts of a SIMD, the one issuing MFMAs goes first, the
+            // other's softmax fills the VALU (measured 2-3% faster; raising
+            // it for the softmax instead was slower).
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) pv_tile<SBS, D, BF16>(vt, pf[nt], acc[nt]);
+            Stage<SBS, D, 1>::read(kf, kbuf[(s + 1) % kStages], r, q4);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) qk_tile<SBS, D, BF16>(kf, qf[nt], sc[nt]);
+            __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                m1[nt] = m_run[nt];
+                l1[nt] = l_run[nt];
+                softmax_open<KT, BF16>(sc[nt], p.scale_log2, m1[nt], l1[nt], a1[nt], pn[nt]);
+                m_run[nt] = next ? m1[nt] : m_run[nt];
+                l_run[nt] = next ? l1[nt] : l_run[nt];
+                alpha[nt] = next ? a1[nt] : 1.f;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) pf[nt][kt] = pn[nt][kt];
+            }
+            ++s;
+            if (!next) break;
+        }
     }
 
     // Epilogue: total row sum over the 4 lanes of a column, normalise, store.
