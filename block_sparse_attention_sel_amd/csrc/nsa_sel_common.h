@@ -431,11 +431,15 @@ __device__ __forceinline__ unsigned wave_or(unsigned x) {
 // Holds all QW*T entries (QW*T <= 128) in two registers per lane: entry
 // e = lane + 64*v belongs to query e / T.  Each step takes the smallest
 // remaining counted block and retires every entry equal to it, so a block
-// repeated within a row, or shared by several rows, is returned once.
+// repeated within a row, or shared by several rows, is returned once.  An
+// entry holds (block << 4) | query (QW <= 8), so the wave-wide minimum is the
+// smallest block and the mask of the queries holding it comes from the
+// entries themselves: no per-lane query masks to keep live across the loop
+// (spilled, their reloads waited on every copy in flight).
 template <int QW, int BS>
 struct RegMerger {
+    static_assert(QW <= 16, "the query index takes 4 bits");
     int e[2];
-    unsigned bit[2];
 
     __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane) {
 #pragma unroll
@@ -446,17 +450,17 @@ struct RegMerger {
             const int m = m0 + (slot ? qi : 0);
             const int32_t *row = p.idx + ((size_t)(b * (size_t)p.M + m) * p.G + g) * p.T;
             const int t = slot ? __builtin_nontemporal_load(&row[ent - qi * p.T]) : -1;
-            const bool ok = t >= 0 && t <= m / BS && t < p.NB;
-            e[v] = ok ? t : INT_MAX;
-            bit[v] = slot ? 1u << qi : 0u;
+            const bool ok = t >= 0 && t <= m / BS && t < p.NB;  // NB < 2^27: (t << 4) fits
+            e[v] = ok ? (t << 4) | qi : INT_MAX;
         }
     }
     __device__ __forceinline__ int next(unsigned &active) {
-        const int t = wave_min(min(e[0], e[1]));
+        const int x = wave_min(min(e[0], e[1]));
         active = 0;
-        if (t == INT_MAX) return kDone;
-        const bool h0 = e[0] == t, h1 = e[1] == t;
-        active = wave_or((h0 ? bit[0] : 0u) | (h1 ? bit[1] : 0u));
+        if (x == INT_MAX) return kDone;
+        const int t = x >> 4;
+        const bool h0 = (e[0] >> 4) == t, h1 = (e[1] >> 4) == t;
+        active = wave_or((h0 ? 1u << (e[0] & 15) : 0u) | (h1 ? 1u << (e[1] & 15) : 0u));
         e[0] = h0 ? INT_MAX : e[0];
         e[1] = h1 ? INT_MAX : e[1];
         return t;
