@@ -203,18 +203,36 @@ def cpu_baseline(cfg: Config, q, k, v, idx, target_s: float = 15.0):
         vis = np.minimum(np.minimum((t + 1) * bs, cfg.N), m + 1) - t * bs
         return 4.0 * cfg.D * cfg.gs * float(np.where(ok, np.maximum(vis, 0), 0).sum())
 
-    probe = pick(max(threads * 4, 64))
-    t0 = time.perf_counter()
-    oracle.oracle_units(q, k, v, idx, cfg.block_size, probe, threads)
-    dt = time.perf_counter() - t0
-    n = int(min(200000, max(probe.shape[0], probe.shape[0] * target_s / max(dt, 1e-3))))
+    # Size the sample from a first timed pass (a few units per thread start
+    # slower than the steady rate, so a second, larger pass refines it).
+    n = max(threads * 4, 64)
+    for _ in range(2):
+        probe = pick(n)
+        t0 = time.perf_counter()
+        oracle.oracle_units(q, k, v, idx, cfg.block_size, probe, threads)
+        dt = time.perf_counter() - t0
+        n = int(min(1_000_000, max(probe.shape[0], probe.shape[0] * min(target_s, 1.0) / max(dt, 1e-3))))
+        if dt >= 0.5:
+            break
+    n = int(min(1_000_000, max(probe.shape[0], probe.shape[0] * target_s / max(dt, 1e-3))))
     units = pick(n)
     t0 = time.perf_counter()
     oracle.oracle_units(q, k, v, idx, cfg.block_size, units, threads)
     dt = time.perf_counter() - t0
     return {"value": unit_flops(units) / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"{n} random (b,m,g) units of the {cfg.name} workload, fp64, {dt:.1f} s",
             "ms_per_unit": dt * 1e3 / n}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
