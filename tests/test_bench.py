@@ -81,14 +81,14 @@ def test_full_size_counts_follow_the_closed_form(name):
     assert bench.work_counts(cfg, block_indices(cfg)) == _closed_form(cfg)
 
 
-# Totals of counted (unit, block) pairs per workload, as derived in the
-# survey's work table from the index rules alone.
-SURVEY_BLOCKS = {"tiny": 3904, "8k": 246784, "64k": 8327168, "32k-bs32": 8261632, "128k-local": 16715776}
+# Totals of counted (unit, block) pairs per workload, worked out by hand from
+# the index rules alone: the sum over units of min(T, m // bs + 1).
+HAND_BLOCKS = {"tiny": 3904, "8k": 246784, "64k": 8327168, "32k-bs32": 8261632, "128k-local": 16715776}
 
 
-@pytest.mark.parametrize("name", sorted(SURVEY_BLOCKS))
+@pytest.mark.parametrize("name", sorted(HAND_BLOCKS))
 def test_closed_form_totals(name):
-    assert _closed_form(CONFIGS[name])[0] == SURVEY_BLOCKS[name]
+    assert _closed_form(CONFIGS[name])[0] == HAND_BLOCKS[name]
 
 
 @pytest.mark.parametrize("qps", [1, 2, 4, 8])
