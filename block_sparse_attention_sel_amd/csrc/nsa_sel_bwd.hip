@@ -527,11 +527,12 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
 
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Items in launch order, so the XCDs (workgroup w runs on XCD w % 8)
+    // share a window of the (b, g)-major item list: one group's Q and dO rows
+    // at a time, instead of every group's at once.
     const int n_items = *w.n_items;
-    const int per_xcd = (n_items + kNumXcd - 1) / kNumXcd;
-    const int loc = blockIdx.x / kNumXcd;
-    const int item = (blockIdx.x % kNumXcd) * per_xcd + loc;
-    if (loc >= per_xcd || item >= n_items) return;  // the whole workgroup
+    const int item = blockIdx.x;
+    if (item >= n_items) return;  // the whole workgroup
     const int2 it = w.items[item];
     const int row = it.x, k = it.y;
     const int bg = row / w.NB, t = row - bg * w.NB;
