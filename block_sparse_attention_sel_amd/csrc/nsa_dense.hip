@@ -133,11 +133,11 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
     constexpr int SBS = kDenseSbs;
     constexpr int DC = D / 32;
     constexpr int KT = SBS / 16;
-    constexpr int NI = Stage<SBS, D, 1>::NI;              // copy instructions per K (or V) sub-block
+    constexpr int NI = Stage<SBS, D>::NI;              // copy instructions per K (or V) sub-block
     constexpr int IPW = (2 * NI) / kDenseWaves;        // of which each wavefront issues
     static_assert((2 * NI) % kDenseWaves == 0 && IPW >= 1, "copy instructions must split evenly");
-    __shared__ __attribute__((aligned(16))) _Float16 kbuf[kStages][Stage<SBS, D, 1>::HALVES];
-    __shared__ __attribute__((aligned(16))) _Float16 vbuf[kStages][Stage<SBS, D, 1>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf[kStages][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf[kStages][Stage<SBS, D>::HALVES];
 
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
     const int my_h = h0 + (r - q_in_tile * p.gs);
 
     // Staging descriptors before the per-lane loads (keeps them scalar).
-    Stage<SBS, D, 1> st;
+    Stage<SBS, D> st;
     {
         const int bb = __builtin_amdgcn_readfirstlane(b), gg = __builtin_amdgcn_readfirstlane(g);
         const size_t first = ((size_t)bb * p.N * p.G + gg) * D;
@@ -277,14 +277,14 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
             ensure(s);
             const int slot = s % kStages;
             const int key0 = (s_begin + s) * SBS;
-            Stage<SBS, D, 1>::read(kf, kbuf[slot], r, q4);
+            Stage<SBS, D>::read(kf, kbuf[slot], r, q4);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 if (!on[nt]) continue;
                 score_block<SBS, D, BF16>(kf, qf[nt], key0, masked[nt], true, live[nt], c_lo[nt], c_hi[nt],
                                           p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
             }
-            Stage<SBS, D, 1>::read_vt(vt, vbuf[slot], lane);
+            Stage<SBS, D>::read_vt(vt, vbuf[slot], lane);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 if (on[nt]) accumulate_block<SBS, D, BF16>(vt, pf[nt], alpha[nt], acc[nt]);
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
         // zero and carry finite values that are never stored; MFMA columns
         // do not mix.
         ensure(s);
-        Stage<SBS, D, 1>::read(kf, kbuf[s % kStages], r, q4);
+        Stage<SBS, D>::read(kf, kbuf[s % kStages], r, q4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) qk_tile<SBS, D, BF16>(kf, qf[nt], sc[nt]);
 #pragma unroll
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
         for (;;) {
             // V^T of s before the group barrier that may come with s + 1 (it
             // frees the half of the ring that holds s).
-            Stage<SBS, D, 1>::read_vt(vt, vbuf[s % kStages], lane);
+            Stage<SBS, D>::read_vt(vt, vbuf[s % kStages], lane);
             bool on1[NT], masked1[NT];
             const bool next = s + 1 < nsub && classify(s + 1, on1, masked1);
             if (next) ensure(s + 1);
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) pv_tile<SBS, D, BF16>(vt, pf[nt], acc[nt]);
-            Stage<SBS, D, 1>::read(kf, kbuf[(s + 1) % kStages], r, q4);
+            Stage<SBS, D>::read(kf, kbuf[(s + 1) % kStages], r, q4);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) qk_tile<SBS, D, BF16>(kf, qf[nt], sc[nt]);
             __builtin_amdgcn_s_setprio(0);

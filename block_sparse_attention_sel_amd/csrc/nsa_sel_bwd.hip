@@ -518,7 +518,7 @@ template <int BS, int D>
 __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(Bw w) {
     constexpr int WAVES = BS / 16;
     constexpr int DC = D / 32;
-    using St = Stage<kRows, D, 1>;
+    using St = Stage<kRows, D>;
     constexpr int NI = St::NI;  // copy instructions per tile and tensor
     static_assert(NI % WAVES == 0, "copy instructions must split evenly");
     constexpr int CPW = NI / WAVES;     // per wavefront, per tensor

@@ -273,18 +273,24 @@ struct LdsTrBatch<32, 64> {
 // instruction reads whole rows and coalesces into full cache lines.
 //
 // In LDS a row occupies D*2 contiguous bytes; its 16-byte pieces are stored
-// XOR-permuted, piece c at slot c ^ swz(row), so that the MFMA-layout reads
-// (16 lanes on 16 different rows, same piece) hit distinct banks.  SWZ = 1
-// (D = 128 only) also folds the row's low two bits into the slot's high
-// bits: the transposing V^T reads, whose 16-lane phases span rows 4j .. 4j+3,
-// then spread over 8 slots instead of 4.  It measured 4% faster for the dense
-// kernel's shared stream and 1-4% slower for the selection kernel's private
-// streams, so each kernel picks its own.
+// XOR-permuted, piece c at slot c ^ swz(row).  The permutation comes from the
+// LDS's service pattern, measured with single-instruction probes on gfx950:
+// 64 banks of 4 bytes; a ds_read_b128 is served in four passes of 16 lanes,
+// pass = (lane / 32, parity of bits 2..4 of the lane), and a ds_read_b64 (and
+// its transposing form) in two passes of 32 consecutive lanes; lanes of one
+// pass that touch the same bank in different rows serialise.  The two read
+// patterns are the MFMA-fragment reads (lane l: row l % 16, piece 4c + l / 16)
+// and the transposing V^T reads (lane l: row 4 (l / 16) + (l / 4) % 4, piece
+// 4c + l % 4, one 8-byte half of it).  swz makes the first conflict-free and
+// the second 2-way, which is the least possible: every lane of a transposing
+// read takes the same half of its piece, so it reaches only 32 of the banks.
+// (Measured per instruction: 4.2 and 4.1 cycles, against 4.2 / 8.1 for
+// slot = c ^ row and 8.1 / 4.1 for c ^ row ^ ((row & 3) << 2).)
 //
 // Addressing: the per-lane part of the byte offset repeats every 16/RPI
 // instructions (the swizzle depends on row % 16), so it lives in NV VGPRs;
 // the per-instruction row step and the block start are uniform (SGPR).
-template <int BS, int D, int SWZ = 0>
+template <int BS, int D>
 struct Stage {
     static constexpr int LPR = D / 8;                // lanes (16-byte pieces) per row
     static constexpr int RPI = kWaveSize / LPR;      // rows per 1 KiB instruction
@@ -292,9 +298,14 @@ struct Stage {
     static constexpr int NV = 16 / RPI;              // distinct per-lane offsets
     static constexpr int HALVES = BS * D;            // fp16 elements per K (or V) block
 
+    // A function of row % 16 (the per-lane copy offsets repeat with it).
+    // D = 128 (16 slots per row): row bits 0, 1 -> slot bits 2, 3 and row bit
+    // 2 -> slot bit 1.  D = 64 (8 slots; two rows share the 64 banks): row
+    // bits 1, 2, 3 -> slot bits 0, 2, 1.
     __device__ static __forceinline__ int swz(int row) {
-        if constexpr (SWZ == 1 && LPR == 16) return (row & 15) ^ ((row & 3) << 2);
-        return (row & 15) * LPR / 16;
+        static_assert(LPR == 16 || LPR == 8, "D must be 64 or 128");
+        if constexpr (LPR == 16) return ((row & 3) << 2) | ((row & 4) >> 1);
+        return ((row >> 1) & 1) | ((row >> 2) & 1) << 2 | ((row >> 3) & 1) << 1;
     }
 
     __amdgpu_buffer_rsrc_t rk, rv;  // K and V of this (b, g), byte-addressed
@@ -670,8 +681,8 @@ __device__ __forceinline__ int wave_slot(const Params &p, int wave) {
 // through readfirstlane keeps the descriptors in scalar registers (without
 // it the compiler may place them in vector registers and wrap every copy in a
 // loop over distinct descriptor values).
-template <int SBS, int D, int SWZ>
-__device__ __forceinline__ void init_stage(Stage<SBS, D, SWZ> &st, const Params &p, int b, int g, int lane) {
+template <int SBS, int D>
+__device__ __forceinline__ void init_stage(Stage<SBS, D> &st, const Params &p, int b, int g, int lane) {
     b = __builtin_amdgcn_readfirstlane(b);
     g = __builtin_amdgcn_readfirstlane(g);
     const _Float16 *Kg = p.K + ((size_t)b * p.N * p.G + g) * D;
