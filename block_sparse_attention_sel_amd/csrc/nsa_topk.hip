@@ -16,8 +16,9 @@
 //
 // A radix select finds the threshold bit by bit from the top: the count of
 // keys at or above a candidate prefix is one v_cmp per register with its
-// ballot popcounted on the scalar unit for even registers and on the VALU
-// for odd ones (no cross-lane arithmetic).  As soon as at most 64 keys lie at or above the accepted prefix
+// ballot popcounted on the scalar unit for three registers in four and on
+// the VALU for the fourth (no cross-lane arithmetic).  As soon as at most 64
+// keys lie at or above the accepted prefix
 // (for random scores, after the sign, the exponent and a mantissa bit or
 // two), they are compacted through LDS into one register in ascending block
 // order, and the remaining bits cost one compare each.  The search stops when
@@ -26,6 +27,12 @@
 // itself.  The row is written in ascending block order with ballots: every
 // key above the threshold, then keys equal to it in index order until T are
 // taken.
+//
+// Both the scalar unit (one per CU, shared by its four SIMDs) and the VALU
+// run close to an instruction per clock per CU here, so the per-row code
+// avoids work on either: row coordinates come from multiply-shift divisions
+// set up on the host, loads need no lane masks, keys come from branch-free
+// integer arithmetic, and the search loops keep single exits.
 #include "nsa_sel_common.h"
 #include "nsa_topk.h"
 
@@ -35,32 +42,52 @@ namespace {
 // two rows ahead beats none of them).
 constexpr int kRowsPerWave = 4;
 
+// In the counting passes, every kValuEvery-th register's compare mask is
+// popcounted on the VALU and the others on the scalar unit (measured: the
+// two units then carry about 0.8 and 0.7 instructions per clock per CU).
+constexpr int kValuEvery = 4;
+
 // Larger score -> larger key; NaN takes the key of -inf and -0 that of +0;
-// every score maps to a key >= 0x007FFFFF, leaving 0 free.
+// every score maps to a key >= kMinKey (the key of -inf), leaving 0 free.
+// Branch-free: -0 becomes +0 by adding +0 (in inline assembly, so that the
+// compiler cannot reason about NaN inputs; f32 denormals are kept, so the
+// sum is exact) and the usual sign flip orders the bit patterns.  The keys
+// of NaNs then lie above +inf's and below -inf's; shifting every key by
+// 0x007FFFFF wraps both ranges under -inf's, the maximum gathers them there,
+// and the shift is undone.  (Left shifted, the keys would straddle the
+// exponent boundaries and the bitwise search would need about three times
+// the passes on 2048-candidate rows.)  No compares, so no lane-mask hazards.
+constexpr unsigned kMinKey = 0x007FFFFFu;
+constexpr unsigned kNanShift = 0x007FFFFFu;
+
 __device__ __forceinline__ unsigned score_key(unsigned u) {
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) u = 0xFF800000u;  // NaN
-    if (u == 0x80000000u) u = 0u;                           // -0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    asm("v_add_f32 %0, 0, %1" : "=v"(u) : "v"(u));
+    const unsigned flip = (unsigned)((int)u >> 31) | 0x80000000u;
+    return max((u ^ flip) + kNanShift, kMinKey + kNanShift) - kNanShift;
 }
 
 __device__ __forceinline__ int ballot_count(bool p) { return __builtin_popcountll(__ballot(p)); }
 
-// Candidates of the row whose first candidate is src: 0 .. nc-1 (nc wave-uniform).
+// Candidates 0 .. nc-1 of the row whose first candidate is src: register j
+// holds candidates 64*j .. 64*j+63 and is loaded while 64*j < nc (one scalar
+// test per register).  Lanes past the last candidate re-read it (their keys
+// are masked when converted), so no lane mask is set per register.
 template <int KREG>
 __device__ __forceinline__ void load_row(const float *src, int nc, int lane, unsigned (&raw)[KREG]) {
     const unsigned *s = reinterpret_cast<const unsigned *>(src);
+    const unsigned last = (unsigned)nc - 1u;
 #pragma unroll
     for (int j = 0; j < KREG; ++j) {
-        const int t = j * kWaveSize + lane;
-        if (j * kWaveSize < nc && t < nc) raw[j] = __builtin_nontemporal_load(s + t);
+        if (j * kWaveSize >= nc) break;
+        raw[j] = __builtin_nontemporal_load(s + min((unsigned)(j * kWaveSize + lane), last));
     }
 }
 
-// The number of keys >= cand in registers 0 .. NJ-1.  The compare masks of
-// even registers are popcounted on the scalar unit, those of odd registers on
-// the VALU (v_bcnt_u32_b32 reading the mask from scalar registers): the CU
-// has one scalar ALU for its four SIMDs, and with every count there it was
-// ~93% busy (SQ counters) while the VALU had room.  The s_nop gives the two
+// The number of keys >= cand in registers 0 .. NJ-1.  The compare masks are
+// popcounted on the scalar unit, except every kValuEvery-th on the VALU
+// (v_bcnt_u32_b32 reading the mask from scalar registers): with every count
+// on the CU's one scalar ALU it was ~93% busy (SQ counters) while the VALU
+// had room.  The s_nop gives the two
 // wait states gfx950 needs between a VALU write of an SGPR (the compare) and
 // a VALU read of it; the compiler cannot insert them for inline assembly, and
 // without them the counts came out wrong.
@@ -71,7 +98,7 @@ __device__ __forceinline__ int count_ge(const unsigned (&key)[KREG], unsigned ca
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const uint64_t m = __ballot(key[j] >= cand);
-        if (j & 1) {
+        if (j % kValuEvery == kValuEvery - 1) {
             asm("s_nop 1\n\tv_bcnt_u32_b32 %0, %1, %2" : "=v"(cv) : "s"((unsigned)m), "v"(cv));
             asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(cv) : "s"((unsigned)(m >> 32)), "v"(cv));
         } else {
@@ -79,7 +106,7 @@ __device__ __forceinline__ int count_ge(const unsigned (&key)[KREG], unsigned ca
         }
         if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
-    if (NJ > 1) cs += (int)__builtin_amdgcn_readfirstlane(cv);
+    if (NJ >= kValuEvery) cs += (int)__builtin_amdgcn_readfirstlane(cv);
     return cs;
 }
 
@@ -106,8 +133,8 @@ __device__ __forceinline__ void write_selection(const unsigned (&key)[NJ], const
     // An opaque copy of kth keeps the compiler from reusing the counting
     // compares above, which would hold every register's compare mask in
     // scalar registers until here.
-    unsigned thr = kth;
-    asm volatile("" : "+v"(thr));
+    unsigned thr = __builtin_amdgcn_readfirstlane(kth);
+    asm volatile("" : "+s"(thr));
     int pos = 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -123,39 +150,54 @@ __device__ __forceinline__ void write_selection(const unsigned (&key)[NJ], const
     }
 }
 
-// Selects the row's T largest keys among registers 0 .. NJ-1 (the later ones
-// hold no candidate) and writes their block indices in ascending order.
-// `sh` is this wavefront's 128-word LDS scratch.
-template <int NJ, int KREG>
-__device__ __forceinline__ void select_row(const unsigned (&keyr)[KREG], int T, int lane, int32_t *dst,
-                                           unsigned *sh) {
+// Selects the row's T largest keys and writes their block indices in
+// ascending order.  The row's raw scores sit in registers 0 .. NJ-1 (lane l
+// of register j: candidate 64*j + l, valid below nc); they are turned into
+// keys first, then `next` issues the following row's loads into the same
+// registers, so that they land while this row is selected.  `sh` is this
+// wavefront's 256-word LDS scratch.
+template <int NJ, int KREG, typename Next>
+__device__ __forceinline__ void select_row(unsigned (&raw)[KREG], int nc, int T, int lane, int32_t *dst,
+                                           unsigned *sh, Next &&next) {
+    // Registers below the next smaller size bucket are full (the bucket was
+    // chosen on nc), so only the upper ones need the per-lane mask.
+    // (NJ = 2 also takes rows with one register.)
+    constexpr int FULL = NJ <= 2 ? 0 : NJ <= 8 ? NJ - 2 : NJ <= 16 ? NJ - 4 : NJ <= 32 ? NJ - 8 : NJ - 16;
     unsigned key[NJ];
     int idx[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        key[j] = keyr[j];
         idx[j] = j * kWaveSize + lane;
+        key[j] = (j < FULL || idx[j] < nc) ? score_key(raw[j]) : 0u;
     }
+    next(raw);
     // kth: the largest prefix with at least T keys >= kth, found bit by bit
-    // from the top; cnt = the number of keys >= kth.
+    // from the top; cnt = the number of keys >= kth.  The search stops early
+    // once T <= cnt <= max(T, 64): the keys fit one register (or are exactly
+    // the answer).  One unsigned compare tests both bounds.
+    // The loop has a single exit on one scalar value (separate exits made
+    // the compiler build lane-mask booleans around them).  `bit` ends one
+    // below the last bit tried.
+    const unsigned stop = (unsigned)((T > kWaveSize ? T : kWaveSize) - T);
     unsigned kth = 0;
     int cnt = 0x7FFFFFFF;
     int bit = 31;
-    for (; bit >= 0; --bit) {
+    int go;
+    do {
         const unsigned cand = kth | (1u << bit);
         const int c = count_ge<NJ>(key, cand);
-        if (c >= T) {
-            kth = cand;
-            cnt = c;
-            if (c <= kWaveSize || c == T) break;  // they fit one register, or are the answer
-        }
-    }
+        const bool take = c >= T;  // (c - T) <= stop implies it
+        kth = take ? cand : kth;
+        cnt = take ? c : cnt;
+        go = (unsigned)(c - T) <= stop ? 0 : bit;
+        --bit;
+    } while (go > 0);
     if (NJ == 1 || cnt > kWaveSize) {
         // Done on the registers themselves: exactly T > 64 keys are >= kth,
         // or the search ran through all 32 bits (more than 64 keys tie at
         // the T-th place), or the row fits one register anyway.
         if (NJ == 1) {
-            for (--bit; bit >= 0 && cnt != T; --bit) {
+            for (; bit >= 0 && cnt != T; --bit) {
                 const unsigned cand = kth | (1u << bit);
                 const int c = ballot_count(key[0] >= cand);
                 if (c >= T) {
@@ -170,16 +212,16 @@ __device__ __forceinline__ void select_row(const unsigned (&keyr)[KREG], int T, 
     // Compact the cnt <= 64 keys >= kth (with their block indices) into one
     // register, in ascending block order: the later bits and the write-out
     // touch that register only.  Keys below kth can no longer be selected.
+    // Every lane writes (the others into their own spare words 128 + lane
+    // and 192 + lane), so no lane mask is set per register.
     int base = 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const bool keep = key[j] >= kth;
         const uint64_t km = __ballot(keep);
-        if (keep) {
-            const int p = base + lanes_below(km);
-            sh[p] = key[j];
-            sh[kWaveSize + p] = (unsigned)idx[j];
-        }
+        const int p = keep ? base + lanes_below(km) : 2 * kWaveSize + lane;
+        sh[p] = key[j];
+        sh[kWaveSize + p] = (unsigned)idx[j];
         base += __builtin_popcountll(km);
         if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
@@ -190,7 +232,7 @@ __device__ __forceinline__ void select_row(const unsigned (&keyr)[KREG], int T, 
     k1[0] = lane < cnt ? sh[lane] : 0u;
     i1[0] = (int)sh[kWaveSize + lane];
     __builtin_amdgcn_wave_barrier();  // the next row's compaction comes after these reads
-    for (--bit; bit >= 0 && cnt != T; --bit) {
+    for (; bit >= 0 && cnt != T; --bit) {
         const unsigned cand = kth | (1u << bit);
         const int c = ballot_count(k1[0] >= cand);
         if (c >= T) {
@@ -203,63 +245,87 @@ __device__ __forceinline__ void select_row(const unsigned (&keyr)[KREG], int T, 
 
 // Dispatch on the number of registers that hold candidates (wave-uniform),
 // rounded up to a size bucket no larger than KREG.
-template <int KREG>
-__device__ __forceinline__ void select_any(const unsigned (&key)[KREG], int nc, int T, int lane, int32_t *dst,
-                                           unsigned *sh) {
+template <int KREG, typename Next>
+__device__ __forceinline__ void select_any(unsigned (&raw)[KREG], int nc, int T, int lane, int32_t *dst,
+                                           unsigned *sh, Next &&next) {
     const int nj = (nc + kWaveSize - 1) / kWaveSize;
-    if (KREG <= 2 || nj <= 2) { select_row<(KREG < 2 ? KREG : 2)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 4 || nj <= 4) { select_row<(KREG < 4 ? KREG : 4)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 6 || nj <= 6) { select_row<(KREG < 6 ? KREG : 6)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 8 || nj <= 8) { select_row<(KREG < 8 ? KREG : 8)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 12 || nj <= 12) { select_row<(KREG < 12 ? KREG : 12)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 16 || nj <= 16) { select_row<(KREG < 16 ? KREG : 16)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 24 || nj <= 24) { select_row<(KREG < 24 ? KREG : 24)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 32 || nj <= 32) { select_row<(KREG < 32 ? KREG : 32)>(key, T, lane, dst, sh); return; }
-    if (KREG <= 48 || nj <= 48) { select_row<(KREG < 48 ? KREG : 48)>(key, T, lane, dst, sh); return; }
-    select_row<KREG>(key, T, lane, dst, sh);
+    if (KREG <= 2 || nj <= 2) { select_row<(KREG < 2 ? KREG : 2)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 4 || nj <= 4) { select_row<(KREG < 4 ? KREG : 4)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 6 || nj <= 6) { select_row<(KREG < 6 ? KREG : 6)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 8 || nj <= 8) { select_row<(KREG < 8 ? KREG : 8)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 12 || nj <= 12) { select_row<(KREG < 12 ? KREG : 12)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 16 || nj <= 16) { select_row<(KREG < 16 ? KREG : 16)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 24 || nj <= 24) { select_row<(KREG < 24 ? KREG : 24)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 32 || nj <= 32) { select_row<(KREG < 32 ? KREG : 32)>(raw, nc, T, lane, dst, sh, next); return; }
+    if (KREG <= 48 || nj <= 48) { select_row<(KREG < 48 ? KREG : 48)>(raw, nc, T, lane, dst, sh, next); return; }
+    select_row<KREG>(raw, nc, T, lane, dst, sh, next);
 }
 
+// Division of n < 2^31 by a divisor fixed for the launch, with a multiplier
+// and shift made on the host (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994): q = (mulhi(n, mul) + n)
+// >> shift.  Three scalar instructions instead of a division sequence.
+struct FastDiv {
+    unsigned mul;
+    unsigned shift;
+};
+
+__device__ __forceinline__ unsigned fast_div(unsigned n, FastDiv d) { return (__umulhi(n, d.mul) + n) >> d.shift; }
+
+FastDiv make_fast_div(unsigned d) {
+    unsigned shift = 0;
+    while ((1ull << shift) < d) ++shift;
+    const uint64_t mul = (((1ull << 32) * ((1ull << shift) - d)) / d) + 1;
+    return FastDiv{(unsigned)mul, shift};
+}
+
+struct TopkArgs {
+    const float *scores;
+    int32_t *out;
+    int rows, M, NB, T;
+    FastDiv div_G, div_M, div_bs;
+};
+
 template <int KREG>
-__global__ __launch_bounds__(256) void nsa_topk_kernel(const float *scores, int32_t *out, int rows, int M, int G,
-                                                       int NB, int bs, int T) {
+__global__ __launch_bounds__(256) void nsa_topk_kernel(TopkArgs a) {
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int r0 = __builtin_amdgcn_readfirstlane((blockIdx.x * 4 + (int)(threadIdx.x >> 6)) * kRowsPerWave);
-    if (r0 >= rows) return;  // whole wavefront
-    const int r1 = min(rows, r0 + kRowsPerWave);
-    __shared__ unsigned lds[4][2 * kWaveSize];
+    if (r0 >= a.rows) return;  // whole wavefront
+    const int r1 = min(a.rows, r0 + kRowsPerWave);
+    __shared__ unsigned lds[4][4 * kWaveSize];
     unsigned *sh = lds[threadIdx.x >> 6];
-    auto cands = [&](int row) { return min(((row / G) % M) / bs, NB - 1) + 1; };  // candidates 0 .. nc-1
-    unsigned raw[KREG] = {};
+    // Candidates 0 .. nc-1 of row (b*M + m)*G + g: the blocks t <= m / bs.
+    auto cands = [&](int row) {
+        const unsigned x = fast_div((unsigned)row, a.div_G);              // b*M + m
+        const unsigned m = x - fast_div(x, a.div_M) * (unsigned)a.M;
+        return min((int)fast_div(m, a.div_bs), a.NB - 1) + 1;
+    };
+    unsigned raw[KREG];
     int nc_next = cands(r0);
-    if (nc_next > T) load_row<KREG>(scores + (size_t)r0 * NB, nc_next, lane, raw);
+    if (nc_next > a.T) load_row<KREG>(a.scores + (size_t)r0 * a.NB, nc_next, lane, raw);
     for (int row = r0; row < r1; ++row) {
         const int nc = nc_next;
-        int32_t *dst = out + (size_t)row * T;
-        unsigned key[KREG];
-        if (nc > T) {
-            // A per-lane select on every register measured faster than
-            // skipping the registers past the prefix with scalar branches.
-#pragma unroll
-            for (int j = 0; j < KREG; ++j) key[j] = (j * kWaveSize + lane < nc) ? score_key(raw[j]) : 0u;
-        }
-        if (row + 1 < r1) {  // the next row's scores load during this row's selection
-            nc_next = cands(row + 1);
-            if (nc_next > T) load_row<KREG>(scores + (size_t)(row + 1) * NB, nc_next, lane, raw);
-        }
-        if (nc <= T) {
-            for (int i = lane; i < T; i += kWaveSize) dst[i] = i < nc ? i : -1;
+        int32_t *dst = a.out + (size_t)row * a.T;
+        // The next row's scores load during this row's selection.
+        auto next = [&](unsigned (&r)[KREG]) {
+            if (row + 1 < r1) {
+                nc_next = cands(row + 1);
+                if (nc_next > a.T) load_row<KREG>(a.scores + (size_t)(row + 1) * a.NB, nc_next, lane, r);
+            }
+        };
+        if (nc <= a.T) {
+            next(raw);
+            for (int i = lane; i < a.T; i += kWaveSize) dst[i] = i < nc ? i : -1;
         } else {
-            select_any<KREG>(key, nc, T, lane, dst, sh);
+            select_any<KREG>(raw, nc, a.T, lane, dst, sh, next);
         }
     }
 }
 
 template <int KREG>
-hipError_t launch_topk(const float *scores, int32_t *out, int rows, int M, int G, int NB, int bs, int T,
-                       hipStream_t stream) {
-    const int waves = (rows + kRowsPerWave - 1) / kRowsPerWave;
-    hipLaunchKernelGGL((nsa_topk_kernel<KREG>), dim3((waves + 3) / 4), dim3(256), 0, stream, scores, out, rows, M,
-                       G, NB, bs, T);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
+    const int waves = (a.rows + kRowsPerWave - 1) / kRowsPerWave;
+    hipLaunchKernelGGL((nsa_topk_kernel<KREG>), dim3((waves + 3) / 4), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -274,21 +340,31 @@ extern "C" int nsa_topk_blocks(const float *scores, int32_t *block_indices, int 
     if ((int64_t)B * M * G > INT_MAX) return NSA_SEL_ERR_RANGE;
     const int rows = B * M * G;
     if (ranges_overlap(block_indices, (size_t)rows * T * 4, scores, (size_t)rows * NB * 4)) return NSA_SEL_ERR_ALIAS;
+    TopkArgs a;
+    a.scores = scores;
+    a.out = block_indices;
+    a.rows = rows;
+    a.M = M;
+    a.NB = NB;
+    a.T = T;
+    a.div_G = make_fast_div((unsigned)G);
+    a.div_M = make_fast_div((unsigned)M);
+    a.div_bs = make_fast_div((unsigned)block_size);
     hipError_t e;
     const int kreg = (NB + kWaveSize - 1) / kWaveSize;
     if (kreg <= 1)
-        e = launch_topk<1>(scores, block_indices, rows, M, G, NB, block_size, T, stream);
+        e = launch_topk<1>(a, stream);
     else if (kreg <= 2)
-        e = launch_topk<2>(scores, block_indices, rows, M, G, NB, block_size, T, stream);
+        e = launch_topk<2>(a, stream);
     else if (kreg <= 4)
-        e = launch_topk<4>(scores, block_indices, rows, M, G, NB, block_size, T, stream);
+        e = launch_topk<4>(a, stream);
     else if (kreg <= 8)
-        e = launch_topk<8>(scores, block_indices, rows, M, G, NB, block_size, T, stream);
+        e = launch_topk<8>(a, stream);
     else if (kreg <= 16)
-        e = launch_topk<16>(scores, block_indices, rows, M, G, NB, block_size, T, stream);
+        e = launch_topk<16>(a, stream);
     else if (kreg <= 32)
-        e = launch_topk<32>(scores, block_indices, rows, M, G, NB, block_size, T, stream);
+        e = launch_topk<32>(a, stream);
     else
-        e = launch_topk<64>(scores, block_indices, rows, M, G, NB, block_size, T, stream);
+        e = launch_topk<64>(a, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
 }

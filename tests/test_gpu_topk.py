@@ -62,13 +62,19 @@ SHAPES = [
 def test_topk_exact(torch_cuda, oracle_mod, shape):
     B, M, G, NB, bs, T = shape
     rng = np.random.default_rng(sum(shape))
-    for kind in ("normal", "special", "binary"):
+    for kind in ("normal", "special", "binary", "bits", "denormal"):
         if kind == "normal":
             scores = rng.standard_normal((B, M, G, NB)).astype(np.float32)
         elif kind == "special":
             scores = _special(rng, (B, M, G, NB))
-        else:  # two values: hundreds of keys tie at the T-th place
+        elif kind == "binary":  # two values: hundreds of keys tie at the T-th place
             scores = rng.integers(0, 2, size=(B, M, G, NB)).astype(np.float32)
+        elif kind == "bits":  # every bit pattern: NaN payloads of both signs, infinities, denormals
+            scores = rng.integers(0, 2**32, size=(B, M, G, NB), dtype=np.uint64).astype(np.uint32).view(np.float32)
+        else:  # denormals and signed zeros only: the key map must keep them exact
+            scores = (rng.integers(-40, 41, size=(B, M, G, NB)).astype(np.float32) * np.float32(2.0**-149))
+            flat = scores.reshape(-1)
+            flat[rng.random(flat.size) < 0.1] = -0.0
         got = _gpu_topk(torch_cuda, scores, bs, T)
         want = oracle_mod.topk_blocks(scores, bs, T)
         bad = np.argwhere((got != want).any(axis=3))
