@@ -81,10 +81,11 @@ def test_no_vector_register_spills(kernels):
         assert _spills(text, "vgpr_spill_count") <= limit, name
 
 
-# Scalar spills (into VGPR lanes) allowed on purpose: the top-k kernel for
-# rows of 3073-4096 candidates (64 key registers per lane) keeps a little row
-# state there; every shorter row length is spill-free.
-ALLOWED_SGPR_SPILLS = {r"nsa_topk_kernelILi64E": 8}
+# Scalar spills (into VGPR lanes, not memory) allowed on purpose: the top-k
+# kernel for rows of 2049-4096 candidates (64 key registers per lane, 256
+# VGPRs) keeps row state and the division constants there (30 at the last
+# count); every shorter row length is spill-free.
+ALLOWED_SGPR_SPILLS = {r"nsa_topk_kernelILi64E": 32}
 
 
 def test_no_scalar_spills_on_the_register_merger_path(kernels):
