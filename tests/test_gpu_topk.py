@@ -55,6 +55,7 @@ SHAPES = [
     (1, 200, 2, 1, 64, 2),          # NB = 1
     (1, 900, 1, 900, 1, 90),        # T > 64: more keys than one register at the threshold
     (3, 499, 5, 70, 7, 9),          # B, G > 1; a wavefront's rows cross a batch boundary (m wraps to 0)
+    (1, 4096, 1, 4096, 1, 16),      # bs = 1: row m has m + 1 candidates, so every register count 1..64 occurs
 ]
 
 
