@@ -16,9 +16,8 @@
 //
 // A radix select finds the threshold bit by bit from the top: the count of
 // keys at or above a candidate prefix is one v_cmp per register with its
-// ballot popcounted on the scalar unit for three registers in four and on
-// the VALU for the fourth (no cross-lane arithmetic).  As soon as at most 64
-// keys lie at or above the accepted prefix
+// ballot popcounted on the scalar unit (no cross-lane arithmetic).  As soon
+// as at most 64 keys lie at or above the accepted prefix
 // (for random scores, after the sign, the exponent and a mantissa bit or
 // two), they are compacted through LDS into one register in ascending block
 // order, and the remaining bits cost one compare each.  The search stops when
@@ -41,11 +40,6 @@ namespace {
 // Consecutive rows per wavefront (measured: 4 beats 8, 16 and 32, and loading
 // two rows ahead beats none of them).
 constexpr int kRowsPerWave = 4;
-
-// In the counting passes, every kValuEvery-th register's compare mask is
-// popcounted on the VALU and the others on the scalar unit (measured: the
-// two units then carry about 0.8 and 0.7 instructions per clock per CU).
-constexpr int kValuEvery = 4;
 
 // Larger score -> larger key; NaN takes the key of -inf and -0 that of +0;
 // every score maps to a key >= kMinKey (the key of -inf), leaving 0 free.
@@ -83,31 +77,17 @@ __device__ __forceinline__ void load_row(const float *src, int nc, int lane, uns
     }
 }
 
-// The number of keys >= cand in registers 0 .. NJ-1.  The compare masks are
-// popcounted on the scalar unit, except every kValuEvery-th on the VALU
-// (v_bcnt_u32_b32 reading the mask from scalar registers): with every count
-// on the CU's one scalar ALU it was ~93% busy (SQ counters) while the VALU
-// had room.  The s_nop gives the two
-// wait states gfx950 needs between a VALU write of an SGPR (the compare) and
-// a VALU read of it; the compiler cannot insert them for inline assembly, and
-// without them the counts came out wrong.
+// The number of keys >= cand in registers 0 .. NJ-1: one compare and one
+// scalar popcount per register.
 template <int NJ, int KREG>
 __device__ __forceinline__ int count_ge(const unsigned (&key)[KREG], unsigned cand) {
-    int cs = 0;
-    unsigned cv = 0u;
+    int c = 0;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-        const uint64_t m = __ballot(key[j] >= cand);
-        if (j % kValuEvery == kValuEvery - 1) {
-            asm("s_nop 1\n\tv_bcnt_u32_b32 %0, %1, %2" : "=v"(cv) : "s"((unsigned)m), "v"(cv));
-            asm("v_bcnt_u32_b32 %0, %1, %2" : "=v"(cv) : "s"((unsigned)(m >> 32)), "v"(cv));
-        } else {
-            cs += __builtin_popcountll(m);
-        }
+        c += ballot_count(key[j] >= cand);
         if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
-    if (NJ >= kValuEvery) cs += (int)__builtin_amdgcn_readfirstlane(cv);
-    return cs;
+    return c;
 }
 
 // Lane-prefix popcount: the number of set bits of m below this lane.
@@ -148,6 +128,22 @@ __device__ __forceinline__ void write_selection(const unsigned (&key)[NJ], const
         pos += __builtin_popcountll(tm);
         if (j % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// Continues the bitwise search on one register of keys, from bit `bit` down,
+// until exactly T keys lie at or above kth.  One loop exit on one scalar
+// value (the next bit, or -1 once the count is exact): separate exits made
+// the compiler build lane-mask booleans around them.
+__device__ __forceinline__ unsigned refine_one(unsigned k, int T, int bit, unsigned kth, int cnt) {
+    int b = cnt == T ? -1 : bit;
+    while (b >= 0) {
+        const unsigned cand = kth | (1u << b);
+        const int c = ballot_count(k >= cand);
+        const bool take = c >= T;
+        kth = take ? cand : kth;
+        b = (take && c == T) ? -1 : b - 1;
+    }
+    return kth;
 }
 
 // Selects the row's T largest keys and writes their block indices in
@@ -197,14 +193,7 @@ __device__ __forceinline__ void select_row(unsigned (&raw)[KREG], int nc, int T,
         // or the search ran through all 32 bits (more than 64 keys tie at
         // the T-th place), or the row fits one register anyway.
         if (NJ == 1) {
-            for (; bit >= 0 && cnt != T; --bit) {
-                const unsigned cand = kth | (1u << bit);
-                const int c = ballot_count(key[0] >= cand);
-                if (c >= T) {
-                    kth = cand;
-                    cnt = c;
-                }
-            }
+            kth = refine_one(key[0], T, bit, kth, cnt);
         }
         write_selection<NJ>(key, idx, kth, T, dst);
         return;
@@ -232,14 +221,7 @@ __device__ __forceinline__ void select_row(unsigned (&raw)[KREG], int nc, int T,
     k1[0] = lane < cnt ? sh[lane] : 0u;
     i1[0] = (int)sh[kWaveSize + lane];
     __builtin_amdgcn_wave_barrier();  // the next row's compaction comes after these reads
-    for (; bit >= 0 && cnt != T; --bit) {
-        const unsigned cand = kth | (1u << bit);
-        const int c = ballot_count(k1[0] >= cand);
-        if (c >= T) {
-            kth = cand;
-            cnt = c;
-        }
-    }
+    kth = refine_one(k1[0], T, bit, kth, cnt);
     write_selection<1>(k1, i1, kth, T, dst);
 }
 

