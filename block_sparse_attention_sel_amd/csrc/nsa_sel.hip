@@ -135,6 +135,11 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
         Stage<SBS, D>::read(kf, kbuf, r, q4);
         if (has1) st.issue(st.rk, kbuf, s1, lane);
         const int key0 = s0 * SBS;
+        // Raised wave priority while the products and the softmax issue (the
+        // copy waits and fragment reads run at the normal one): of the two
+        // wavefronts of a SIMD, the one with math ready goes first (measured
+        // 1% at 64k, bitwise equal).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const unsigned tb = (a0 >> (nt * PACK)) & tile_bits;
@@ -145,17 +150,20 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             score_block<SBS, D, BF16>(kf, qf[nt], key0, causal, true, col_on, INT_MIN, min(my_m[nt], p.N - 1),
                                       p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (has1)
             __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(s0) landed; K(s1) may be pending
         else
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
         Stage<SBS, D>::read_vt(vt, vbuf, lane);
         if (has1) st.issue(st.rv, vbuf, s1, lane);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             if (((a0 >> (nt * PACK)) & tile_bits) == 0) continue;
             accumulate_block<SBS, D, BF16>(vt, pf[nt], alpha[nt], acc[nt]);
         }
+        __builtin_amdgcn_s_setprio(0);
         s0 = s1;
         a0 = a1;
     }
