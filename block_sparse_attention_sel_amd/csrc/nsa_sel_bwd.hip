@@ -200,9 +200,12 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
         Stage<SBS, D>::read_vt(kt, kbuf, lane);
         if (has1) st.issue(st.rk, kbuf, s1, lane);
         float4v sc[NT][KT];
+        // Raised wave priority while products issue, as in the forward.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             if ((a0 >> (nt * PACK)) & tile_bits) dq_scores<SBS, D>(kf, qf[nt], sc[nt]);
+        __builtin_amdgcn_s_setprio(0);
         if (has1)
             __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(s0) landed
         else
@@ -210,6 +213,7 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
         Stage<SBS, D>::read(vf, vbuf, r, q4);
         if (has1) st.issue(st.rv, vbuf, s1, lane);
         const int key0 = s0 * SBS;
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const unsigned tb = (a0 >> (nt * PACK)) & tile_bits;
@@ -220,6 +224,7 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
             dq_grad<SBS, D>(vf, kt, df[nt], sc[nt], key0, causal, col_on, min(my_m[nt], p.N - 1), p.scale_log2,
                             lse2[nt], delta[nt], acc[nt], q4);
         }
+        __builtin_amdgcn_s_setprio(0);
         s0 = s1;
         a0 = a1;
     }
