@@ -3,7 +3,8 @@
 One step is one nsa_sel_fwd launch over the whole workload (all (b, m, g)
 units of the config) with inputs already resident in HBM.  Prints ONE JSON
 line: effective TFLOP/s as ``value``, plus ms per step, gathered-KV GB/s, the
-roofline of the kernel (HBM-bound on gathered bytes), cold-cache timings, the
+roofline of the kernel (the larger of compulsory bytes at the HBM peak and
+effective flops at the fp16 MFMA peak), cold-cache timings, the
 gather-ceiling probe (the kernel's block-gather stream alone), the MFMA
 utilisation, the same kernel with every causal block selected (dense mode),
 the dense causal attention kernel on the same tensors (the reference point of
@@ -74,16 +75,39 @@ def _kernel_sha() -> str:
     return h.hexdigest()
 
 
-def _traffic():
-    """HBM bytes per nsa_sel_fwd call from committed rocprofv3 counters, if
-    they were taken on the current kernel source; else None."""
+def _counters():
+    """The committed rocprofv3 counter summary of nsa_sel_fwd (HBM bytes per
+    call, L2 hits), if it was taken on the current kernel source; else None."""
     try:
         rec = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_sha256") != _kernel_sha():
         return None
-    return rec.get("hbm_bytes_per_call")
+    return rec
+
+
+def compulsory_bytes(cfg: Config) -> int:
+    """Bytes every launch must move at least once: Q and O [B,M,H,D] (2 B),
+    K and V [B,N,G,D] (2 B), the index rows [B,M,G,T] (4 B), LSE [B,H,M] (4 B)."""
+    q = cfg.B * cfg.M * cfg.H * cfg.D * 2
+    kv = cfg.B * cfg.N * cfg.G * cfg.D * 2
+    return 2 * q + 2 * kv + cfg.B * cfg.M * cfg.G * cfg.T * 4 + cfg.B * cfg.H * cfg.M * 4
+
+
+def roofline(flops: float, compulsory: int, ms: float, traffic=None) -> dict:
+    """The kernel against its binding roofline: the larger of compulsory bytes
+    at the HBM peak and effective flops at the fp16 MFMA peak is the time a
+    launch cannot beat; frac = that time / the measured time (= achieved /
+    peak in the binding unit)."""
+    t_hbm = compulsory / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (FP16_PEAK_TFLOPS * 1e12)
+    s = ms * 1e-3
+    if t_mfma >= t_hbm:
+        return {"bound": "mfma", "achieved": round(flops / s / 1e12, 2), "peak": FP16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(t_mfma / s, 4), "traffic": traffic}
+    return {"bound": "hbm", "achieved": round(compulsory / s / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(t_hbm / s, 4), "traffic": traffic}
 
 
 def _counter_sums(csv_path: str, counter: str):
@@ -99,12 +123,19 @@ def _counter_sums(csv_path: str, counter: str):
     return out
 
 
-def summarize_pmc(fetch_csv: str, write_csv: str, calls: int, copy_mib: int, out_path: str):
+def summarize_pmc(fetch_csv: str, write_csv: str, calls: int, copy_mib: int, out_path: str, l2_csv=None):
     """Turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) of `bench.py --copy-probe-mib N --steps S --warmup W --no-dense
     --no-cpu-baseline` into HBM bytes per nsa_sel_fwd call.  Each counter is
-    scaled by what it reads for the plain N MiB device copy in the same run."""
+    scaled by what it reads for the plain N MiB device copy in the same run.
+    l2_csv: an optional third run with TCC_HIT_sum and TCC_MISS_sum, giving the
+    L2 hit rate of the forward's requests."""
     res = {"kernel_sha256": _kernel_sha(), "calls": calls, "copy_probe_mib": copy_mib}
+    if l2_csv:
+        hit = sum(v for (n, v) in _counter_sums(l2_csv, "TCC_HIT_sum").values() if "nsa_sel_fwd_kernel" in n)
+        miss = sum(v for (n, v) in _counter_sums(l2_csv, "TCC_MISS_sum").values() if "nsa_sel_fwd_kernel" in n)
+        res["l2_requests_per_call"] = (hit + miss) / calls
+        res["l2_hit"] = hit / (hit + miss) if hit + miss > 0 else None
     for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         sums = _counter_sums(path, counter)
         copy = [v for (n, v) in sums.values() if "copyBuffer" in n and v > 1000]
@@ -254,14 +285,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for HBM counters)")
-    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the HBM-traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="write the counter summary from rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE and "
+                         "optionally TCC_HIT_sum/TCC_MISS_sum) and exit")
     ap.add_argument("--pmc-calls", type=int, default=0, help="nsa_sel_fwd calls in the --pmc runs")
     args = ap.parse_args()
 
     if args.summarize_pmc:
+        if len(args.summarize_pmc) not in (2, 3):
+            ap.error("--summarize-pmc takes FETCH_CSV WRITE_CSV [L2_CSV]")
         res = summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.pmc_calls,
-                            args.copy_probe_mib, COUNTERS_FILE)
+                            args.copy_probe_mib, COUNTERS_FILE,
+                            args.summarize_pmc[2] if len(args.summarize_pmc) == 3 else None)
         print(json.dumps(res))
         return
 
@@ -297,6 +332,7 @@ def main():
     blocks, keys = work_counts(cfg, idx)
     gathered = blocks * cfg.block_size * cfg.D * 2 * 2
     flops = 4.0 * cfg.D * cfg.gs * keys
+    compulsory = compulsory_bytes(cfg)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warmup", file=sys.stderr, flush=True)
     wall_ms, ev_ms, ev_min = time_launches(torch, launch, args.steps, args.warmup)
     assert torch.isfinite(L).all().item(), "non-finite LSE"
@@ -324,10 +360,26 @@ def main():
         "gathered_GBps": round(gbps, 1),
         "eff_TFLOPs": round(flops / (ev_ms * 1e-3) / 1e12, 3),
         "work": {"counted_blocks": blocks, "visible_keys": keys, "gathered_bytes": gathered,
-                 "effective_flops": flops},
-        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": _traffic()},
+                 "effective_flops": flops, "compulsory_bytes": compulsory},
     }
+    counters = _counters()
+    traffic = counters.get("hbm_bytes_per_call") if counters else None
+    out["roofline"] = roofline(flops, compulsory, ev_ms, traffic)
+    # Beside the roofline: the time each bound alone allows, the counter
+    # traffic past the L2 (measured HBM/Infinity-Cache bytes) as a rate and a
+    # fraction of the HBM peak, the L2 hit rate of the kernel's requests, and
+    # the logical gathered-K/V rate (cache-served re-reads included, so it may
+    # exceed the HBM peak).
+    detail = {"compulsory_bytes": compulsory,
+              "t_hbm_ms": round(compulsory / (HBM_PEAK_GBPS * 1e9) * 1e3, 4),
+              "t_mfma_ms": round(flops / (FP16_PEAK_TFLOPS * 1e12) * 1e3, 4),
+              "gathered_GBps": round(gbps, 1)}
+    if traffic:
+        detail["traffic_GBps"] = round(traffic / (ev_ms * 1e-3) / 1e9, 1)
+        detail["traffic_frac_of_hbm_peak"] = round(traffic / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+        detail["traffic_over_compulsory"] = round(traffic / compulsory, 2)
+    if counters and counters.get("l2_hit") is not None:
+        detail["l2_hit"] = round(counters["l2_hit"], 4)
 
     if args.cold_steps > 0:
         print(f"[bench] cold timing, {args.cold_steps} calls", file=sys.stderr, flush=True)
@@ -335,6 +387,8 @@ def main():
         out["cold"] = {"ms_median": round(c_med, 4), "ms_min": round(c_min, 4), "flush_MiB": 1024,
                        "eff_TFLOPs": round(flops / (c_med * 1e-3) / 1e12, 3),
                        "gathered_GBps": round(gathered / (c_med * 1e-3) / 1e9, 1)}
+        detail["frac_cold_median"] = roofline(flops, compulsory, c_med)["frac"]
+    out["roofline_detail"] = detail
 
     # MFMA work actually issued: every (16-column tile, staged block) pair runs
     # the QK and PV products over the whole block, 4 * 16 * bs * D flops.

@@ -84,6 +84,29 @@ def _addr(x) -> int:
     return int(x.data_ptr())
 
 
+def _check(t, name: str, dtype, shape=None, device=None):
+    """Argument check of a torch tensor handed to an entry point: type, dtype,
+    shape, contiguity and (when given) the device of the call.  Raises
+    TypeError for a wrong type or dtype and ValueError for the rest; the C ABI
+    sees only pointers, so a buffer of the wrong size would be written out of
+    bounds."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError(f"{name} must be a {dtype} tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+
+
+def _require_gpu(**tensors):
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+
+
 def nsa_sel_status_string(status: int) -> str:
     return load_library().nsa_sel_status_string(int(status)).decode()
 
@@ -99,11 +122,21 @@ def nsa_sel_fwd_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size
               ctypes.c_void_p(_addr(stream)))
 
 
-def nsa_sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> None:
-    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
-    rc = nsa_sel_fwd_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream)
+def nsa_sel_fwd(*args, **kwargs):
+    """Two forms of the one entry point.
+
+    ``nsa_sel_fwd(q, k, v, block_indices, block_size, out=None, lse=None,
+    stream=None) -> (O, LSE)``: torch tensors (see ``sel_attn_fwd``).
+
+    ``nsa_sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D,
+    block_size, T, stream=0) -> None``: the C entry point's own arguments
+    (pointers as ints or tensors); raises NsaSelError on a nonzero status."""
+    if len(args) + len(kwargs) <= 8 and len(args) <= 5:
+        return sel_attn_fwd(*args, **kwargs)
+    rc = nsa_sel_fwd_raw(*args, **kwargs)
     if rc != NSA_SEL_OK:
         raise NsaSelError(rc)
+    return None
 
 
 def nsa_sel_fwd_bf16(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> None:
@@ -124,13 +157,17 @@ def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, st
                         ("block_indices", block_indices, torch.int32)):
         if not isinstance(t, torch.Tensor) or t.dtype != dt or t.dim() != 4:
             raise TypeError(f"{name} must be a 4-d {dt} tensor")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        _check(t, name, dt, device=q.device)
     B, M, H, D = q.shape
     _, N, G, _ = k.shape
     T = block_indices.shape[3]
     if (k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape or tuple(block_indices.shape[:3]) != (B, M, G):
         raise ValueError("inconsistent shapes")
+    if out is not None:
+        _check(out, "out", et, (B, M, H, D), q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, M), q.device)
+    _require_gpu(q=q, k=k, v=v, block_indices=block_indices)
     if out is None:
         out = torch.empty((B, M, H, D), dtype=et, device=q.device)
     if lse is None:
@@ -191,19 +228,24 @@ def sel_attn_bwd(q, k, v, block_indices, out, lse, dout, block_size: int, worksp
                         ("dout", dout, torch.float16)):
         if not isinstance(t, torch.Tensor) or t.dtype != dt or t.dim() != 4:
             raise TypeError(f"{name} must be a 4-d {dt} tensor")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
-    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous():
-        raise TypeError("lse must be a contiguous float32 GPU tensor")
+        _check(t, name, dt, device=q.device)
+    _check(lse, "lse", torch.float32, device=q.device)
     B, M, H, D = q.shape
     _, N, G, _ = k.shape
     T = block_indices.shape[3]
     if ((k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape or tuple(block_indices.shape[:3]) != (B, M, G)
             or out.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, H, M)):
         raise ValueError("inconsistent shapes")
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, device=q.device)
+        if workspace.dim() != 1:
+            raise ValueError("workspace must be a 1-d uint8 tensor")
+    _require_gpu(q=q, k=k, v=v, block_indices=block_indices, out=out, dout=dout, lse=lse)
     nbytes = nsa_sel_bwd_workspace_size(B, M, N, H, G, D, block_size, T)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes; {nbytes} are needed")
     dq = torch.empty((B, M, H, D), dtype=torch.float32, device=q.device)
     dk = torch.empty((B, N, G, D), dtype=torch.float32, device=q.device)
     dv = torch.empty((B, N, G, D), dtype=torch.float32, device=q.device)
@@ -236,12 +278,16 @@ def dense_attn_fwd(q, k, v, out=None, lse=None, stream=None):
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dtype != torch.float16 or t.dim() != 4:
             raise TypeError(f"{name} must be a 4-d float16 tensor")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        _check(t, name, torch.float16, device=q.device)
     B, M, H, D = q.shape
     _, N, G, _ = k.shape
     if (k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape:
         raise ValueError("inconsistent shapes")
+    if out is not None:
+        _check(out, "out", torch.float16, (B, M, H, D), q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, M), q.device)
+    _require_gpu(q=q, k=k, v=v)
     if out is None:
         out = torch.empty((B, M, H, D), dtype=torch.float16, device=q.device)
     if lse is None:
@@ -282,12 +328,16 @@ def window_attn_fwd(q, k, v, left: int, right: int, out=None, lse=None, stream=N
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.dtype != et or t.dim() != 4:
             raise TypeError(f"{name} must be a 4-d {et} tensor")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous GPU tensor")
+        _check(t, name, et, device=q.device)
     B, M, H, D = q.shape
     _, N, G, _ = k.shape
     if (k.shape[0], k.shape[3]) != (B, D) or v.shape != k.shape:
         raise ValueError("inconsistent shapes")
+    if out is not None:
+        _check(out, "out", et, (B, M, H, D), q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, (B, H, M), q.device)
+    _require_gpu(q=q, k=k, v=v)
     if out is None:
         out = torch.empty((B, M, H, D), dtype=et, device=q.device)
     if lse is None:
@@ -322,9 +372,11 @@ def topk_blocks(scores, block_size: int, T: int, out=None, stream=None):
 
     if not isinstance(scores, torch.Tensor) or scores.dtype != torch.float32 or scores.dim() != 4:
         raise TypeError("scores must be a 4-d float32 tensor")
-    if not scores.is_cuda or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous GPU tensor")
+    _check(scores, "scores", torch.float32)
     B, M, G, NB = scores.shape
+    if out is not None:
+        _check(out, "out", torch.int32, (B, M, G, T), scores.device)
+    _require_gpu(scores=scores)
     if out is None:
         out = torch.empty((B, M, G, T), dtype=torch.int32, device=scores.device)
     if stream is None:

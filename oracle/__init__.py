@@ -58,6 +58,8 @@ def _load():
         lib.nsa_oracle_window_units.argtypes = ([p, p, p] + [i64] * 8 + [p, i64, p, p, ctypes.c_int, ctypes.c_int])
         lib.nsa_oracle_bwd_units.restype = ctypes.c_int
         lib.nsa_oracle_bwd_units.argtypes = ([p] * 5 + [i64] * 8 + [p, i64, p, i64, p, p, p, p, p, p, ctypes.c_int])
+        lib.nsa_oracle_compare.restype = ctypes.c_int
+        lib.nsa_oracle_compare.argtypes = ([p] * 4 + [i64] * 10 + [p, p, i64, i64, ctypes.c_int, ctypes.c_int, p])
         lib.nsa_oracle_topk.restype = ctypes.c_int
         lib.nsa_oracle_topk.argtypes = [p] + [i64] * 6 + [p]
         lib.nsa_oracle_topk_rows.restype = ctypes.c_int
@@ -182,6 +184,42 @@ def dense_full(q, k, v, threads: int = 0):
     G = k.shape[2]
     O, L = dense_units(q, k, v, all_units(B, M, G), threads)
     return O.reshape(B, M, H, D), L.reshape(B, M, H).transpose(0, 2, 1).copy()
+
+
+def compare(q, k, v, idx, block_size: int, O, L, u0: int = 0, u1: int | None = None, threads: int = 0,
+            dtype: str = "fp16", window: tuple[int, int] | None = None) -> dict:
+    """Compares a computed forward result O [B, M, H, D] (fp16, or bf16 bit
+    patterns as uint16) and LSE L fp32 [B, H, M] with the oracle over the units
+    u0 .. u1-1 of the order u = (b*M + m)*G + g, one unit at a time (no fp64
+    copy of the outputs is kept).  idx None compares with the attention
+    without index rows over ``window`` = (left, right) (default (-1, 0): dense
+    causal).  Returns max_err_O (every element; an empty row's reference is
+    0), max_err_LSE (rows with a finite reference), bad_rows (non-finite O or
+    LSE where the reference is finite, or LSE != -inf on an empty row), the
+    units holding the largest errors, units compared, units with repeated
+    blocks and empty rows."""
+    if idx is None:
+        idx_arr = np.zeros((q.shape[0], q.shape[1], k.shape[2], 1), np.int32)
+    else:
+        idx_arr = idx
+    B, M, N, H, G, D, T = _check_inputs(q, k, v, idx_arr, dtype)
+    et = _ELEM[dtype][0]
+    if O.dtype != et or O.shape != q.shape or not O.flags.c_contiguous:
+        raise ValueError("O must be a C-contiguous array shaped and typed like Q")
+    if L.dtype != np.float32 or L.shape != (B, H, M) or not L.flags.c_contiguous:
+        raise ValueError("L must be a C-contiguous float32 [B, H, M] array")
+    left, right = window if window is not None else (-1, 0)
+    if u1 is None:
+        u1 = B * M * G
+    stats = np.zeros(8, dtype=np.float64)
+    rc = _load().nsa_oracle_compare(_ptr(q), _ptr(k), _ptr(v), None if idx is None else _ptr(idx_arr), B, M, N, H,
+                                    G, D, block_size, T, left, right, _ptr(O), _ptr(L), int(u0), int(u1),
+                                    _ELEM[dtype][1], threads, _ptr(stats))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return {"max_err_O": float(stats[0]), "max_err_LSE": float(stats[1]), "bad_rows": int(stats[2]),
+            "worst_unit_O": int(stats[3]), "worst_unit_LSE": int(stats[4]), "units": int(stats[5]),
+            "dup_units": int(stats[6]), "empty_rows": int(stats[7])}
 
 
 def bwd_units(q, k, v, idx, do, block_size: int, units: np.ndarray, kblocks: np.ndarray | None = None,

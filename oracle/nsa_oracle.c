@@ -334,6 +334,187 @@ int nsa_oracle_window_units(const uint16_t *Q, const uint16_t *K, const uint16_t
 }
 
 /*
+ * Streaming comparison of a computed forward result with the oracle, unit by
+ * unit, keeping no fp64 copy of the outputs (the plain definition above is
+ * evaluated for each unit into a per-thread buffer and compared at once).
+ *
+ *   Og  : 16-bit patterns [B, M, H, D] of the output to check (elem 0 = fp16,
+ *         1 = bf16), decoded exactly;
+ *   Lg  : fp32 [B, H, M] log-sum-exp to check;
+ *   units u0 .. u1-1 of the linear order u = (b*M + m)*G + g;
+ *   idx NULL with (left, right) compares against the attention without index
+ *   rows (keys m - left .. m + right, negative = unbounded; (-1, 0) = dense
+ *   causal).
+ *
+ * stats (double[8]) receives:
+ *   [0] max |O - O_ref| over every element of the units (an empty row's
+ *       O_ref is 0);
+ *   [1] max |LSE - LSE_ref| over the rows whose LSE_ref is finite;
+ *   [2] rows with a non-finite O element, a non-finite LSE where LSE_ref is
+ *       finite, or an LSE other than -inf where the row is empty (LSE_ref =
+ *       -inf);
+ *   [3] the unit (linear index) holding the largest O error, [4] the one
+ *       holding the largest LSE error (the smallest such unit; -1 while
+ *       every error is 0);
+ *   [5] units compared; [6] units whose row repeats a valid block;
+ *   [7] rows whose LSE_ref is -inf.
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+typedef struct {
+    job_t base;
+    const uint16_t *Og;
+    const float *Lg;
+    int64_t u0, u1;
+    double max_o, max_l;
+    int64_t worst_o, worst_l, bad, empty, count;
+} cjob_t;
+
+static void *cworker(void *arg) {
+    cjob_t *c = (cjob_t *)arg;
+    job_t *J = &c->base;
+    const int64_t NB = (J->N + J->bs - 1) / J->bs;
+    const int64_t gs = J->H / J->G, D = J->D, M = J->M, G = J->G, H = J->H;
+    scratch_t w;
+    double *O = (double *)malloc(sizeof(double) * (size_t)(gs * D));
+    double *L = (double *)malloc(sizeof(double) * (size_t)gs);
+    w.mark = (unsigned char *)malloc((size_t)NB);
+    w.keys = (int64_t *)malloc(sizeof(int64_t) * (size_t)J->N);
+    w.score = (double *)malloc(sizeof(double) * (size_t)(gs * J->N));
+    w.qd = (double *)malloc(sizeof(double) * (size_t)(gs * D));
+    w.kd = (double *)malloc(sizeof(double) * (size_t)D);
+    w.mu = (double *)malloc(sizeof(double) * (size_t)gs);
+    w.z = (double *)malloc(sizeof(double) * (size_t)gs);
+    c->max_o = 0.0;
+    c->max_l = 0.0;
+    c->worst_o = -1;
+    c->worst_l = -1;
+    if (!O || !L || !w.mark || !w.keys || !w.score || !w.qd || !w.kd || !w.mu || !w.z) {
+        J->error = 1;
+    } else {
+        job_t fj = *J;
+        fj.O = O;
+        fj.LSE = L;
+        for (int64_t u = c->u0 + J->thread_id; u < c->u1; u += J->n_threads) {
+            const int64_t g = u % G, m = (u / G) % M, b = u / (G * M);
+            int64_t one[3] = {b, m, g};
+            fj.units = one;
+            one_unit(&fj, 0, &w);
+            for (int64_t i = 0; i < gs; ++i) {
+                const int64_t h = g * gs + i;
+                const uint16_t *og = c->Og + ((b * M + m) * H + h) * D;
+                int bad = 0;
+                for (int64_t d = 0; d < D; ++d) {
+                    const double x = J->tab[og[d]];
+                    if (!isfinite(x)) {
+                        bad = 1;
+                        continue;
+                    }
+                    const double e = fabs(x - O[i * D + d]);
+                    if (e > c->max_o) {
+                        c->max_o = e;
+                        c->worst_o = u;
+                    }
+                }
+                const double lg = (double)c->Lg[(b * H + h) * M + m];
+                if (isfinite(L[i])) {
+                    if (!isfinite(lg)) {
+                        bad = 1;
+                    } else {
+                        const double e = fabs(lg - L[i]);
+                        if (e > c->max_l) {
+                            c->max_l = e;
+                            c->worst_l = u;
+                        }
+                    }
+                } else {
+                    c->empty++;
+                    if (!(isinf(lg) && lg < 0)) bad = 1;
+                }
+                c->bad += bad;
+            }
+            c->count++;
+        }
+        J->dup_units = fj.dup_units;
+    }
+    free(O); free(L);
+    free(w.mark); free(w.keys); free(w.score); free(w.qd); free(w.kd); free(w.mu); free(w.z);
+    return NULL;
+}
+
+int nsa_oracle_compare(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const int32_t *block_indices,
+                       int64_t B, int64_t M, int64_t N, int64_t H, int64_t G, int64_t D, int64_t block_size,
+                       int64_t T, int64_t left, int64_t right, const uint16_t *Og, const float *Lg, int64_t u0,
+                       int64_t u1, int elem, int n_threads, double *stats) {
+    if (elem != 0 && elem != 1) return -1;
+    if (!Q || !K || !V || !Og || !Lg || !stats) return -1;
+    if (B < 1 || M < 1 || N < 1 || H < 1 || G < 1 || D < 1 || block_size < 1 || T < 1) return -1;
+    if (H % G) return -1;
+    if (u0 < 0 || u1 < u0 || u1 > B * M * G) return -1;
+    pthread_once(&g_half_once, fill_half_table);
+    if (n_threads <= 0) n_threads = (int)sysconf(_SC_NPROCESSORS_ONLN);
+    if (n_threads < 1) n_threads = 1;
+    if (u1 - u0 < n_threads) n_threads = u1 > u0 ? (int)(u1 - u0) : 1;
+    cjob_t *jobs = (cjob_t *)calloc((size_t)n_threads, sizeof(cjob_t));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    for (int i = 0; i < n_threads; ++i) {
+        job_t *J = &jobs[i].base;
+        J->Q = Q; J->K = K; J->V = V; J->idx = block_indices;
+        J->B = B; J->M = M; J->N = N; J->H = H; J->G = G; J->D = D;
+        J->bs = block_indices ? block_size : 1;
+        J->T = block_indices ? T : 1;
+        J->thread_id = i; J->n_threads = n_threads;
+        J->tab = elem ? g_bf16 : g_half;
+        J->left = left; J->right = right;
+        jobs[i].Og = Og; jobs[i].Lg = Lg; jobs[i].u0 = u0; jobs[i].u1 = u1;
+    }
+    int rc = 0, started = 0;
+    for (int i = 0; i < n_threads; ++i) {
+        if (pthread_create(&th[i], NULL, cworker, &jobs[i]) != 0) {
+            rc = -1;
+            break;
+        }
+        started++;
+    }
+    for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    if (started < n_threads) rc = -1;
+    double mo = 0.0, ml = 0.0;
+    int64_t wo = -1, wl = -1, bad = 0, dup = 0, empty = 0, count = 0;
+    for (int i = 0; i < started; ++i) {
+        const cjob_t *c = &jobs[i];
+        if (c->base.error) rc = -1;
+        /* Largest error; among equal ones the smallest unit. */
+        if (c->worst_o >= 0 && (c->max_o > mo || (c->max_o == mo && (wo < 0 || c->worst_o < wo)))) {
+            mo = c->max_o;
+            wo = c->worst_o;
+        }
+        if (c->worst_l >= 0 && (c->max_l > ml || (c->max_l == ml && (wl < 0 || c->worst_l < wl)))) {
+            ml = c->max_l;
+            wl = c->worst_l;
+        }
+        bad += c->bad;
+        dup += c->base.dup_units;
+        empty += c->empty;
+        count += c->count;
+    }
+    stats[0] = mo;
+    stats[1] = ml;
+    stats[2] = (double)bad;
+    stats[3] = (double)wo;
+    stats[4] = (double)wl;
+    stats[5] = (double)count;
+    stats[6] = (double)dup;
+    stats[7] = (double)empty;
+    free(jobs);
+    free(th);
+    return rc;
+}
+
+/*
  * Backward of the same operation, in fp64 (the reason the forward returns LSE:
  * wave issue "[wave] NSA: selection attention forward kernel", section
  * Requirements).  For a unit (b, m, g), head h of the group, with the visible

@@ -320,3 +320,70 @@ def _topk_call(S=1 << 36, I=2 << 36, B=1, M=256, G=2, NB=4, bs=64, T=4):
 ])
 def test_topk_rejects_bad_arguments(lib, over, code):
     assert _topk_call(**over) == code
+
+
+# --- the torch wrappers check caller-supplied buffers before any call ----------
+
+def _cpu_inputs(B=1, M=64, N=64, H=8, G=2, D=64, T=4, dtype=None):
+    import torch
+    dt = dtype or torch.float16
+    q = torch.zeros((B, M, H, D), dtype=dt)
+    k = torch.zeros((B, N, G, D), dtype=dt)
+    v = torch.zeros((B, N, G, D), dtype=dt)
+    idx = torch.zeros((B, M, G, T), dtype=torch.int32)
+    return q, k, v, idx
+
+
+def test_wrappers_reject_bad_out_and_lse():
+    import torch
+    q, k, v, idx = _cpu_inputs()
+    good_o = torch.empty_like(q)
+    good_l = torch.empty((1, 8, 64), dtype=torch.float32)
+    bad = [
+        (dict(out=torch.empty((1, 64, 8, 32), dtype=torch.float16)), ValueError),   # short
+        (dict(out=torch.empty_like(q, dtype=torch.float32)), TypeError),            # dtype
+        (dict(out=torch.empty((1, 64, 64, 8), dtype=torch.float16).transpose(2, 3)), ValueError),  # strided
+        (dict(lse=torch.empty((1, 64, 8), dtype=torch.float32)), ValueError),       # [B, M, H] instead of [B, H, M]
+        (dict(lse=torch.empty((1, 8, 64), dtype=torch.float16)), TypeError),
+        (dict(out=good_o.numpy()), TypeError),                                      # not a tensor
+    ]
+    for kw, err in bad:
+        with pytest.raises(err):
+            binding.sel_attn_fwd(q, k, v, idx, 32, **kw)
+        with pytest.raises(err):
+            binding.nsa_sel_fwd(q, k, v, idx, 32, **kw)     # the tensor form of the entry point
+    # Good buffers get as far as the GPU check (these are host tensors).
+    with pytest.raises(ValueError, match="GPU"):
+        binding.sel_attn_fwd(q, k, v, idx, 32, out=good_o, lse=good_l)
+    with pytest.raises(ValueError):
+        binding.dense_attn_fwd(q, k, v, out=torch.empty((1, 64, 8, 32), dtype=torch.float16))
+    with pytest.raises(ValueError):
+        binding.window_attn_fwd(q, k, v, 8, 0, lse=torch.empty((1, 8, 65), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        binding.topk_blocks(torch.zeros((1, 64, 2, 2), dtype=torch.float32), 32, 4,
+                            out=torch.empty((1, 64, 2, 3), dtype=torch.int32))
+    with pytest.raises(TypeError):
+        binding.topk_blocks(torch.zeros((1, 64, 2, 2), dtype=torch.float32), 32, 4,
+                            out=torch.empty((1, 64, 2, 4), dtype=torch.int64))
+
+
+def test_bwd_wrapper_rejects_bad_workspace():
+    import torch
+    q, k, v, idx = _cpu_inputs()
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 8, 64), dtype=torch.float32)
+    for ws, err in ((torch.empty(1024, dtype=torch.int8), TypeError),
+                    (torch.empty((4, 256), dtype=torch.uint8), ValueError),
+                    (torch.empty(2048, dtype=torch.uint8)[::2], ValueError)):
+        with pytest.raises(err):
+            binding.sel_attn_bwd(q, k, v, idx, o, lse, o, 32, workspace=ws)
+
+
+def test_entry_point_forms_dispatch_on_their_arguments(lib):
+    # Fifteen C arguments -> the C entry point (status from the host checks).
+    with pytest.raises(binding.NsaSelError):
+        binding.nsa_sel_fwd(0, 1, 2, 3, 4, 5, 1, 1, 1, 1, 1, 64, 32, 1, 0)
+    # Five tensors-and-block-size arguments -> the tensor form.
+    q, k, v, idx = _cpu_inputs()
+    with pytest.raises(ValueError, match="GPU"):
+        binding.nsa_sel_fwd(q, k, v, idx, 32)

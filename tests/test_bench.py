@@ -147,3 +147,45 @@ def test_committed_counters_match_the_kernel_sources():
     assert rec["kernel_sha256"] == bench._kernel_sha(), "re-take the FETCH_SIZE / WRITE_SIZE runs"
     assert rec["hbm_bytes_per_call"] > 0
     assert os.path.exists(bench.COUNTERS_FILE.replace(".json", ".md"))
+
+
+def test_summarize_pmc_l2_hit_rate(tmp_path):
+    kern = "void (anonymous namespace)::nsa_sel_fwd_kernel<64, 2, 128, 2, 2, false>(Params)"
+    copy = "__amd_rocclr_copyBuffer"
+    fetch, write, l2 = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "l2.csv"
+    _write_counter_csv(fetch, "FETCH_SIZE", [(1, copy, [2048.0]), (2, kern, [10.0])])
+    _write_counter_csv(write, "WRITE_SIZE", [(1, copy, [4096.0]), (2, kern, [1.0])])
+    with open(l2, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, v in (("TCC_HIT_sum", 300.0), ("TCC_MISS_sum", 100.0)):
+            w.writerow({"Dispatch_Id": 2, "Kernel_Name": kern, "Counter_Name": name, "Counter_Value": v})
+            w.writerow({"Dispatch_Id": 1, "Kernel_Name": copy, "Counter_Name": name, "Counter_Value": 7.0})
+    out = tmp_path / "s.json"
+    rec = bench.summarize_pmc(str(fetch), str(write), calls=1, copy_mib=4, out_path=str(out), l2_csv=str(l2))
+    assert rec["l2_hit"] == pytest.approx(0.75)
+    assert rec["l2_requests_per_call"] == pytest.approx(400.0)
+
+
+def test_compulsory_bytes_by_hand():
+    cfg = CONFIGS["64k"]
+    # Q and O: 65536 * 64 * 128 * 2 B each; K and V: 65536 * 8 * 128 * 2 B each;
+    # index rows 65536 * 8 * 16 * 4 B; LSE 64 * 65536 * 4 B.
+    want = 2 * 1073741824 + 2 * 134217728 + 33554432 + 16777216
+    assert bench.compulsory_bytes(cfg) == want
+
+
+def test_roofline_picks_the_binding_bound():
+    # 2.5e12 flops take 1 ms at the MFMA peak; 8e9 bytes take 1 ms at the HBM peak.
+    r = bench.roofline(2.5e12, 4e9, 4.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert r["frac"] == pytest.approx(0.25) and r["achieved"] == pytest.approx(625.0)
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], rel=1e-3)
+    r = bench.roofline(1.25e12, 16e9, 4.0, traffic=123.0)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert r["frac"] == pytest.approx(0.5) and r["achieved"] == pytest.approx(4000.0)
+    assert r["traffic"] == 123.0
+    # A physical roofline: no kernel can exceed it.
+    for ms in (0.5, 1.0, 10.0):
+        r = bench.roofline(2.5e12, 8e9, ms)
+        assert r["frac"] == pytest.approx(1.0 / ms)

@@ -98,15 +98,56 @@ def _parity_sampled(torch, cfg, count, tail=2):
     assert torch.isfinite(O).all().item()
 
 
+def _oracle_threads() -> int:
+    import os
+    n = os.cpu_count() or 1
+    return max(1, min(n, int(os.environ.get("OMP_NUM_THREADS", n))))
+
+
+def parity_every_unit(torch, cfg, launch=None, chunks: int = 8):
+    """Runs the forward once at the config's full size, in the launch
+    configuration the bench times, and compares every (b, m, g) unit with the
+    oracle, streamed in unit ranges (no fp64 copy of the outputs is kept)."""
+    import time
+
+    import oracle
+    _say(f"case {cfg} (every unit)")
+    q, k, v, idx = make_inputs(cfg)
+    O, L = _gpu_run(torch, q, k, v, idx, cfg.block_size) if launch is None else launch(q, k, v, idx)
+    On = O.cpu().numpy()
+    Ln = L.cpu().numpy()
+    del O, L
+    U = cfg.B * cfg.M * cfg.G
+    worst_o = worst_l = 0.0
+    t0 = time.perf_counter()
+    for i in range(chunks):
+        u0, u1 = U * i // chunks, U * (i + 1) // chunks
+        r = oracle.compare(q, k, v, idx, cfg.block_size, On, Ln, u0, u1, _oracle_threads())
+        worst_o = max(worst_o, r["max_err_O"])
+        worst_l = max(worst_l, r["max_err_LSE"])
+        _say(f"  units {u0}..{u1 - 1}: max|dO| = {r['max_err_O']:.3e} (unit {r['worst_unit_O']})  "
+             f"max|dLSE| = {r['max_err_LSE']:.3e} (unit {r['worst_unit_LSE']})  bad rows {r['bad_rows']}  "
+             f"{time.perf_counter() - t0:.1f} s")
+        assert r["units"] == u1 - u0
+        assert r["bad_rows"] == 0 and r["empty_rows"] == 0 and r["dup_units"] == 0
+        assert r["max_err_O"] <= O_TOL and r["max_err_LSE"] <= LSE_TOL
+    return worst_o, worst_l
+
+
+# Every unit of each of the five workloads at full size (wave issue, section
+# Algorithm: the computation is defined for every query position m).
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", list(CONFIGS))
-def test_parity_full_size_sampled(torch_cuda, name):
-    _parity_sampled(torch_cuda, CONFIGS[name], 2048)
+def test_parity_full_size_every_unit(torch_cuda, name):
+    parity_every_unit(torch_cuda, CONFIGS[name])
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["8k", "64k"])
 def test_parity_dense_mode_sampled(torch_cuda, name):
-    # Trailing query blocks see the whole sequence; keep the oracle's share small.
-    _parity_sampled(torch_cuda, CONFIGS[name].dense(), 256, tail=2 if name == "8k" else 0)
+    # Every causal block selected (T = NB): the first two and the last query
+    # block of every group (the longest rows) plus random units.
+    _parity_sampled(torch_cuda, CONFIGS[name].dense(), 512, tail=2 if name == "8k" else 1)
 
 
 KERNEL_SHAPES = [
