@@ -34,6 +34,7 @@
 #include "nsa_sel_common.h"
 #include "nsa_sel_bwd.h"
 
+
 #include <algorithm>
 
 namespace {
@@ -309,7 +310,7 @@ struct Bw {
     int *row_part;      // [R] first partial slot of a row with >= 2 items
     int *starts;        // [R][kmax] first query of each item
     int2 *items;        // [cap] (row, k)
-    int *n_items;       // [1]
+    int *n_items;       // [2]: items, then the overflow flag (nonzero: a capacity bound was exceeded)
     float *part;        // [pcap][2][bs][D] partial dK, dV
     float *dK, *dV;
     int B, M, N, H, G, gs, T, bs, NB, MW, R, qc, kmax, cap, pcap, qpt;
@@ -430,7 +431,11 @@ __global__ __launch_bounds__(1024) void nsa_sel_bwd_scan_kernel(Bw w) {
         __syncthreads();
     }
     if (tid == 0) {
-        *w.n_items = min(carry_i, w.cap);
+        w.n_items[0] = min(carry_i, w.cap);
+        // The plan bounds both from the sizes alone, so this stays 0; were a
+        // bound ever wrong, the caller reads the flag instead of getting
+        // silently clamped gradients.
+        w.n_items[1] = (carry_i > w.cap || carry_p > w.pcap) ? 1 : 0;
         w.rowstat[w.sentinel] = make_float2(INFINITY, 0.f);
     }
 }
@@ -792,7 +797,7 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
             pk = w.dK + o;
             pv = w.dV + o;
         } else {
-            const int psi = w.row_part[row] + k;  // < pcap by the plan's bound
+            const int psi = w.row_part[row] + k;  // < pcap by the plan's bound (else the overflow flag is set)
             const size_t ps = (size_t)(psi < w.pcap ? psi : w.pcap - 1);
             pk = w.part + ((ps * 2 + 0) * BS + (my_key - t * BS)) * D;
             pv = w.part + ((ps * 2 + 1) * BS + (my_key - t * BS)) * D;
@@ -817,7 +822,7 @@ __global__ __launch_bounds__(256) void nsa_sel_bwd_reduce_kernel(Bw w) {
     const int bg = row / w.NB, t = row - bg * w.NB;
     const int b = bg / w.G, g = bg - b * w.G;
     const int p0 = n >= 2 ? w.row_part[row] : 0;
-    if (p0 + n > w.pcap) return;  // cannot happen: the plan bounds the partial slots
+    if (p0 + n > w.pcap) return;  // the plan bounds the partial slots; the scan flags an overflow
     constexpr int V4 = BS * D / 4;  // float4 per tensor
     for (int e = threadIdx.x; e < 2 * V4; e += 256) {
         const int tensor = e / V4, f = e - tensor * V4;
@@ -872,6 +877,8 @@ int bwd_plan(const Params &p, int D, int bs, BwdPlan &pl) {
     if (rows + 1 > (int64_t)1 << 28) return NSA_SEL_ERR_RANGE;          // rowstat byte offsets in 32 bits
     if ((int64_t)p.M * p.H * D * 2 > (int64_t)UINT_MAX) return NSA_SEL_ERR_RANGE;  // Q / dO offsets of one batch
     size_t o = 0;
+    pl.off_nitems = o;  // bytes 0..3 item count, 4..7 overflow flag (documented in the header)
+    o = align256(o + 8);
     pl.off_rowstat = o;
     o = align256(o + (size_t)(rows + 1) * 8);
     pl.off_bits = o;
@@ -886,8 +893,6 @@ int bwd_plan(const Params &p, int D, int bs, BwdPlan &pl) {
     o = align256(o + (size_t)R * pl.kmax * 4);
     pl.off_items = o;
     o = align256(o + (size_t)pl.cap * 8);
-    pl.off_nitems = o;
-    o = align256(o + 4);
     pl.off_part = o;
     o = align256(o + (size_t)pl.pcap * 2 * bs * D * 4);
     pl.total = o;
@@ -922,10 +927,14 @@ extern "C" int nsa_sel_bwd_workspace_size(int B, int M, int N, int H, int G, int
     return NSA_SEL_OK;
 }
 
-extern "C" int nsa_sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
-                           const void *O, const float *LSE, const void *dO, float *dQ, float *dK, float *dV,
-                           void *workspace, size_t workspace_bytes, int B, int M, int N, int H, int G, int D,
-                           int block_size, int T, hipStream_t stream) {
+namespace {
+
+// The backward with its arguments checked against the workspace of
+// workspace_bytes at `workspace`.
+int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_indices, const void *O,
+            const float *LSE, const void *dO, float *dQ, float *dK, float *dV, void *workspace,
+            size_t workspace_bytes, int B, int M, int N, int H, int G, int D, int block_size, int T,
+            hipStream_t stream) {
     if (!Q || !K || !V || !block_indices || !O || !LSE || !dO || !dQ || !dK || !dV) return NSA_SEL_ERR_NULL;
     Params p;
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
@@ -1005,3 +1014,14 @@ extern "C" int nsa_sel_bwd(const void *Q, const void *K, const void *V, const in
         e = (D == 128) ? launch_key_passes<32, 128>(w, pl, stream) : launch_key_passes<32, 64>(w, pl, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" int nsa_sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                           const void *O, const float *LSE, const void *dO, float *dQ, float *dK, float *dV,
+                           void *workspace, size_t workspace_bytes, int B, int M, int N, int H, int G, int D,
+                           int block_size, int T, hipStream_t stream) {
+    return sel_bwd(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, B, M, N, H, G, D,
+                   block_size, T, stream);
+}
+

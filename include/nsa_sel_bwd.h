@@ -59,7 +59,12 @@ int nsa_sel_bwd_workspace_size(int B, int M, int N, int H, int G, int D, int blo
  *   dV    fp32 [B, N, G, D]  output, fully overwritten
  *   workspace, workspace_bytes  device scratch of at least
  *         nsa_sel_bwd_workspace_size() bytes, 256-byte aligned; its contents
- *         on entry do not matter and on return are unspecified
+ *         on entry do not matter.  Once the queued work has completed, the
+ *         32-bit word at byte offset 4 of the workspace is 0; a nonzero value
+ *         means an internal capacity bound of the key-major pass was exceeded
+ *         and dK/dV are incomplete (the bounds are derived from the sizes, so
+ *         this is a guard, not an expected outcome).  The rest of the
+ *         workspace is unspecified on return
  *   B, M, N, H, G, D, block_size, T, stream   as for nsa_sel_fwd
  *
  * Behaviour: every argument is checked on the host before any HIP call, with

@@ -387,3 +387,65 @@ def test_entry_point_forms_dispatch_on_their_arguments(lib):
     q, k, v, idx = _cpu_inputs()
     with pytest.raises(ValueError, match="GPU"):
         binding.nsa_sel_fwd(q, k, v, idx, 32)
+
+
+def _bwd_capacity(idx, M, N, H, G, bs, T):
+    """Brute-force item and partial-slot counts of the key-major backward pass
+    for these index rows, and the bounds the library sizes its workspace with
+    (include/nsa_sel_bwd.h: a key block's selecting queries are cut into items
+    of qc queries; a block with two or more items writes one partial per
+    item)."""
+    import numpy as np
+    B = idx.shape[0]
+    gs = H // G
+    NB = -(-N // bs)
+    qc = min(2048, max(32, (8192 // gs) // 32 * 32))
+    items = parts = 0
+    for b in range(B):
+        for g in range(G):
+            sel = np.zeros((NB, M), bool)
+            for m in range(M):
+                row = idx[b, m, g]
+                ok = (row >= 0) & (row <= m // bs) & (row < NB)
+                sel[row[ok], m] = True
+            n = -(-sel.sum(axis=1) // qc)
+            items += int(n.sum())
+            parts += int(n[n >= 2].sum())
+    pairs = sum(min(bs, M - c * bs) * min(T, c + 1, NB) for c in range(-(-M // bs)))
+    cap = B * G * (NB + -(-pairs // qc))
+    pcap = B * G * -(-2 * pairs // qc) + 1
+    return items, parts, cap, pcap
+
+
+@pytest.mark.parametrize("shape", [
+    # B, M, N, H, G, bs, T, rule
+    (1, 2500, 2500, 16, 1, 64, 8, "uniform"),     # several items per key block
+    (2, 300, 300, 16, 2, 64, 5, "uniform"),
+    (1, 500, 180, 16, 1, 64, 4, "uniform"),       # M > N
+    (1, 200, 333, 6, 2, 32, 6, "uniform"),        # M < N
+    (1, 700, 700, 2, 2, 32, 6, "geometric"),
+    (1, 640, 640, 1, 1, 32, 40, "dense-rows"),    # T > NB, every causal block (gs = 1: qc = 2048)
+    (1, 1100, 1100, 16, 1, 32, 40, "dense-rows"),  # T > NB, qc = 512: blocks with three items
+    (1, 1300, 1300, 32, 2, 64, 16, "noisy"),      # repeats, padding, future and out-of-range entries
+])
+def test_bwd_capacity_bounds_hold(shape):
+    """The workspace's item list and partial slots are sized from the sizes
+    alone; the counts real index rows produce must stay within them."""
+    import numpy as np
+    from block_sparse_attention_sel_amd.inputs import Config, block_indices
+    B, M, N, H, G, bs, T, rule = shape
+    NB = -(-N // bs)
+    if rule == "dense-rows":
+        c = np.arange(M) // bs
+        row = np.arange(T)[None, :]
+        idx = np.where(row <= np.minimum(c, NB - 1)[:, None], row, -1).astype(np.int32)
+        idx = np.ascontiguousarray(np.broadcast_to(idx[None, :, None, :], (B, M, G, T)))
+    elif rule == "noisy":
+        rng = np.random.default_rng(3)
+        idx = rng.integers(-3, NB + 3, size=(B, M, G, T)).astype(np.int32)
+        idx[..., 1] = idx[..., 0]
+    else:
+        idx = block_indices(Config("c", B=B, M=M, N=N, H=H, G=G, D=64, block_size=bs, T=T, rule=rule, seed=7))
+    items, parts, cap, pcap = _bwd_capacity(idx, M, N, H, G, bs, T)
+    assert items <= cap and parts <= pcap
+    assert items > 0

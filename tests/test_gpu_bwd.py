@@ -46,12 +46,24 @@ def _to_dev(torch, *arrs):
     return [torch.from_numpy(np.ascontiguousarray(a)).to("cuda") for a in arrs]
 
 
+def _overflow_word(torch, workspace):
+    """The workspace's overflow flag (32-bit word at byte offset 4): nonzero
+    when a capacity bound of the key-major pass was exceeded."""
+    return int(workspace[4:8].cpu().numpy().view(np.int32)[0])
+
+
 def _gpu_bwd(torch, q, k, v, idx, do, bs, workspace=None):
-    from block_sparse_attention_sel_amd.binding import sel_attn_bwd, sel_attn_fwd
+    from block_sparse_attention_sel_amd.binding import nsa_sel_bwd_workspace_size, sel_attn_bwd, sel_attn_fwd
     tq, tk, tv, ti, tdo = _to_dev(torch, q, k, v, idx, do)
     O, L = sel_attn_fwd(tq, tk, tv, ti, bs)
+    if workspace is None:
+        B, M, H, D = q.shape
+        _, N, G, _ = k.shape
+        workspace = torch.empty(nsa_sel_bwd_workspace_size(B, M, N, H, G, D, bs, idx.shape[3]),
+                                dtype=torch.uint8, device="cuda")
     dq, dk, dv = sel_attn_bwd(tq, tk, tv, ti, O, L, tdo, bs, workspace=workspace)
     torch.cuda.synchronize()
+    assert _overflow_word(torch, workspace) == 0, "a capacity bound of the key-major pass was exceeded"
     return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
 
 
