@@ -1,7 +1,7 @@
 """Thin ctypes binding of libnsa_sel.so and libnsa_gather_probe.so.
 
 ``nsa_sel_fwd``, ``nsa_sel_fwd_bf16``, ``nsa_sel_bwd``,
-``nsa_sel_bwd_workspace_size``, ``nsa_dense_fwd``, ``nsa_window_fwd``,
+``nsa_sel_bwd_workspace_size``, ``nsa_sel_bwd_noalloc``, ``nsa_dense_fwd``, ``nsa_window_fwd``,
 ``nsa_window_fwd_bf16``, ``nsa_topk_blocks`` and ``nsa_sel_status_string``
 mirror the C entry points one to one (pointers may be given as ints or as torch tensors);
 ``sel_attn_fwd``, ``sel_attn_bwd``, ``dense_attn_fwd``, ``window_attn_fwd`` and
@@ -30,10 +30,11 @@ NSA_SEL_ERR_RANGE = 5
 NSA_SEL_ERR_ALIAS = 6
 NSA_SEL_ERR_HIP = 7
 NSA_SEL_ERR_WORKSPACE = 8
+NSA_SEL_ERR_SCRATCH = 9
 
 EXPORTED = ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_status_string")
 DENSE_EXPORTED = ("nsa_dense_fwd", "nsa_window_fwd", "nsa_window_fwd_bf16")
-BWD_EXPORTED = ("nsa_sel_bwd", "nsa_sel_bwd_workspace_size")
+BWD_EXPORTED = ("nsa_sel_bwd", "nsa_sel_bwd_workspace_size", "nsa_sel_bwd_noalloc")
 TOPK_EXPORTED = ("nsa_topk_blocks",)
 PROBE_EXPORTED = ("nsa_gather_probe",)
 
@@ -69,6 +70,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nsa_sel_bwd_workspace_size.restype = ci
     lib.nsa_sel_bwd.argtypes = [vp] * 11 + [ctypes.c_size_t] + [ci] * 8 + [vp]
     lib.nsa_sel_bwd.restype = ci
+    lib.nsa_sel_bwd_noalloc.argtypes = [vp] * 10 + [ci] * 8 + [vp]
+    lib.nsa_sel_bwd_noalloc.restype = ci
     lib.nsa_topk_blocks.argtypes = [vp, vp] + [ci] * 6 + [vp]
     lib.nsa_topk_blocks.restype = ci
     if path == LIB_PATH:
@@ -212,6 +215,24 @@ def nsa_sel_bwd(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, workspace, works
     """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
     rc = nsa_sel_bwd_raw(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, B, M, N, H, G,
                          D, block_size, T, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def nsa_sel_bwd_noalloc_raw(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, B, M, N, H, G, D, block_size, T,
+                            stream=0) -> int:
+    """Calls the allocation-free C entry point and returns its status code unchanged."""
+    lib = load_library()
+    return lib.nsa_sel_bwd_noalloc(_addr(Q), _addr(K), _addr(V), _addr(block_indices), _addr(O), _addr(LSE),
+                                   _addr(dO), _addr(dQ), _addr(dK), _addr(dV), int(B), int(M), int(N), int(H),
+                                   int(G), int(D), int(block_size), int(T), ctypes.c_void_p(_addr(stream)))
+
+
+def nsa_sel_bwd_noalloc(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, B, M, N, H, G, D, block_size, T,
+                        stream=0) -> None:
+    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
+    rc = nsa_sel_bwd_noalloc_raw(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, B, M, N, H, G, D, block_size, T,
+                                 stream)
     if rc != NSA_SEL_OK:
         raise NsaSelError(rc)
 

@@ -233,6 +233,9 @@ extern "C" const char *nsa_sel_status_string(int status) {
         case NSA_SEL_ERR_HIP: return "nsa_sel: the HIP runtime reported an error at kernel launch";
         case NSA_SEL_ERR_WORKSPACE:
             return "nsa_sel: the backward workspace is NULL, not 256-byte aligned or smaller than required";
+        case NSA_SEL_ERR_SCRATCH:
+            return "nsa_sel: these sizes need more workspace than the 64 MiB scratch of nsa_sel_bwd_noalloc; "
+                   "call nsa_sel_bwd with a workspace";
         default: return "nsa_sel: unknown status";
     }
 }

@@ -34,6 +34,16 @@
 #include "nsa_sel_common.h"
 #include "nsa_sel_bwd.h"
 
+#include <mutex>
+
+// Scratch of the allocation-free entry point (nsa_sel_bwd_noalloc): its
+// workspace lives in this file-scope device array, one copy per GPU, held for
+// the life of the process.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy is looked up once, with that GPU current, and
+// used instead.
+static constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 #include <algorithm>
 
@@ -838,6 +848,24 @@ __global__ __launch_bounds__(256) void nsa_sel_bwd_reduce_kernel(Bw w) {
 }
 
 // ---------------------------------------------------------------------------
+// Device address of this GPU's scratch array, or NULL if the runtime could
+// not give it.  The first call on each device asks the runtime; later calls
+// reuse the stored address.
+void *scratch_address() {
+    static std::mutex mu;
+    static void *addr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = ptr;
+    }
+    return addr[dev];
+}
+
+// ---------------------------------------------------------------------------
 // Host-side planning.
 
 struct BwdPlan {
@@ -930,11 +958,13 @@ extern "C" int nsa_sel_bwd_workspace_size(int B, int M, int N, int H, int G, int
 namespace {
 
 // The backward with its arguments checked against the workspace of
-// workspace_bytes at `workspace`.
+// workspace_bytes at `workspace`.  noalloc: the workspace is the library's own
+// scratch array (a short one is then NSA_SEL_ERR_SCRATCH; it is looked up only
+// after every other check has passed).
 int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_indices, const void *O,
             const float *LSE, const void *dO, float *dQ, float *dK, float *dV, void *workspace,
             size_t workspace_bytes, int B, int M, int N, int H, int G, int D, int block_size, int T,
-            hipStream_t stream) {
+            hipStream_t stream, bool noalloc) {
     if (!Q || !K || !V || !block_indices || !O || !LSE || !dO || !dQ || !dK || !dV) return NSA_SEL_ERR_NULL;
     Params p;
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
@@ -946,6 +976,11 @@ int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_in
          (uintptr_t)dK | (uintptr_t)dV) & 15)
         return NSA_SEL_ERR_ALIGN;
     if (((uintptr_t)block_indices | (uintptr_t)LSE) & 3) return NSA_SEL_ERR_ALIGN;
+    if (noalloc) {
+        if (pl.total > workspace_bytes) return NSA_SEL_ERR_SCRATCH;
+        workspace = scratch_address();
+        if (!workspace) return NSA_SEL_ERR_HIP;
+    }
     if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < pl.total) return NSA_SEL_ERR_WORKSPACE;
 
     const size_t q_bytes = (size_t)B * M * H * D * 2, kv_bytes = (size_t)B * N * G * D * 2;
@@ -1022,6 +1057,13 @@ extern "C" int nsa_sel_bwd(const void *Q, const void *K, const void *V, const in
                            void *workspace, size_t workspace_bytes, int B, int M, int N, int H, int G, int D,
                            int block_size, int T, hipStream_t stream) {
     return sel_bwd(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, workspace, workspace_bytes, B, M, N, H, G, D,
-                   block_size, T, stream);
+                   block_size, T, stream, false);
 }
 
+extern "C" int nsa_sel_bwd_noalloc(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                                   const void *O, const float *LSE, const void *dO, float *dQ, float *dK,
+                                   float *dV, int B, int M, int N, int H, int G, int D, int block_size, int T,
+                                   hipStream_t stream) {
+    return sel_bwd(Q, K, V, block_indices, O, LSE, dO, dQ, dK, dV, nullptr, kScratchBytes, B, M, N, H, G, D,
+                   block_size, T, stream, true);
+}

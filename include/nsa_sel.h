@@ -41,7 +41,8 @@ enum {
     NSA_SEL_ERR_RANGE = 5,       /* B*M*G units or a tensor size beyond the limits  */
     NSA_SEL_ERR_ALIAS = 6,       /* an output buffer overlaps an input or the other */
     NSA_SEL_ERR_HIP = 7,         /* the HIP runtime reported an error at launch     */
-    NSA_SEL_ERR_WORKSPACE = 8    /* workspace NULL, misaligned or too small (bwd)   */
+    NSA_SEL_ERR_WORKSPACE = 8,   /* workspace NULL, misaligned or too small (bwd)   */
+    NSA_SEL_ERR_SCRATCH = 9      /* sizes need more than the fixed scratch (bwd)    */
 };
 
 /*

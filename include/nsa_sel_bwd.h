@@ -81,6 +81,27 @@ int nsa_sel_bwd(const void *Q, const void *K, const void *V, const int32_t *bloc
                 size_t workspace_bytes, int B, int M, int N, int H, int G, int D, int block_size, int T,
                 hipStream_t stream);
 
+/*
+ * nsa_sel_bwd_noalloc -- nsa_sel_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments (minus workspace and workspace_bytes), checks,
+ * status codes and results as nsa_sel_bwd: the two are bitwise equal.  The
+ * workspace is a 64 MiB array inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends; the call allocates nothing
+ * and calls no allocating routine.  Sizes whose workspace
+ * (nsa_sel_bwd_workspace_size) exceeds 64 MiB return NSA_SEL_ERR_SCRATCH
+ * before any HIP call (for example the 8192-query shape with 32 heads in 2
+ * groups, D = 128, block_size 64, T = 16 fits; a 64k-query shape does not).
+ * Every call on a GPU shares that GPU's array and leaves its last contents
+ * there: calls that may overlap on one GPU (different streams, or threads
+ * without ordering) race and must be serialised by the caller.
+ */
+int nsa_sel_bwd_noalloc(const void *Q, const void *K, const void *V, const int32_t *block_indices, const void *O,
+                        const float *LSE, const void *dO, float *dQ, float *dK, float *dV, int B, int M, int N,
+                        int H, int G, int D, int block_size, int T, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,7 +51,7 @@ def test_status_codes_match_header():
 
 
 def test_status_strings(lib):
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = binding.nsa_sel_status_string(code)
         assert isinstance(s, str) and s
     assert binding.nsa_sel_status_string(0) == "ok"
@@ -286,6 +286,40 @@ def test_bwd_null_pointer(lib, which):
 ])
 def test_bwd_rejects_bad_arguments(lib, over, code):
     assert _bwd_call(**over) == code
+
+
+def _noalloc_call(**over):
+    args = dict(GOOD)
+    ptrs = dict(BADDR)
+    for k in list(over):
+        if k in ptrs:
+            ptrs[k] = over.pop(k)
+    args.update(over)
+    return binding.nsa_sel_bwd_noalloc_raw(*(ptrs[k] for k in BNAMES[:-1]), args["B"], args["M"], args["N"],
+                                           args["H"], args["G"], args["D"], args["block_size"], args["T"], 0)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(Q=0), binding.NSA_SEL_ERR_NULL), (dict(dV=0), binding.NSA_SEL_ERR_NULL),
+    (dict(M=0), binding.NSA_SEL_ERR_SHAPE), (dict(D=96), binding.NSA_SEL_ERR_UNSUPPORTED),
+    (dict(L=BADDR["L"] + 2), binding.NSA_SEL_ERR_ALIGN),
+    # sizes whose workspace exceeds the 64 MiB scratch: rejected before any HIP call
+    (dict(B=1, M=65536, N=65536, H=64, G=8, D=128, block_size=64, T=16), binding.NSA_SEL_ERR_SCRATCH),
+    (dict(B=2, M=4096, N=4096, H=64, G=4, D=128, block_size=32, T=32), binding.NSA_SEL_ERR_SCRATCH),
+])
+def test_bwd_noalloc_rejects_bad_arguments(lib, over, code):
+    assert _noalloc_call(**over) == code
+
+
+def test_bwd_noalloc_limit_is_the_documented_64_mib(lib):
+    # The 8192-query workload named in the header fits; its workspace is
+    # within 64 MiB, and one query block more than 64 MiB is refused.
+    n = binding.nsa_sel_bwd_workspace_size(B=1, M=8192, N=8192, H=32, G=2, D=128, block_size=64, T=16)
+    assert n <= 64 << 20
+    assert binding.nsa_sel_bwd_workspace_size(B=1, M=16384, N=16384, H=32, G=2, D=128, block_size=64,
+                                              T=16) > 64 << 20
+    assert _noalloc_call(B=1, M=16384, N=16384, H=32, G=2, D=128, block_size=64, T=16) == \
+        binding.NSA_SEL_ERR_SCRATCH
 
 
 # --- top-k selection (include/nsa_topk.h) ---------------------------------------
