@@ -32,7 +32,7 @@ NSA_SEL_ERR_HIP = 7
 NSA_SEL_ERR_WORKSPACE = 8
 NSA_SEL_ERR_SCRATCH = 9
 
-EXPORTED = ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_status_string")
+EXPORTED = ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_fwd_unpipelined", "nsa_sel_status_string")
 DENSE_EXPORTED = ("nsa_dense_fwd", "nsa_window_fwd", "nsa_window_fwd_bf16")
 BWD_EXPORTED = ("nsa_sel_bwd", "nsa_sel_bwd_workspace_size", "nsa_sel_bwd_noalloc")
 TOPK_EXPORTED = ("nsa_topk_blocks",)
@@ -56,7 +56,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(path)
     vp, ci = ctypes.c_void_p, ctypes.c_int
-    for name in ("nsa_sel_fwd", "nsa_sel_fwd_bf16"):
+    for name in ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_fwd_unpipelined"):
         getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp]
         getattr(lib, name).restype = ci
     lib.nsa_sel_status_string.argtypes = [ci]
@@ -140,6 +140,17 @@ def nsa_sel_fwd(*args, **kwargs):
     if rc != NSA_SEL_OK:
         raise NsaSelError(rc)
     return None
+
+
+def nsa_sel_fwd_unpipelined(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> None:
+    """The verification build of the forward (no copy in flight while LDS is
+    read); same arguments as nsa_sel_fwd; raises NsaSelError on a nonzero status."""
+    lib = load_library()
+    rc = lib.nsa_sel_fwd_unpipelined(_addr(Q), _addr(K), _addr(V), _addr(block_indices), _addr(O), _addr(LSE),
+                                     int(B), int(M), int(N), int(H), int(G), int(D), int(block_size), int(T),
+                                     ctypes.c_void_p(_addr(stream)))
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
 
 
 def nsa_sel_fwd_bf16(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream=0) -> None:

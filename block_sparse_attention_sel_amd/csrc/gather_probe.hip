@@ -15,7 +15,8 @@ namespace {
 // wait for K(s0), read its fragments, issue K(s1); wait for V(s0), read its
 // transposed fragments, issue V(s1).  Returns the number of blocks staged.
 template <int BS, int SPLIT, int D, int PACK, int NT, class Merger>
-__device__ __forceinline__ int probe_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf) {
+__device__ __forceinline__ int probe_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf,
+                                          void *mbuf) {
     constexpr int SBS = BS / SPLIT;
     constexpr int DC = D / 32;
     constexpr int KT = SBS / 16;
@@ -27,7 +28,7 @@ __device__ __forceinline__ int probe_slot(const Params &p, int ws, int lane, _Fl
     Stage<SBS, D> st;
     init_stage(st, p, sl.b, sl.g, lane);
     Merger mg;
-    mg.init(p, sl.b, sl.g, sl.m0, sl.nq, lane);
+    mg.init(p, sl.b, sl.g, sl.m0, sl.nq, lane, mbuf);
 
     half8 kf[KT][DC];
     half4 vt[SBS / 32][DC][2][2];
@@ -73,14 +74,17 @@ __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_gath
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
     __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    // Block maps of the rows of any length (MODE 0 only).
+    __shared__ __attribute__((aligned(16))) unsigned char mbuf_all[MODE == 0 ? WAVES : 1][MODE == 0 ? kMapBlocks : 16];
     const int ws = wave_slot<WAVES>(p, wave);
     if (ws < 0) return;
     int n;
     if constexpr (MODE == 0)
-        n = probe_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+        n = probe_slot<BS, SPLIT, D, PACK, 1, MapMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave],
+                                                                 mbuf_all[wave]);
     else
         n = probe_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, ws, lane, kbuf_all[wave],
-                                                                               vbuf_all[wave]);
+                                                                               vbuf_all[wave], nullptr);
     if (lane == 0) atomicAdd((unsigned long long *)staged, (unsigned long long)n);
 }
 

@@ -41,8 +41,15 @@ namespace {
 // SPLIT > 1 stages and computes each selected block as SPLIT consecutive
 // sub-blocks of SBS = BS / SPLIT keys: half the LDS per wavefront, so twice as
 // many wavefronts fit a CU.
-template <int BS, int SPLIT, int D, int PACK, int NT, class Merger, bool BF16>
-__device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf) {
+//
+// PIPE false is the unpipelined check build: the copies of sub-block s1 are
+// issued only after all of s0's math, and each sub-block waits for every copy,
+// so no copy is ever in flight while the wavefront reads LDS.  It runs the
+// same arithmetic in the same order, so its results are bitwise those of the
+// pipelined kernel unless a pipelined copy overwrote LDS still being read.
+template <int BS, int SPLIT, int D, int PACK, int NT, class Merger, bool BF16, bool PIPE = true>
+__device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Float16 *kbuf, _Float16 *vbuf,
+                                         void *mbuf) {
     constexpr int SBS = BS / SPLIT;
     constexpr int DC = D / 32;
     constexpr int KT = SBS / 16;
@@ -86,7 +93,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
     }
 
     Merger mg;
-    mg.init(p, b, g, m0, nq, lane);
+    mg.init(p, b, g, m0, nq, lane, mbuf);
 
     float m_run[NT], l_run[NT], alpha[NT];
     float4v acc[NT][DC][2];
@@ -131,9 +138,12 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             s1 = t1 == kDone ? kDone : t1 * SPLIT;
         }
         const bool has1 = s1 != kDone;
-        __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K(s0) landed; V(s0) may be pending
+        if constexpr (PIPE)
+            __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // K(s0) landed; V(s0) may be pending
+        else
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
         Stage<SBS, D>::read(kf, kbuf, r, q4);
-        if (has1) st.issue(st.rk, kbuf, s1, lane);
+        if (PIPE && has1) st.issue(st.rk, kbuf, s1, lane);
         const int key0 = s0 * SBS;
         // Raised wave priority while the products and the softmax issue (the
         // copy waits and fragment reads run at the normal one): of the two
@@ -151,12 +161,12 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
                                       p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
         }
         __builtin_amdgcn_s_setprio(0);
-        if (has1)
+        if (PIPE && has1)
             __builtin_amdgcn_s_waitcnt(wait_vm(NI));  // V(s0) landed; K(s1) may be pending
         else
             __builtin_amdgcn_s_waitcnt(wait_vm(0));
         Stage<SBS, D>::read_vt(vt, vbuf, lane);
-        if (has1) st.issue(st.rv, vbuf, s1, lane);
+        if (PIPE && has1) st.issue(st.rv, vbuf, s1, lane);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -164,6 +174,10 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             accumulate_block<SBS, D, BF16>(vt, pf[nt], alpha[nt], acc[nt]);
         }
         __builtin_amdgcn_s_setprio(0);
+        if (!PIPE && has1) {  // all of s0's LDS reads are done: stage s1
+            st.issue(st.rk, kbuf, s1, lane);
+            st.issue(st.rv, vbuf, s1, lane);
+        }
         s0 = s1;
         a0 = a1;
     }
@@ -192,7 +206,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
 
 // MODE 0: rows streamed through cursors (any T), one tile.  MODE 1/2: rows
 // held in registers, NT = MODE tiles.
-template <int BS, int SPLIT, int D, int PACK, int MODE, bool BF16>
+template <int BS, int SPLIT, int D, int PACK, int MODE, bool BF16, bool PIPE>
 __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_fwd_kernel(Params p) {
     constexpr int SBS = BS / SPLIT;
     constexpr int WAVES = waves_per_wg(SBS);
@@ -200,20 +214,23 @@ __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
     __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    // Block maps of the rows of any length (MODE 0 only).
+    __shared__ __attribute__((aligned(16))) unsigned char mbuf_all[MODE == 0 ? WAVES : 1][MODE == 0 ? kMapBlocks : 16];
     const int ws = wave_slot<WAVES>(p, wave);
     if (ws < 0) return;
     if constexpr (MODE == 0)
-        run_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>, BF16>(p, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+        run_slot<BS, SPLIT, D, PACK, 1, MapMerger<PACK, BS>, BF16, PIPE>(p, ws, lane, kbuf_all[wave], vbuf_all[wave],
+                                                                 mbuf_all[wave]);
     else
-        run_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>, BF16>(p, ws, lane, kbuf_all[wave],
-                                                                               vbuf_all[wave]);
+        run_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>, BF16, PIPE>(p, ws, lane, kbuf_all[wave],
+                                                                               vbuf_all[wave], nullptr);
 }
 
-template <bool BF16>
+template <bool BF16, bool PIPE = true>
 struct FwdKernel {
     template <int BS, int SPLIT, int D, int PACK, int MODE>
     void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
-        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE, BF16>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE, BF16, PIPE>), grid, block, 0, stream, p);
     }
 };
 
@@ -243,7 +260,8 @@ extern "C" const char *nsa_sel_status_string(int status) {
 namespace {
 
 int sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices, void *O, float *LSE, int B,
-            int M, int N, int H, int G, int D, int block_size, int T, hipStream_t stream, bool bf16) {
+            int M, int N, int H, int G, int D, int block_size, int T, hipStream_t stream, bool bf16,
+            bool pipelined = true) {
     if (!Q || !K || !V || !block_indices || !O || !LSE) return NSA_SEL_ERR_NULL;
     Params p;
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
@@ -270,8 +288,9 @@ int sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_in
     p.idx = block_indices;
     p.O = (_Float16 *)O;
     p.LSE = LSE;
-    const hipError_t e = bf16 ? launch_all(FwdKernel<true>{}, p, block_size, D, cus, stream)
-                              : launch_all(FwdKernel<false>{}, p, block_size, D, cus, stream);
+    const hipError_t e = !pipelined ? launch_all(FwdKernel<false, false>{}, p, block_size, D, cus, stream)
+                         : bf16     ? launch_all(FwdKernel<true>{}, p, block_size, D, cus, stream)
+                                    : launch_all(FwdKernel<false>{}, p, block_size, D, cus, stream);
     return e == hipSuccess ? NSA_SEL_OK : NSA_SEL_ERR_HIP;
 }
 
@@ -287,4 +306,10 @@ extern "C" int nsa_sel_fwd_bf16(const void *Q, const void *K, const void *V, con
                                 void *O, float *LSE, int B, int M, int N, int H, int G, int D,
                                 int block_size, int T, hipStream_t stream) {
     return sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, true);
+}
+
+extern "C" int nsa_sel_fwd_unpipelined(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                                       void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                                       int block_size, int T, hipStream_t stream) {
+    return sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, false, false);
 }

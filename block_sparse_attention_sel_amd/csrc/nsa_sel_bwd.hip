@@ -121,7 +121,7 @@ __device__ __forceinline__ void dq_grad(const half8 (&vf)[SBS / 16][D / 32], con
 // gradient step in place of the online softmax.
 template <int BS, int SPLIT, int D, int PACK, int NT, class Merger>
 __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws, int lane, _Float16 *kbuf,
-                                        _Float16 *vbuf) {
+                                        _Float16 *vbuf, void *mbuf) {
     constexpr int SBS = BS / SPLIT;
     constexpr int DC = D / 32;
     constexpr int KT = SBS / 16;
@@ -171,7 +171,7 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
     }
 
     Merger mg;
-    mg.init(p, b, g, m0, nq, lane);
+    mg.init(p, b, g, m0, nq, lane, mbuf);
 
     float4v acc[NT][DC][2];
 #pragma unroll
@@ -267,13 +267,16 @@ void nsa_sel_bwd_dq_kernel(Params p, DqArgs x) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
     __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    // Block maps of the rows of any length (MODE 0 only).
+    __shared__ __attribute__((aligned(16))) unsigned char mbuf_all[MODE == 0 ? WAVES : 1][MODE == 0 ? kMapBlocks : 16];
     const int ws = wave_slot<WAVES>(p, wave);
     if (ws < 0) return;
     if constexpr (MODE == 0)
-        dq_slot<BS, SPLIT, D, PACK, 1, CursorMerger<PACK, BS>>(p, x, ws, lane, kbuf_all[wave], vbuf_all[wave]);
+        dq_slot<BS, SPLIT, D, PACK, 1, MapMerger<PACK, BS>>(p, x, ws, lane, kbuf_all[wave], vbuf_all[wave],
+                                                                 mbuf_all[wave]);
     else
         dq_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, x, ws, lane, kbuf_all[wave],
-                                                                        vbuf_all[wave]);
+                                                                        vbuf_all[wave], nullptr);
 }
 
 struct DqKernel {

@@ -29,6 +29,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaveSize = 64;
 // Wavefronts per workgroup: with 32-key stages (16 KiB per wavefront at
@@ -57,88 +58,7 @@ struct Params {
     float scale_log2;   // log2(e) / sqrt(D)
 };
 
-// Scans one index row in chunks of 64 entries: lane j holds entry base + j and
-// a wave ballot marks the counted ones, so finding the next counted entry is
-// scalar bit arithmetic.
-struct IndexScan {
-    const int32_t *row;
-    int T, cm, NB, lane;
-    int base;
-    uint64_t mask;
-    int val;
-
-    __device__ __forceinline__ void load(int b) {
-        base = b;
-        const int j = b + lane;
-        const int v = (j < T) ? __builtin_nontemporal_load(&row[j]) : -1;
-        val = v;
-        const bool ok = v >= 0 && v <= cm && v < NB;
-        mask = __ballot(ok);
-    }
-    // Position of the first counted entry at or after i, or T.
-    __device__ __forceinline__ int next(int i) {
-        while (i < T) {
-            if (i >= base + kWaveSize) load(i);
-            const uint64_t mm = mask >> (i - base);
-            if (mm) return i + __builtin_ctzll(mm);
-            i = base + kWaveSize;
-        }
-        return T;
-    }
-    // Entry at position i; valid while i lies in the loaded chunk.
-    __device__ __forceinline__ int value(int i) const {
-        return __builtin_amdgcn_readlane(val, i - base);
-    }
-};
-
 constexpr int kDone = INT_MAX;
-
-// Walks the counted entries of one index row in row order.
-struct Cursor {
-    IndexScan sc;
-    int pos;
-    int cur;  // block of the current counted entry, or kDone
-
-    __device__ __forceinline__ void init(const int32_t *row, int T, int cm, int NB, int lane, bool live) {
-        sc.row = row;
-        sc.T = live ? T : 0;
-        sc.cm = cm;
-        sc.NB = NB;
-        sc.lane = lane;
-        sc.base = 0;
-        sc.mask = 0;
-        sc.val = -1;
-        if (live) sc.load(0);
-        pos = sc.next(0);
-        cur = pos < sc.T ? sc.value(pos) : kDone;
-    }
-    __device__ __forceinline__ void advance() {
-        pos = sc.next(pos + 1);
-        cur = pos < sc.T ? sc.value(pos) : kDone;
-    }
-};
-
-// Merges the rows of the packed queries: returns the smallest current block
-// and the mask of queries whose current entry is that block (advancing
-// them).  Every counted entry of every row is returned exactly once; rows
-// sorted ascending are swept in ascending block order and a block several
-// rows select at the same time is returned once for all of them.
-template <int PACK>
-__device__ __forceinline__ int merge_next(Cursor (&c)[PACK], unsigned &active) {
-    int t = c[0].cur;
-#pragma unroll
-    for (int k = 1; k < PACK; ++k) t = c[k].cur < t ? c[k].cur : t;
-    active = 0;
-    if (t == kDone) return t;
-#pragma unroll
-    for (int k = 0; k < PACK; ++k) {
-        if (c[k].cur == t) {
-            active |= 1u << k;
-            c[k].advance();
-        }
-    }
-    return t;
-}
 
 // Batched ds_read_b128 of one staged block into MFMA fragments, ending in
 // s_waitcnt lgkmcnt(0).  f[kt][c] comes from address a[c] + kt * 16 rows.
@@ -403,20 +323,97 @@ struct Stage {
 // ascending block order (for any row order) together with the mask of the
 // queries whose rows hold that block.
 
-// Streams each row through an IndexScan; handles any T.
-template <int QW, int BS>
-struct CursorMerger {
-    Cursor c[QW];
+// Any T (rows of any length): a per-wavefront map in LDS with one byte per
+// block, bit k set when query k of the slot selects the block, built for a
+// window of kMapBlocks blocks at a time from every counted entry of the rows
+// and walked in ascending order (a 256-block chunk per step: lane l holds
+// blocks 4l .. 4l+3 of the chunk in one register, a ballot marks the lanes
+// with a block left).  A block that a row repeats, or that several rows
+// select, is returned once, for any row order, as by RegMerger.  The map's
+// LDS accesses are inline assembly so the compiler does not guard them with
+// waits for the direct-to-LDS copies in flight.
+constexpr int kMapBlocks = 2048;  // bytes of LDS per wavefront
 
-    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane) {
+template <int QW, int BS>
+struct MapMerger {
+    static_assert(QW <= 8, "the query mask takes one byte");
+    const int32_t *rows;  // index row of query m0
+    int row_stride;       // elements between consecutive queries' rows (G * T)
+    int T, m0, nq, NB, lane;
+    unsigned base;        // LDS byte address of the map
+    int lo, lim;          // window start; one past the last block any query may select
+    int cb;               // first block of the loaded chunk
+    unsigned word;        // this lane's four blocks of the chunk
+    uint64_t nz;          // lanes with a block left in the chunk
+
+    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0_, int nq_, int lane_, void *lds) {
+        rows = p.idx + ((size_t)(b * (size_t)p.M + m0_) * p.G + g) * p.T;
+        row_stride = p.G * p.T;
+        T = p.T;
+        m0 = m0_;
+        nq = nq_;
+        NB = p.NB;
+        lane = lane_;
+        base = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char *)lds;
+        lim = min(NB, (m0 + nq - 1) / BS + 1);
+        lo = 0;
+        build();
+    }
+    // Map of blocks lo .. lo + kMapBlocks - 1 from every counted entry.
+    __device__ __forceinline__ void build() {
+        const int4v zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < kMapBlocks / (kWaveSize * 16); ++i)
+            asm volatile("ds_write_b128 %0, %1" ::"v"(base + (unsigned)(i * kWaveSize + lane) * 16u), "v"(zero)
+                         : "memory");
 #pragma unroll
         for (int k = 0; k < QW; ++k) {
-            const int mk = m0 + (k < nq ? k : 0);
-            c[k].init(p.idx + ((size_t)(b * (size_t)p.M + mk) * p.G + g) * p.T, p.T, mk / BS, p.NB, lane,
-                      k < nq);
+            if (k >= nq) break;
+            const int32_t *row = rows + (size_t)k * row_stride;
+            const int cm = (m0 + k) / BS;
+            for (int e0 = 0; e0 < T; e0 += kWaveSize) {
+                const int e = e0 + lane;
+                const int t = e < T ? __builtin_nontemporal_load(&row[e]) : -1;
+                const int d = t - lo;
+                if (t >= 0 && t <= cm && t < NB && d >= 0 && d < kMapBlocks) {
+                    const unsigned bits = (1u << k) << (8 * (d & 3));
+                    asm volatile("ds_or_b32 %0, %1" ::"v"(base + (unsigned)(d & ~3)), "v"(bits) : "memory");
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        cb = lo - 4 * kWaveSize;
+        word = 0;
+        nz = 0;
+    }
+    __device__ __forceinline__ int next(unsigned &active) {
+        for (;;) {
+            if (nz) {
+                const int l = __builtin_ctzll(nz);
+                const unsigned w = (unsigned)__builtin_amdgcn_readlane((int)word, l);
+                const int bi = __builtin_ctz(w) >> 3;
+                active = (w >> (8 * bi)) & 0xffu;
+                if (lane == l) word &= ~(0xffu << (8 * bi));
+                nz = __ballot(word != 0u);
+                return cb + 4 * l + bi;
+            }
+            cb += 4 * kWaveSize;
+            if (cb >= lim) {
+                active = 0;
+                return kDone;
+            }
+            if (cb >= lo + kMapBlocks) {  // next window
+                lo += kMapBlocks;
+                build();
+                continue;
+            }
+            asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                         : "=v"(word)
+                         : "v"(base + (unsigned)(cb - lo) + (unsigned)lane * 4u)
+                         : "memory");
+            nz = __ballot(word != 0u);
         }
     }
-    __device__ __forceinline__ int next(unsigned &active) { return merge_next<QW>(c, active); }
 };
 
 // Wave-wide reductions over 64 lanes: DPP prefix within each 16-lane row,
@@ -452,7 +449,7 @@ struct RegMerger {
     static_assert(QW <= 16, "the query index takes 4 bits");
     int e[2];
 
-    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane) {
+    __device__ __forceinline__ void init(const Params &p, int b, int g, int m0, int nq, int lane, void *) {
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
             const int ent = lane + 64 * v;
@@ -775,10 +772,10 @@ int slot_queries(const Params &p) { return p.pack * (p.mode > 0 ? p.mode : 1); }
 template <class F, int BS, int SPLIT, int D, int PACK, int MODE>
 hipError_t launch_generations(const F &f, Params p, int cus, hipStream_t stream) {
     // One generation fills every workgroup slot of every CU: the staging
-    // buffers (K and V, one sub-block each per wavefront) set how many
-    // workgroups fit the CU's 160 KiB of LDS.
+    // buffers (K and V, one sub-block each per wavefront, plus the block map
+    // of MODE 0) set how many workgroups fit the CU's 160 KiB of LDS.
     constexpr int WAVES = waves_per_wg(BS / SPLIT);
-    constexpr int lds_per_wg = 2 * Stage<BS / SPLIT, D>::HALVES * 2 * WAVES;
+    constexpr int lds_per_wg = (2 * Stage<BS / SPLIT, D>::HALVES * 2 + (MODE == 0 ? kMapBlocks : 0)) * WAVES;
     constexpr int by_lds = 160 * 1024 / lds_per_wg;
     constexpr int wg_per_cu = by_lds < 4 ? (by_lds > 0 ? by_lds : 1) : 4;
     const int wg_per_xcd = (cus / kNumXcd > 0 ? cus / kNumXcd : 1) * wg_per_cu;

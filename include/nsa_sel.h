@@ -17,9 +17,9 @@
  * Index entries: an entry t counts when 0 <= t <= m / block_size and
  * t * block_size < N.  Any other value (negative padding such as -1, a block
  * after the query's own block, a block past the end) contributes nothing.
- * Counted entries of one row must be distinct: a repeated block would be
- * weighted twice (outside the contract).  A query with no counted entry gets
- * O = 0 and LSE = -inf.
+ * The selected key set is the union of the counted blocks: a block a row
+ * repeats counts once, for any T and any order of the row.  A query with no
+ * counted entry gets O = 0 and LSE = -inf.
  */
 #ifndef NSA_SEL_H
 #define NSA_SEL_H
@@ -86,6 +86,19 @@ int nsa_sel_fwd(const void *Q, const void *K, const void *V, const int32_t *bloc
 int nsa_sel_fwd_bf16(const void *Q, const void *K, const void *V, const int32_t *block_indices,
                      void *O, float *LSE, int B, int M, int N, int H, int G, int D,
                      int block_size, int T, hipStream_t stream);
+
+/*
+ * nsa_sel_fwd_unpipelined -- verification aid: nsa_sel_fwd (fp16) with the
+ * copy of the next gathered block into LDS issued only after the current
+ * block's math, and every block waiting for all of its copies, so no copy is
+ * in flight while a wavefront reads LDS.  Same arguments, checks and
+ * arithmetic in the same order: its outputs are bitwise those of nsa_sel_fwd,
+ * which is how a copy that overwrote LDS still being read would show.
+ * Slower; not meant for production use.
+ */
+int nsa_sel_fwd_unpipelined(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                            void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                            int block_size, int T, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *nsa_sel_status_string(int status);

@@ -364,3 +364,111 @@ def test_non_default_stream(torch_cuda):
     s.synchronize()
     Or, Lr = oracle.oracle_full(q, k, v, idx, cfg.block_size)
     _check_full(O.cpu().numpy(), L.cpu().numpy(), Or, Lr)
+
+
+def _with_repeats(idx, rng, frac=0.5):
+    """Rows whose padding slots are partly filled with copies of the row's own
+    counted entries, then shuffled; returns (rows with repeats, the same rows
+    with those copies as -1 in the same positions)."""
+    rep = idx.copy()
+    B, M, G, T = idx.shape
+    clean = idx.copy()
+    flat_r = rep.reshape(-1, T)
+    flat_c = clean.reshape(-1, T)
+    for i in range(flat_r.shape[0]):
+        row = flat_r[i]
+        valid = row[row >= 0]
+        pads = np.nonzero(row < 0)[0]
+        if valid.size == 0 or pads.size == 0:
+            continue
+        take = pads[rng.random(pads.size) < frac]
+        row[take] = rng.choice(valid, take.size)
+        perm = rng.permutation(T)
+        flat_r[i] = row[perm]
+        crow = flat_c[i].copy()
+        crow[take] = -1
+        flat_c[i] = crow[perm]
+    return np.ascontiguousarray(rep), np.ascontiguousarray(clean)
+
+
+# Repeated entries count once (the union), on the register merger (T <= 64
+# here) and on the block map (pack * T > 128): parity with the oracle, and
+# bitwise equality with the same rows without the copies at the same T.
+@pytest.mark.parametrize("shape", [
+    (1, 4096, 4096, 64, 8, 128, 64, 16),    # register merger, two tiles
+    (1, 2048, 2048, 16, 1, 64, 32, 40),     # gs = 16, one query per tile: register merger, 80 entries
+    (2, 1024, 1024, 16, 2, 128, 32, 80),    # gs = 8, pack 2: 160 entries -> block map
+    (1, 1500, 1500, 8, 2, 64, 32, 48),      # gs = 4, pack 4: 192 entries -> block map
+])
+def test_repeated_entries_are_bitwise_the_union(torch_cuda, shape):
+    import oracle
+    torch = torch_cuda
+    B, M, N, H, G, D, bs, T = shape
+    _say(f"case repeats shape={shape}")
+    cfg = Config("r", B=B, M=M, N=N, H=H, G=G, D=D, block_size=bs, T=T, seed=sum(shape) + 3)
+    q, k, v, idx = make_inputs(cfg)
+    rep, clean = _with_repeats(idx, np.random.default_rng(sum(shape)))
+    assert (rep != clean).any()
+    O1, L1 = _gpu_run(torch, q, k, v, rep, bs)
+    O2, L2 = _gpu_run(torch, q, k, v, clean, bs)
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    Or, Lr = oracle.oracle_full(q, k, v, rep, bs)
+    assert oracle.oracle_units.last_dup_units > 0
+    _check_full(O1.cpu().numpy(), L1.cpu().numpy(), Or, Lr)
+
+
+# The block map covers 2048 blocks at a time: queries whose causal range
+# reaches past block 2048 build a second window.  Shuffled rows put counted
+# entries of both windows anywhere in the row; units of the last query blocks
+# (the second window) are compared with the oracle.
+def test_block_map_windows(torch_cuda):
+    import oracle
+    torch = torch_cuda
+    cfg = Config("w", B=1, M=66560, N=66560, H=8, G=1, D=64, block_size=32, T=72, seed=31)
+    _say(f"case block-map windows {cfg}")
+    q, k, v, idx = make_inputs(cfg)
+    rng = np.random.default_rng(31)
+    tail = slice(cfg.M - 3 * cfg.block_size, cfg.M)
+    rows = idx[0, tail, 0].copy()
+    for i in range(rows.shape[0]):        # some entries in the second window, shuffled rows
+        c = (cfg.M - 3 * cfg.block_size + i) // cfg.block_size
+        free = np.nonzero(rows[i] < 0)[0]
+        extra = rng.choice(np.arange(2048, c), min(free.size, 6), replace=False)
+        rows[i, free[:extra.size]] = extra
+        rows[i] = rows[i][rng.permutation(cfg.T)]
+    idx = idx.copy()
+    idx[0, tail, 0] = rows
+    O, L = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    units = sample_units(cfg, 1024, tail=3)
+    Or, Lr = oracle.oracle_units(q, k, v, idx, cfg.block_size, units)
+    ub = torch.from_numpy(units).to("cuda")
+    heads = ub[:, 2:3] * cfg.gs + torch.arange(cfg.gs, device="cuda")[None, :]
+    Og = O[ub[:, 0:1], ub[:, 1:2], heads].float().cpu().numpy()
+    Lg = L[ub[:, 0:1], heads, ub[:, 1:2]].cpu().numpy()
+    _check_full(Og, Lg, Or, Lr)
+
+
+# Race check: the unpipelined build (no copy in flight while LDS is read)
+# runs the same arithmetic in the same order, so any difference from the
+# pipelined kernel is a copy that overwrote LDS still being read.
+@pytest.mark.parametrize("name", ["64k@4096", "32k-bs32@2048", "8k-dense@2048", "tiny"])
+def test_pipelined_matches_unpipelined_bitwise(torch_cuda, name):
+    torch = torch_cuda
+    from block_sparse_attention_sel_amd.binding import nsa_sel_fwd_unpipelined
+    base, _, size = name.partition("@")
+    if base == "8k-dense":
+        cfg = CONFIGS["8k"].with_(M=int(size), N=int(size)).dense()
+    elif size:
+        cfg = CONFIGS[base].with_(M=int(size), N=int(size))
+    else:
+        cfg = CONFIGS[base]
+    _say(f"case unpipelined {cfg}")
+    q, k, v, idx = make_inputs(cfg)
+    O1, L1 = _gpu_run(torch, q, k, v, idx, cfg.block_size)
+    tq, tk, tv, ti = _to_dev(torch, q, k, v, idx)
+    O2 = torch.full_like(O1, float("nan"))
+    L2 = torch.full_like(L1, float("nan"))
+    nsa_sel_fwd_unpipelined(tq, tk, tv, ti, O2, L2, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size,
+                            cfg.T, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
