@@ -108,8 +108,9 @@ extern "C" int nsa_gather_probe(const void *K, const void *V, const int32_t *blo
     if (((uintptr_t)K | (uintptr_t)V) & 15) return NSA_SEL_ERR_ALIGN;
     if ((uintptr_t)block_indices & 3) return NSA_SEL_ERR_ALIGN;
     if ((uintptr_t)staged & 7) return NSA_SEL_ERR_ALIGN;
-    const int cus = device_cus();
-    plan_slots(p, cus);
+    const Topology tp = device_topology();
+    const int cus = tp.cus;
+    plan_slots(p, tp);
     if (queries_per_slot) *queries_per_slot = slot_queries(p);
     p.Q = nullptr;
     p.K = (const _Float16 *)K;

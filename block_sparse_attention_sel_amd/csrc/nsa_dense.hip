@@ -53,7 +53,8 @@ struct DenseParams {
     int B, M, N, H, G, gs;
     int qtiles;   // query tiles per (b, g)
     int units;    // B * G * qtiles
-    int per_xcd;  // ceil(units / 8)
+    int per_xcd;  // ceil(units / nxcd)
+    int nxcd;     // XCDs workgroups are dealt to (w % nxcd)
     int left, right;  // window: keys m - left .. m + right visible (negative = unbounded)
     float scale_log2;
 };
@@ -141,7 +142,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
 
     const int lane = threadIdx.x & (kWaveSize - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int unit = (blockIdx.x % kNumXcd) * p.per_xcd + (int)(blockIdx.x / kNumXcd);
+    const int unit = (blockIdx.x % p.nxcd) * p.per_xcd + (int)(blockIdx.x / p.nxcd);
     if (unit >= p.units) return;  // the whole workgroup
     const int bg = unit / p.qtiles;
     const int qt = p.qtiles - 1 - (unit - bg * p.qtiles);  // longest tiles first
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
 
 template <int D, int PACK, bool BF16>
 hipError_t launch_dense(const DenseParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((nsa_dense_kernel<D, PACK, BF16>), dim3(p.per_xcd * kNumXcd), dim3(kWaveSize * kDenseWaves),
+    hipLaunchKernelGGL((nsa_dense_kernel<D, PACK, BF16>), dim3(p.per_xcd * p.nxcd), dim3(kWaveSize * kDenseWaves),
                        0, stream, p);
     return hipGetLastError();
 }
@@ -422,7 +423,8 @@ int window_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
     p.B = B; p.M = M; p.N = N; p.H = H; p.G = G; p.gs = gs;
     p.qtiles = (M + qwg - 1) / qwg;
     p.units = B * G * p.qtiles;
-    p.per_xcd = (p.units + kNumXcd - 1) / kNumXcd;
+    p.nxcd = device_topology().nxcd;
+    p.per_xcd = (p.units + p.nxcd - 1) / p.nxcd;
     // A bound that reaches past every query (left >= M) or every key
     // (right >= N) is the same as none.
     p.left = (left < 0 || left >= M) ? -1 : left;

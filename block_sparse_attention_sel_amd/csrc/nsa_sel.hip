@@ -280,8 +280,9 @@ int sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_in
     }
     if (ranges_overlap(O, q_bytes, LSE, lse_bytes)) return NSA_SEL_ERR_ALIAS;
 
-    const int cus = device_cus();
-    plan_slots(p, cus);
+    const Topology tp = device_topology();
+    const int cus = tp.cus;
+    plan_slots(p, tp);
     p.Q = (const _Float16 *)Q;
     p.K = (const _Float16 *)K;
     p.V = (const _Float16 *)V;

@@ -328,6 +328,7 @@ struct Bw {
     float *dK, *dV;
     int B, M, N, H, G, gs, T, bs, NB, MW, R, qc, kmax, cap, pcap, qpt;
     int sentinel;       // B*H*M
+    int nxcd;           // XCDs of the device (grid rounding)
     float scale, scale_log2;
 };
 
@@ -936,8 +937,8 @@ hipError_t launch_key_passes(const Bw &w, const BwdPlan &pl, hipStream_t stream)
     hipLaunchKernelGGL(nsa_sel_bwd_bitmap_kernel, dim3(w.B * w.G * chunks), dim3(kBitQ), 0, stream, w);
     hipLaunchKernelGGL(nsa_sel_bwd_count_kernel, dim3((w.R + 3) / 4), dim3(256), 0, stream, w);
     hipLaunchKernelGGL(nsa_sel_bwd_scan_kernel, dim3(1), dim3(1024), 0, stream, w);
-    const int per_xcd = (int)((pl.cap + kNumXcd - 1) / kNumXcd);
-    hipLaunchKernelGGL((nsa_sel_bwd_dkv_kernel<BS, D>), dim3(per_xcd * kNumXcd), dim3(kWaveSize * (BS / 16)), 0,
+    const int per_xcd = (int)((pl.cap + w.nxcd - 1) / w.nxcd);
+    hipLaunchKernelGGL((nsa_sel_bwd_dkv_kernel<BS, D>), dim3(per_xcd * w.nxcd), dim3(kWaveSize * (BS / 16)), 0,
                        stream, w);
     hipLaunchKernelGGL((nsa_sel_bwd_reduce_kernel<BS, D>), dim3(w.R), dim3(256), 0, stream, w);
     return hipGetLastError();
@@ -999,8 +1000,9 @@ int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_in
             if (ranges_overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return NSA_SEL_ERR_ALIAS;
     }
 
-    const int cus = device_cus();
-    plan_slots(p, cus);
+    const Topology tp = device_topology();
+    const int cus = tp.cus;
+    plan_slots(p, tp);
     p.Q = (const _Float16 *)Q;
     p.K = (const _Float16 *)K;
     p.V = (const _Float16 *)V;
@@ -1037,6 +1039,7 @@ int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_in
     w.B = B; w.M = M; w.N = N; w.H = H; w.G = G; w.gs = p.gs; w.T = T; w.bs = block_size;
     w.NB = pl.NB; w.MW = pl.MW; w.R = pl.R; w.qc = pl.qc; w.kmax = pl.kmax; w.cap = (int)pl.cap; w.pcap = (int)pl.pcap; w.qpt = pl.qpt;
     w.sentinel = B * H * M;
+    w.nxcd = tp.nxcd;
     w.scale = 1.0f / sqrtf((float)D);
     w.scale_log2 = p.scale_log2;
 

@@ -36,7 +36,6 @@ constexpr int kWaveSize = 64;
 // D = 128) two 4-wavefront workgroups share a CU, two wavefronts per SIMD;
 // with 64-key stages five wavefronts fill the CU's 160 KiB of LDS.
 constexpr int waves_per_wg(int sbs) { return sbs == 32 ? 4 : 5; }
-constexpr int kNumXcd = 8;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -55,6 +54,7 @@ struct Params {
     int per_xcd;        // wavefront slots owned by each XCD: ceil(wslots / 8)
     int gen_step;       // wavefront slots one XCD runs per launch (its workgroup slots x waves)
     int gen;            // generation (launch) index
+    int nxcd;           // XCDs workgroups are dealt to (w % nxcd); 1 = one contiguous range
     float scale_log2;   // log2(e) / sqrt(D)
 };
 
@@ -663,13 +663,13 @@ __device__ __forceinline__ Slot decode_slot(const Params &p, int ws, int qw) {
 }
 
 // Wavefront slot of wavefront `wave` of this workgroup in generation p.gen,
-// or -1.  XCD w % 8 runs the next gen_step slots of its contiguous range, so
-// one generation fills every workgroup slot of every CU.
+// or -1.  XCD w % nxcd runs the next gen_step slots of its contiguous range,
+// so one generation fills every workgroup slot of every CU.
 template <int WAVES>
 __device__ __forceinline__ int wave_slot(const Params &p, int wave) {
     const int w = blockIdx.x;
-    const int loc = p.gen * p.gen_step + (w / kNumXcd) * WAVES + wave;
-    const int ws = (w % kNumXcd) * p.per_xcd + loc;
+    const int loc = p.gen * p.gen_step + (w / p.nxcd) * WAVES + wave;
+    const int ws = (w % p.nxcd) * p.per_xcd + loc;
     return (loc >= p.per_xcd || ws >= p.wslots) ? -1 : ws;
 }
 
@@ -695,19 +695,31 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// Compute units of the current device, cached per device (the first call on a
-// device asks the runtime; a failed query falls back to 256).
-int device_cus() {
-    static std::atomic<int> cached[64];
+// Compute units and XCDs of the current device, cached per device (the first
+// call on a device asks the runtime).  The launch plans deal workgroup w to
+// XCD w % nxcd, the order in which the hardware spreads a grid over the XCDs
+// of a device that is not partitioned; an XCD count the runtime does not give,
+// or one that does not divide the CUs evenly, falls back to nxcd = 1 (one
+// contiguous range of work: correct everywhere, without the L2 locality).  A
+// failed CU query falls back to 256.
+struct Topology {
+    int cus, nxcd;
+};
+Topology device_topology() {
+    static std::atomic<int> cached_cus[64], cached_xcd[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n <= 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev].store(n, std::memory_order_relaxed);
+    Topology t{cached_cus[dev].load(std::memory_order_relaxed), cached_xcd[dev].load(std::memory_order_relaxed)};
+    if (t.cus <= 0 || t.nxcd <= 0) {
+        if (hipDeviceGetAttribute(&t.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || t.cus <= 0)
+            t.cus = 256;
+        if (hipDeviceGetAttribute(&t.nxcd, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || t.nxcd < 1 ||
+            t.nxcd > 64 || t.cus % t.nxcd != 0)
+            t.nxcd = 1;
+        cached_cus[dev].store(t.cus, std::memory_order_relaxed);
+        cached_xcd[dev].store(t.nxcd, std::memory_order_relaxed);
     }
-    return n;
+    return t;
 }
 
 
@@ -732,6 +744,7 @@ int check_sizes(int B, int M, int N, int H, int G, int D, int block_size, int T,
     p.scale_log2 = kLog2e / sqrtf((float)D);
     p.gen = 0;
     p.gen_step = 0;
+    p.nxcd = 1;
     return NSA_SEL_OK;
 }
 
@@ -742,7 +755,9 @@ int check_sizes(int B, int M, int N, int H, int G, int D, int block_size, int T,
 // wavefront slots.  Two tiles keep a wavefront within 256 registers, so two
 // wavefronts share each SIMD.
 // max_mode caps the tiles per wavefront.
-void plan_slots(Params &p, int cus, int max_mode = 2) {
+void plan_slots(Params &p, const Topology &tp, int max_mode = 2) {
+    const int cus = tp.cus;
+    p.nxcd = tp.nxcd;
     int mode = 0;
     for (int nt = max_mode; nt >= 1; nt /= 2) {
         if ((int64_t)p.pack * nt * p.T <= 128) {
@@ -757,7 +772,7 @@ void plan_slots(Params &p, int cus, int max_mode = 2) {
     p.mode = mode;
     p.wslots_per_bg = (int)wslots_per_bg;
     p.wslots = (int)wslots;
-    p.per_xcd = (int)((wslots + kNumXcd - 1) / kNumXcd);
+    p.per_xcd = (int)((wslots + p.nxcd - 1) / p.nxcd);
 }
 
 // Queries per wavefront slot of a planned launch.
@@ -778,12 +793,12 @@ hipError_t launch_generations(const F &f, Params p, int cus, hipStream_t stream)
     constexpr int lds_per_wg = (2 * Stage<BS / SPLIT, D>::HALVES * 2 + (MODE == 0 ? kMapBlocks : 0)) * WAVES;
     constexpr int by_lds = 160 * 1024 / lds_per_wg;
     constexpr int wg_per_cu = by_lds < 4 ? (by_lds > 0 ? by_lds : 1) : 4;
-    const int wg_per_xcd = (cus / kNumXcd > 0 ? cus / kNumXcd : 1) * wg_per_cu;
+    const int wg_per_xcd = (cus / p.nxcd > 0 ? cus / p.nxcd : 1) * wg_per_cu;
     p.gen_step = wg_per_xcd * WAVES;
     const int gens = (p.per_xcd + p.gen_step - 1) / p.gen_step;
     for (int g = 0; g < gens; ++g) {
         p.gen = g;
-        f.template launch<BS, SPLIT, D, PACK, MODE>(dim3(wg_per_xcd * kNumXcd), dim3(kWaveSize * WAVES), stream,
+        f.template launch<BS, SPLIT, D, PACK, MODE>(dim3(wg_per_xcd * p.nxcd), dim3(kWaveSize * WAVES), stream,
                                                     p);
     }
     return hipGetLastError();
