@@ -20,7 +20,6 @@ SRC = os.path.join(CSRC, "nsa_sel.hip")
 DENSE_SRC = os.path.join(CSRC, "nsa_dense.hip")
 BWD_SRC = os.path.join(CSRC, "nsa_sel_bwd.hip")
 TOPK_SRC = os.path.join(CSRC, "nsa_topk.hip")
-STREAM_SRC = os.path.join(CSRC, "nsa_sel_stream.hip")
 LIB = os.path.join(PKG, "libnsa_sel.so")
 PROBE_SRC = os.path.join(CSRC, "gather_probe.hip")
 PROBE_LIB = os.path.join(PKG, "libnsa_gather_probe.so")
@@ -40,7 +39,7 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(extra_flags=(), out: str = LIB, srcs=(SRC, DENSE_SRC, BWD_SRC, TOPK_SRC, STREAM_SRC)) -> str:
+def build(extra_flags=(), out: str = LIB, srcs=(SRC, DENSE_SRC, BWD_SRC, TOPK_SRC)) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = out + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
