@@ -176,6 +176,17 @@ def test_bwd_32k_bs32_sampled(torch_cuda):
     _sampled(torch_cuda, cfg, 200, [(1, 3, cfg.NB - 1), (0, 1, 900)])
 
 
+@pytest.mark.timeout(900)
+def test_bwd_8k_every_element(torch_cuda):
+    """dQ, dK and dV of the 8k workload (M = N = 8192, H = 32, G = 2, D = 128),
+    every element against the oracle's whole-tensor backward."""
+    cfg = CONFIGS["8k"]
+    _say(f"case {cfg} (every element)")
+    q, k, v, idx = make_inputs(cfg)
+    do = make_grad_output(cfg)
+    _full(torch_cuda, q, k, v, idx, do, cfg.block_size)
+
+
 def test_bwd_128k_local_sampled(torch_cuda):
     cfg = CONFIGS["128k-local"]
     _sampled(torch_cuda, cfg, 200, [(0, 5, cfg.NB - 1), (0, 2, 1000)])

@@ -128,3 +128,29 @@ def test_dense_repeat_runs_are_bitwise_identical(torch_cuda):
     O1, L1 = _run(torch_cuda, q, k, v)
     O2, L2 = _run(torch_cuda, q, k, v)
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["8k", "16k"])
+def test_dense_every_unit(torch_cuda, name):
+    """Every unit against the oracle, streamed in unit ranges: the 8k
+    workload's shape (M = N = 8192, H = 32, G = 2, D = 128) and M = N = 16384
+    with the 64k workload's heads (H = 64, G = 8, D = 128)."""
+    import os
+    import time
+
+    import oracle
+    cfg = CONFIGS["8k"] if name == "8k" else CONFIGS["64k"].with_(M=16384, N=16384)
+    _say(f"case dense {cfg} (every unit)")
+    q, k, v = _qkv(cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, seed=cfg.seed)
+    O, L = _run(torch_cuda, q, k, v)
+    threads = max(1, min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))))
+    U = cfg.B * cfg.M * cfg.G
+    t0 = time.perf_counter()
+    for i in range(4):
+        u0, u1 = U * i // 4, U * (i + 1) // 4
+        r = oracle.compare(q, k, v, None, cfg.block_size, O, L, u0, u1, threads)
+        _say(f"  units {u0}..{u1 - 1}: max|dO| = {r['max_err_O']:.3e}  max|dLSE| = {r['max_err_LSE']:.3e}"
+             f"  {time.perf_counter() - t0:.1f} s")
+        assert r["units"] == u1 - u0 and r["bad_rows"] == 0 and r["empty_rows"] == 0
+        assert r["max_err_O"] <= O_TOL and r["max_err_LSE"] <= LSE_TOL

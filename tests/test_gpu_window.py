@@ -195,3 +195,68 @@ def test_selection_bf16_matches_fp16_path_structure(torch_cuda):
     torch.cuda.synchronize()
     assert torch.allclose(L16, Lbf, atol=1e-4, rtol=0)
     assert (O16.float() - Obf.float()).abs().max().item() <= 2.0 ** -8 * (1 + O16.float().abs().max().item())
+
+
+def _oracle_threads() -> int:
+    import os
+    n = os.cpu_count() or 1
+    return max(1, min(n, int(os.environ.get("OMP_NUM_THREADS", n))))
+
+
+def _every_unit(torch, q, k, v, idx, bs, O, L, dtype, window=None, chunks=4):
+    """Compares every (b, m, g) unit of a GPU result with the oracle, streamed
+    in unit ranges.  The bf16 O bound takes max|O| from the GPU output: it
+    differs from the reference's by at most the error being bounded."""
+    import time
+
+    import oracle
+    if dtype == "bf16":
+        On = O.view(torch.int16).cpu().numpy().view(np.uint16)
+        otol = 1.25 * 2.0 ** -9 * (np.abs(_bf16_values(v)).max() + O.float().abs().max().item())
+    else:
+        On = O.cpu().numpy()
+        otol = O_TOL
+    Ln = L.cpu().numpy()
+    B, M, _, _ = q.shape
+    G = k.shape[2]
+    U = B * M * G
+    t0 = time.perf_counter()
+    for i in range(chunks):
+        u0, u1 = U * i // chunks, U * (i + 1) // chunks
+        r = oracle.compare(q, k, v, idx, bs, On, Ln, u0, u1, _oracle_threads(), dtype=dtype, window=window)
+        _say(f"  units {u0}..{u1 - 1}: max|dO| = {r['max_err_O']:.3e} (bound {otol:.3e}, unit {r['worst_unit_O']})"
+             f"  max|dLSE| = {r['max_err_LSE']:.3e}  bad rows {r['bad_rows']}  empty rows {r['empty_rows']}"
+             f"  {time.perf_counter() - t0:.1f} s")
+        assert r["units"] == u1 - u0 and r["bad_rows"] == 0
+        assert r["max_err_O"] <= otol and r["max_err_LSE"] <= LSE_TOL
+
+
+@pytest.mark.timeout(900)
+def test_selection_bf16_64k_every_unit(torch_cuda):
+    """The bf16 selection forward at the 64k workload's full size, every unit."""
+    torch = torch_cuda
+    from block_sparse_attention_sel_amd.binding import sel_attn_fwd
+    cfg = CONFIGS["64k"]
+    _say(f"case {cfg} bf16 (every unit)")
+    q, k, v, idx = make_inputs_bf16(cfg)
+    O, L = sel_attn_fwd(_dev(torch, q), _dev(torch, k), _dev(torch, v), _dev(torch, idx), cfg.block_size)
+    torch.cuda.synchronize()
+    _every_unit(torch, q, k, v, idx, cfg.block_size, O, L, "bf16", chunks=8)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("case", [("64k", (512, 0), "fp16"), ("64k", (512, 0), "bf16"),
+                                  ("16k", (8192, 0), "fp16")])
+def test_window_every_unit(torch_cuda, case):
+    """Every unit of the FlyDSL page's head layout (H=64, H_KV=8, D=128) with a
+    512 window at sequence 65536, and with an 8192 window at 16384 (the window
+    filling up over the first 8192 queries, then sliding)."""
+    torch = torch_cuda
+    from block_sparse_attention_sel_amd.binding import window_attn_fwd
+    size, window, dtype = case
+    cfg = CONFIGS["64k"] if size == "64k" else CONFIGS["64k"].with_(M=16384, N=16384)
+    _say(f"case {cfg} window {window} {dtype} (every unit)")
+    q, k, v, _ = (make_inputs_bf16 if dtype == "bf16" else make_inputs)(cfg)
+    O, L = window_attn_fwd(_dev(torch, q), _dev(torch, k), _dev(torch, v), *window)
+    torch.cuda.synchronize()
+    _every_unit(torch, q, k, v, None, 1, O, L, dtype, window=window, chunks=8)
