@@ -59,18 +59,6 @@ struct DenseParams {
     float scale_log2;
 };
 
-// S^T = K Q^T of one 16-column tile over a staged sub-block (no masking).
-template <int SBS, int D, bool BF16>
-__device__ __forceinline__ void qk_tile(const half8 (&kf)[SBS / 16][D / 32], const half8 (&qf)[D / 32],
-                                        float4v (&s)[SBS / 16]) {
-#pragma unroll
-    for (int kt = 0; kt < SBS / 16; ++kt) {
-        s[kt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < D / 32; ++c) s[kt] = mfma16<BF16>(kf[kt][c], qf[c], s[kt]);
-    }
-}
-
 // The softmax step of score_block for a sub-block that no column masks and
 // every column takes: the same arithmetic, on scores computed beforehand, so
 // that one tile's softmax can be scheduled beside another tile's MFMAs.
@@ -98,6 +86,52 @@ __device__ __forceinline__ void softmax_open(const float4v (&s)[KT], float scale
         pf[kt] = pack4<BF16>(pv);
     }
     l_run = l_run * alpha + psum;
+}
+
+// softmax_open over a wavefront's NT tiles behind one wave-uniform test:
+// when no lane's scaled scores exceed their column's running max by more
+// than kLazyMax, every tile keeps its running max (alpha = 1) and P follows
+// without the column reductions; otherwise (and on the first sub-block, where
+// the running max is -inf) each tile takes softmax_open's full step.  Where
+// the running max is kept both give the same P.
+template <int NT, int KT, bool BF16>
+__device__ __forceinline__ void softmax_open_tiles(const float4v (&s)[NT][KT], float scale_log2, float (&m_run)[NT],
+                                                   float (&l_run)[NT], float (&alpha)[NT], half4 (&pf)[NT][KT]) {
+    float x[NT][KT][4];
+    bool raise = false;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        float xmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[nt][kt][i] = __builtin_fmaf(s[nt][kt][i], scale_log2, -m_run[nt]);
+            xmax = fmaxf(xmax, fmaxf(fmaxf(x[nt][kt][0], x[nt][kt][1]), fmaxf(x[nt][kt][2], x[nt][kt][3])));
+        }
+        raise = raise || xmax > kLazyMax || m_run[nt] == -INFINITY;
+    }
+    if (!__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float part[KT];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                float4v pv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(x[nt][kt][i]);
+                part[kt] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+                pf[nt][kt] = pack4<BF16>(pv);
+            }
+            float psum = part[0];
+#pragma unroll
+            for (int kt = 1; kt < KT; ++kt) psum += part[kt];
+            alpha[nt] = 1.f;
+            l_run[nt] += psum;
+        }
+        return;
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) softmax_open<KT, BF16>(s[nt], scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt]);
 }
 
 // accumulate_block split in two, so that the (rare) rescale branch can sit
@@ -303,9 +337,7 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
         Stage<SBS, D>::read(kf, kbuf[s % kStages], r, q4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) qk_tile<SBS, D, BF16>(kf, qf[nt], sc[nt]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            softmax_open<KT, BF16>(sc[nt], p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt]);
+        softmax_open_tiles<NT, KT, BF16>(sc, p.scale_log2, m_run, l_run, alpha, pf);
         for (;;) {
             // V^T of s before the group barrier that may come with s + 1 (it
             // frees the half of the ring that holds s).
@@ -338,7 +370,10 @@ __global__ __launch_bounds__(kWaveSize * kDenseWaves) void nsa_dense_kernel(Dens
             for (int nt = 0; nt < NT; ++nt) {
                 m1[nt] = m_run[nt];
                 l1[nt] = l_run[nt];
-                softmax_open<KT, BF16>(sc[nt], p.scale_log2, m1[nt], l1[nt], a1[nt], pn[nt]);
+            }
+            softmax_open_tiles<NT, KT, BF16>(sc, p.scale_log2, m1, l1, a1, pn);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
                 m_run[nt] = next ? m1[nt] : m_run[nt];
                 l_run[nt] = next ? l1[nt] : l_run[nt];
                 alpha[nt] = next ? a1[nt] : 1.f;

@@ -551,10 +551,23 @@ __device__ __forceinline__ float col_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Scores of one gathered block folded into the running softmax state:
-// S^T = K * Q^T (lane l: keys key0 + 16*kt + 4*(l/16) + i, column l%16), then
-// the running max, the rescale factor of the accumulator and the block's
+// S^T = K Q^T of one 16-column tile over a staged sub-block: lane l holds
+// keys 16*kt + 4*(l/16) + i of column l%16.
+template <int SBS, int D, bool BF16>
+__device__ __forceinline__ void qk_tile(const half8 (&kf)[SBS / 16][D / 32], const half8 (&qf)[D / 32],
+                                        float4v (&s)[SBS / 16]) {
+#pragma unroll
+    for (int kt = 0; kt < SBS / 16; ++kt) {
+        s[kt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) s[kt] = mfma16<BF16>(kf[kt][c], qf[c], s[kt]);
+    }
+}
+
+// Scores of one gathered block folded into the running softmax state: the
+// running max, the rescale factor of the accumulator and the block's
 // probabilities P^T (fp16), all in the log2 domain (x * log2(e) / sqrt(D)).
+// s holds S^T from qk_tile (keys key0 + 16*kt + 4*q4 + i) and is overwritten.
 //
 // causal: the block reaches past the smallest packed query or past N (or,
 //   for a sliding window, before some column's first visible key), so keys
@@ -565,23 +578,19 @@ __device__ __forceinline__ float col_sum(float x) {
 //   (col_on false) the running state is left unchanged and P is zero.
 // The running max is only raised when a block's max exceeds it by more than
 // kLazyMax (P then stays below 2^kLazyMax, well inside fp16), so most blocks
-// need no rescale of the accumulator (alpha == 1 exactly).
+// need no rescale of the accumulator (alpha == 1 exactly).  That is tested
+// first, lane by lane, against each column's running max: when no lane's
+// scaled scores exceed it by more than kLazyMax (a wave-uniform test), P
+// follows with the running max as it stands and no reduction over a column.
+// Otherwise -- and on a column's first block, where the running max is -inf
+// -- the step takes each column's block max over its four lanes.  Both ways
+// give the same P wherever the running max is kept.
 constexpr float kLazyMax = 8.0f;
 
-template <int BS, int D, bool BF16 = false>
-__device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
-                                            int key0, bool causal, bool col_mask, bool col_on, int lo, int lim,
-                                            float scale_log2, float &m_run, float &l_run,
-                                            float &alpha, half4 (&pf)[BS / 16], int q4) {
-    constexpr int KT = BS / 16;
-    constexpr int DC = D / 32;
-    float4v s[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-        s[kt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < DC; ++c) s[kt] = mfma16<BF16>(kf[kt][c], qf[c], s[kt]);
-    }
+template <int KT, bool BF16 = false>
+__device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool causal, bool col_mask, bool col_on,
+                                             int lo, int lim, float scale_log2, float &m_run, float &l_run,
+                                             float &alpha, half4 (&pf)[KT], int q4) {
     if (causal) {
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
@@ -591,6 +600,34 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
                 if (key > lim || key < lo) s[kt][i] = -INFINITY;
             }
     }
+    const bool off = col_mask && !col_on;
+    {
+        const float m_keep = off ? INFINITY : m_run;
+        float x[KT][4];
+        float xmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[kt][i] = __builtin_fmaf(s[kt][i], scale_log2, -m_keep);
+            xmax = fmaxf(xmax, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
+        }
+        if (!__builtin_amdgcn_ballot_w64(xmax > kLazyMax || m_keep == -INFINITY)) {
+            float psum = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                float4v pv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pv[i] = fast_exp2(x[kt][i]);
+                    psum += pv[i];
+                }
+                pf[kt] = pack4<BF16>(pv);
+            }
+            alpha = 1.f;
+            l_run += psum;
+            return;
+        }
+    }
     // Row max of the raw scores (the scale is positive), then over the 4
     // lanes (l, l^16, l^32, l^48) that share a column.
     float mloc = -INFINITY;
@@ -599,7 +636,6 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
     mloc = col_max(mloc);
     const float m_blk = mloc * scale_log2;
     float m_new = (m_blk > m_run + kLazyMax) ? m_blk : m_run;
-    const bool off = col_mask && !col_on;
     if (off) m_new = m_run;
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_use);
@@ -618,6 +654,17 @@ __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], 
         pf[kt] = pack4<BF16>(pv);
     }
     l_run = l_run * alpha + psum;  // per-lane partial; lanes are summed at the end
+}
+
+// qk_tile and softmax_tile in one step.
+template <int BS, int D, bool BF16 = false>
+__device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
+                                            int key0, bool causal, bool col_mask, bool col_on, int lo, int lim,
+                                            float scale_log2, float &m_run, float &l_run,
+                                            float &alpha, half4 (&pf)[BS / 16], int q4) {
+    float4v s[BS / 16];
+    qk_tile<BS, D, BF16>(kf, qf, s);
+    softmax_tile<BS / 16, BF16>(s, key0, causal, col_mask, col_on, lo, lim, scale_log2, m_run, l_run, alpha, pf, q4);
 }
 
 // O^T = alpha * O^T + V^T * P^T over 32-key chunks.  acc[c][hh] holds O^T rows
