@@ -827,27 +827,60 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
 }
 
 // Key blocks with no item get zeros; those with several items the sum of
-// their partials in item order.  One workgroup per key block row.
+// their partials in item order.  kReduceSlices workgroups per key block row
+// (grid y), each thread holding EPT float4 sums whose loads for one partial
+// (and the next) are issued together, so a thread keeps 2 * EPT loads in
+// flight instead of one.  The order of the additions is that of the items, so the
+// result does not depend on the launch shape.
+constexpr int kReduceSlices = 4;
+
 template <int BS, int D>
 __global__ __launch_bounds__(256) void nsa_sel_bwd_reduce_kernel(Bw w) {
     const int row = blockIdx.x;
+    const int slice = blockIdx.y;
     const int n = w.row_items[row];
     if (n == 1) return;
     const int bg = row / w.NB, t = row - bg * w.NB;
     const int b = bg / w.G, g = bg - b * w.G;
     const int p0 = n >= 2 ? w.row_part[row] : 0;
     if (p0 + n > w.pcap) return;  // the plan bounds the partial slots; the scan flags an overflow
-    constexpr int V4 = BS * D / 4;  // float4 per tensor
-    for (int e = threadIdx.x; e < 2 * V4; e += 256) {
-        const int tensor = e / V4, f = e - tensor * V4;
+    constexpr int V4 = BS * D / 4;  // float4 per tensor; a partial holds dK then dV
+    constexpr int EPT = 2 * V4 / (kReduceSlices * 256);
+    static_assert(EPT >= 1 && (2 * V4) % (kReduceSlices * 256) == 0, "slices must split the row evenly");
+    const float4v *src = (const float4v *)w.part + (size_t)p0 * 2 * V4;
+    int e[EPT];
+    float4v acc[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        e[i] = (slice * EPT + i) * 256 + (int)threadIdx.x;
+        acc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+    }
+    int j = 0;
+    for (; j + 1 < n; j += 2) {
+        float4v x[EPT], y[EPT];
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            x[i] = __builtin_nontemporal_load(src + (size_t)j * 2 * V4 + e[i]);
+            y[i] = __builtin_nontemporal_load(src + (size_t)(j + 1) * 2 * V4 + e[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            acc[i] += x[i];
+            acc[i] += y[i];
+        }
+    }
+    if (j < n) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) acc[i] += __builtin_nontemporal_load(src + (size_t)j * 2 * V4 + e[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const int tensor = e[i] / V4, f = e[i] - tensor * V4;
         const int key = f / (D / 4), d4 = f - key * (D / 4);
         const int na = t * BS + key;
         if (na >= w.N) continue;
-        float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-        for (int j = 0; j < n; ++j)
-            acc += __builtin_nontemporal_load((const float4v *)(w.part + ((size_t)(p0 + j) * 2 + tensor) * BS * D) + f);
         float *dst = (tensor ? w.dV : w.dK) + ((size_t)(b * (size_t)w.N + na) * w.G + g) * D;
-        __builtin_nontemporal_store(acc, (float4v *)dst + d4);
+        __builtin_nontemporal_store(acc[i], (float4v *)dst + d4);
     }
 }
 
@@ -940,7 +973,7 @@ hipError_t launch_key_passes(const Bw &w, const BwdPlan &pl, hipStream_t stream)
     const int per_xcd = (int)((pl.cap + w.nxcd - 1) / w.nxcd);
     hipLaunchKernelGGL((nsa_sel_bwd_dkv_kernel<BS, D>), dim3(per_xcd * w.nxcd), dim3(kWaveSize * (BS / 16)), 0,
                        stream, w);
-    hipLaunchKernelGGL((nsa_sel_bwd_reduce_kernel<BS, D>), dim3(w.R), dim3(256), 0, stream, w);
+    hipLaunchKernelGGL((nsa_sel_bwd_reduce_kernel<BS, D>), dim3(w.R, kReduceSlices), dim3(256), 0, stream, w);
     return hipGetLastError();
 }
 
