@@ -187,6 +187,19 @@ def test_bwd_8k_every_element(torch_cuda):
     _full(torch_cuda, q, k, v, idx, do, cfg.block_size)
 
 
+@pytest.mark.timeout(900)
+def test_bwd_64k_every_element(torch_cuda):
+    """dQ, dK and dV of the 64k workload (M = N = 65536, H = 64, G = 8,
+    D = 128, bs = 64, T = 16) at full size, every element against the
+    oracle's whole-tensor backward (about 3 minutes of oracle time on 16
+    host threads)."""
+    cfg = CONFIGS["64k"]
+    _say(f"case {cfg} (every element)")
+    q, k, v, idx = make_inputs(cfg)
+    do = make_grad_output(cfg)
+    _full(torch_cuda, q, k, v, idx, do, cfg.block_size)
+
+
 def test_bwd_128k_local_sampled(torch_cuda):
     cfg = CONFIGS["128k-local"]
     _sampled(torch_cuda, cfg, 200, [(0, 5, cfg.NB - 1), (0, 2, 1000)])
