@@ -830,8 +830,8 @@ __global__ __launch_bounds__(kWaveSize * (BS / 16)) void nsa_sel_bwd_dkv_kernel(
 // their partials in item order.  kReduceSlices workgroups per key block row
 // (grid y), each thread holding EPT float4 sums whose loads for one partial
 // (and the next) are issued together, so a thread keeps 2 * EPT loads in
-// flight instead of one.  The order of the additions is that of the items, so the
-// result does not depend on the launch shape.
+// flight instead of one.  The additions follow the item order, so the result
+// does not depend on the launch shape.
 constexpr int kReduceSlices = 4;
 
 template <int BS, int D>
