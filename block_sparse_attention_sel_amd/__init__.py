@@ -4,7 +4,8 @@ The compute path is the C-ABI library ``libnsa_sel.so`` built from
 ``csrc/``; ``nsa_sel_fwd`` here marshals torch tensors into it.
 """
 
-__all__ = ["nsa_sel_fwd", "nsa_sel_fwd_raw", "nsa_sel_status_string", "sel_attn_fwd", "load_library", "NsaSelError"]
+__all__ = ["nsa_sel_fwd", "nsa_sel_fwd_raw", "nsa_sel_status_string", "sel_attn_fwd", "sel_attn_bwd", "sel_attn",
+           "load_library", "NsaSelError"]
 
 
 def __getattr__(name):

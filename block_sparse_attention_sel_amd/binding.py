@@ -6,9 +6,12 @@
 mirror the C entry points one to one (pointers may be given as ints or as torch tensors);
 ``sel_attn_fwd``, ``sel_attn_bwd``, ``dense_attn_fwd``, ``window_attn_fwd`` and
 ``topk_blocks`` are conveniences that check torch tensors, allocate the outputs and call the
-entry point on the current stream (the fp16 or bf16 one by the tensors' dtype).  ``nsa_gather_probe`` mirrors the
-measurement probe of include/nsa_gather_probe.h.  All arithmetic happens in the
-HIP kernels; when a library is missing every call into it raises.
+entry point on the current stream (the fp16 or bf16 one by the tensors' dtype);
+``sel_attn`` joins the forward and the backward as a torch.autograd.Function.
+``nsa_gather_probe`` mirrors the measurement probe of include/nsa_gather_probe.h.
+All arithmetic happens in the HIP kernels, except that ``sel_attn`` has torch cast
+the backward's fp32 gradients to the inputs' dtype; when a library is missing every
+call into it raises.
 """
 
 from __future__ import annotations
@@ -286,6 +289,46 @@ def sel_attn_bwd(q, k, v, block_indices, out, lse, dout, block_size: int, worksp
     nsa_sel_bwd(q, k, v, block_indices, out, lse, dout, dq, dk, dv, workspace, workspace.numel(), B, M, N, H, G, D,
                 block_size, T, stream)
     return dq, dk, dv
+
+
+_sel_attn_fn = None
+
+
+def _sel_attn_function():
+    """The torch.autograd.Function behind sel_attn (made on first use, so that
+    importing this module does not import torch)."""
+    global _sel_attn_fn
+    if _sel_attn_fn is None:
+        import torch
+
+        class SelAttnFunction(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, block_indices, block_size):
+                out, lse = sel_attn_fwd(q, k, v, block_indices, block_size)
+                ctx.block_size = block_size
+                ctx.save_for_backward(q, k, v, block_indices, out, lse)
+                ctx.mark_non_differentiable(lse)
+                return out, lse
+
+            @staticmethod
+            def backward(ctx, dout, dlse):
+                q, k, v, block_indices, out, lse = ctx.saved_tensors
+                if q.dtype != torch.float16:
+                    raise NotImplementedError("the selection-attention backward takes fp16 tensors")
+                dq, dk, dv = sel_attn_bwd(q, k, v, block_indices, out, lse, dout.to(torch.float16).contiguous(),
+                                          ctx.block_size)
+                return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
+
+        _sel_attn_fn = SelAttnFunction
+    return _sel_attn_fn
+
+
+def sel_attn(q, k, v, block_indices, block_size: int):
+    """sel_attn_fwd as a torch.autograd.Function: returns (out, lse); the
+    gradient of out flows to q, k and v through sel_attn_bwd (fp16 tensors;
+    the fp32 gradients are cast to the inputs' dtype).  lse is returned
+    without a gradient: the backward takes gradients of out only."""
+    return _sel_attn_function().apply(q, k, v, block_indices, block_size)
 
 
 def nsa_dense_fwd_raw(Q, K, V, O, LSE, B, M, N, H, G, D, stream=0) -> int:

@@ -413,6 +413,18 @@ def test_bwd_wrapper_rejects_bad_workspace():
             binding.sel_attn_bwd(q, k, v, idx, o, lse, o, 32, workspace=ws)
 
 
+def test_autograd_wrapper_checks_like_the_forward():
+    # sel_attn runs sel_attn_fwd first, with the same checks: host tensors stop at
+    # the GPU check, and no gradient machinery runs before it.
+    import torch
+    q, k, v, idx = _cpu_inputs()
+    q.requires_grad_(True)
+    with pytest.raises(ValueError, match="GPU"):
+        binding.sel_attn(q, k, v, idx, 32)
+    with pytest.raises(TypeError):
+        binding.sel_attn(q.detach().float(), k, v, idx, 32)
+
+
 def test_entry_point_forms_dispatch_on_their_arguments(lib):
     # Fifteen C arguments -> the C entry point (status from the host checks).
     with pytest.raises(binding.NsaSelError):

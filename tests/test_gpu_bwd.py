@@ -240,3 +240,38 @@ def test_bwd_errors(torch_cuda):
     assert binding.nsa_sel_bwd_raw(*args(tq, n)) == binding.NSA_SEL_ERR_ALIAS   # workspace over Q
     assert binding.nsa_sel_bwd_raw(*args(ws, n)) == binding.NSA_SEL_OK
     torch.cuda.synchronize()
+
+
+def test_sel_attn_autograd_matches_the_entry_points(torch_cuda):
+    """sel_attn as an autograd function: its forward is sel_attn_fwd, the
+    gradients it hands to q, k and v are sel_attn_bwd's cast to fp16, and lse
+    carries no gradient."""
+    torch = torch_cuda
+    from block_sparse_attention_sel_amd.binding import sel_attn, sel_attn_bwd, sel_attn_fwd
+    cfg = SMALL["b2-ragged"]
+    q, k, v, idx = make_inputs(cfg)
+    do = make_grad_output(cfg)
+    tq, tk, tv, ti, tdo = _to_dev(torch, q, k, v, idx, do)
+    lq, lk, lv = (t.clone().requires_grad_(True) for t in (tq, tk, tv))
+    out, lse = sel_attn(lq, lk, lv, ti, cfg.block_size)
+    assert not lse.requires_grad and out.requires_grad
+    out.backward(tdo)
+    torch.cuda.synchronize()
+    o_ref, l_ref = sel_attn_fwd(tq, tk, tv, ti, cfg.block_size)
+    dq, dk, dv = sel_attn_bwd(tq, tk, tv, ti, o_ref, l_ref, tdo, cfg.block_size)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), o_ref) and torch.equal(lse, l_ref)
+    assert lq.grad.dtype == torch.float16
+    assert torch.equal(lq.grad, dq.half()) and torch.equal(lk.grad, dk.half()) and torch.equal(lv.grad, dv.half())
+
+
+def test_sel_attn_autograd_rejects_bf16_backward(torch_cuda):
+    torch = torch_cuda
+    from block_sparse_attention_sel_amd.binding import sel_attn
+    cfg = SMALL["tiny"]
+    q, k, v, idx = make_inputs(cfg)
+    tq, tk, tv = (torch.from_numpy(a).to("cuda").to(torch.bfloat16).requires_grad_(True) for a in (q, k, v))
+    ti = torch.from_numpy(idx).to("cuda")
+    out, _ = sel_attn(tq, tk, tv, ti, cfg.block_size)
+    with pytest.raises(NotImplementedError):
+        out.float().sum().backward()
