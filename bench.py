@@ -282,6 +282,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10, help="cold-cache timed calls (0 = skip)")
     ap.add_argument("--no-probe", action="store_true", help="skip the gather-ceiling probe")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (scale for HBM counters)")
@@ -389,6 +390,27 @@ def main():
                        "gathered_GBps": round(gathered / (c_med * 1e-3) / 1e9, 1)}
         detail["frac_cold_median"] = roofline(flops, compulsory, c_med)["frac"]
     out["roofline_detail"] = detail
+
+    if not args.no_graph:
+        # One forward call (its 64 dispatches) captured in a HIP graph and
+        # replayed: the launch cost a caller that captures the call avoids.
+        print("[bench] HIP graph replay", file=sys.stderr, flush=True)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            nsa_sel_fwd(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
+                        side.cuda_stream)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            nsa_sel_fwd(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
+                        torch.cuda.current_stream(dev).cuda_stream)
+        _, g_ev, g_min = time_launches(torch, graph.replay, args.steps, args.warmup)
+        assert torch.isfinite(L).all().item(), "non-finite LSE after graph replay"
+        out["graph"] = {"ms": round(g_ev, 4), "ms_min": round(g_min, 4),
+                        "eager_over_graph": round(ev_ms / g_ev, 4)}
+        del graph
 
     # MFMA work actually issued: every (16-column tile, staged block) pair runs
     # the QK and PV products over the whole block, 4 * 16 * bs * D flops.

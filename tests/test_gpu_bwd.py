@@ -275,3 +275,45 @@ def test_sel_attn_autograd_rejects_bf16_backward(torch_cuda):
     out, _ = sel_attn(tq, tk, tv, ti, cfg.block_size)
     with pytest.raises(NotImplementedError):
         out.float().sum().backward()
+
+
+def test_forward_and_backward_replay_in_a_hip_graph(torch_cuda):
+    """nsa_sel_fwd (64 dispatches per call) and nsa_sel_bwd captured into one
+    HIP graph with preallocated outputs and workspace: every replay, with
+    eager work in between, is bitwise the eager result (the library issues
+    kernel launches only: no memset, allocation or synchronisation)."""
+    torch = torch_cuda
+    from block_sparse_attention_sel_amd import binding
+    cfg = CONFIGS["8k"].with_(M=2048, N=2048)
+    q, k, v, idx = make_inputs(cfg)
+    do = make_grad_output(cfg)
+    tq, tk, tv, ti, tdo = _to_dev(torch, q, k, v, idx, do)
+    B, M, N, H, G, D, bs, T = cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T
+    ws = torch.empty(binding.nsa_sel_bwd_workspace_size(B, M, N, H, G, D, bs, T), dtype=torch.uint8, device="cuda")
+    o_e, l_e = binding.sel_attn_fwd(tq, tk, tv, ti, bs)
+    dq_e, dk_e, dv_e = binding.sel_attn_bwd(tq, tk, tv, ti, o_e, l_e, tdo, bs, workspace=ws)
+    torch.cuda.synchronize()
+    o = torch.empty_like(o_e)
+    lse = torch.empty_like(l_e)
+    dq, dk, dv = torch.empty_like(dq_e), torch.empty_like(dk_e), torch.empty_like(dv_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one call on a side stream before capture
+        binding.nsa_sel_fwd(tq, tk, tv, ti, o, lse, B, M, N, H, G, D, bs, T, side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        st = torch.cuda.current_stream().cuda_stream
+        binding.nsa_sel_fwd(tq, tk, tv, ti, o, lse, B, M, N, H, G, D, bs, T, st)
+        binding.nsa_sel_bwd(tq, tk, tv, ti, o, lse, tdo, dq, dk, dv, ws, ws.numel(), B, M, N, H, G, D, bs, T, st)
+    for replay in range(3):
+        for t in (o, lse, dq, dk, dv):
+            t.fill_(float("nan"))
+        ws.fill_(0xA5)
+        graph.replay()
+        torch.cuda.synchronize()
+        _say(f"  replay {replay}")
+        assert torch.equal(o, o_e) and torch.equal(lse, l_e)
+        assert torch.equal(dq, dq_e) and torch.equal(dk, dk_e) and torch.equal(dv, dv_e)
+        assert _overflow_word(torch, ws) == 0
