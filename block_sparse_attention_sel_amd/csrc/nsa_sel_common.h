@@ -52,9 +52,11 @@ struct Params {
     int wslots_per_bg;  // wavefront slots per (b, g): ceil(M / queries per wavefront)
     int wslots;         // B * G * wslots_per_bg
     int per_xcd;        // wavefront slots owned by each XCD: ceil(wslots / 8)
-    int gen_step;       // wavefront slots one XCD runs per launch (its workgroup slots x waves)
-    int gen;            // generation (launch) index
+    int gen_step;       // wavefront slots one XCD runs per generation (its workgroup slots x waves)
+    int gen;            // first generation of this launch
+    int wg_per_gen;     // workgroups of one generation (a launch carries one or all generations)
     int nxcd;           // XCDs workgroups are dealt to (w % nxcd); 1 = one contiguous range
+    int l2_bytes;       // L2 of one XCD
     float scale_log2;   // log2(e) / sqrt(D)
 };
 
@@ -709,13 +711,15 @@ __device__ __forceinline__ Slot decode_slot(const Params &p, int ws, int qw) {
     return s;
 }
 
-// Wavefront slot of wavefront `wave` of this workgroup in generation p.gen,
-// or -1.  XCD w % nxcd runs the next gen_step slots of its contiguous range,
-// so one generation fills every workgroup slot of every CU.
+// Wavefront slot of wavefront `wave` of this workgroup, or -1.  Workgroup
+// blockIdx.x belongs to generation p.gen + blockIdx.x / wg_per_gen; within a
+// generation, XCD w % nxcd runs the next gen_step slots of its contiguous
+// range, so one generation fills every workgroup slot of every CU.
 template <int WAVES>
 __device__ __forceinline__ int wave_slot(const Params &p, int wave) {
-    const int w = blockIdx.x;
-    const int loc = p.gen * p.gen_step + (w / p.nxcd) * WAVES + wave;
+    const int gen = p.gen + (int)blockIdx.x / p.wg_per_gen;
+    const int w = (int)blockIdx.x - (gen - p.gen) * p.wg_per_gen;
+    const int loc = gen * p.gen_step + (w / p.nxcd) * WAVES + wave;
     const int ws = (w % p.nxcd) * p.per_xcd + loc;
     return (loc >= p.per_xcd || ws >= p.wslots) ? -1 : ws;
 }
@@ -750,21 +754,25 @@ bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb) {
 // contiguous range of work: correct everywhere, without the L2 locality).  A
 // failed CU query falls back to 256.
 struct Topology {
-    int cus, nxcd;
+    int cus, nxcd, l2;  // l2: bytes of one XCD's L2 (the device attribute reports it per XCD)
 };
 Topology device_topology() {
-    static std::atomic<int> cached_cus[64], cached_xcd[64];
+    static std::atomic<int> cached_cus[64], cached_xcd[64], cached_l2[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    Topology t{cached_cus[dev].load(std::memory_order_relaxed), cached_xcd[dev].load(std::memory_order_relaxed)};
-    if (t.cus <= 0 || t.nxcd <= 0) {
+    Topology t{cached_cus[dev].load(std::memory_order_relaxed), cached_xcd[dev].load(std::memory_order_relaxed),
+               cached_l2[dev].load(std::memory_order_relaxed)};
+    if (t.cus <= 0 || t.nxcd <= 0 || t.l2 <= 0) {
         if (hipDeviceGetAttribute(&t.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || t.cus <= 0)
             t.cus = 256;
         if (hipDeviceGetAttribute(&t.nxcd, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || t.nxcd < 1 ||
             t.nxcd > 64 || t.cus % t.nxcd != 0)
             t.nxcd = 1;
+        if (hipDeviceGetAttribute(&t.l2, hipDeviceAttributeL2CacheSize, dev) != hipSuccess || t.l2 <= 0)
+            t.l2 = 4 << 20;
         cached_cus[dev].store(t.cus, std::memory_order_relaxed);
         cached_xcd[dev].store(t.nxcd, std::memory_order_relaxed);
+        cached_l2[dev].store(t.l2, std::memory_order_relaxed);
     }
     return t;
 }
@@ -791,7 +799,9 @@ int check_sizes(int B, int M, int N, int H, int G, int D, int block_size, int T,
     p.scale_log2 = kLog2e / sqrtf((float)D);
     p.gen = 0;
     p.gen_step = 0;
+    p.wg_per_gen = 1;
     p.nxcd = 1;
+    p.l2_bytes = 0;
     return NSA_SEL_OK;
 }
 
@@ -805,6 +815,7 @@ int check_sizes(int B, int M, int N, int H, int G, int D, int block_size, int T,
 void plan_slots(Params &p, const Topology &tp, int max_mode = 2) {
     const int cus = tp.cus;
     p.nxcd = tp.nxcd;
+    p.l2_bytes = tp.l2;
     int mode = 0;
     for (int nt = max_mode; nt >= 1; nt /= 2) {
         if ((int64_t)p.pack * nt * p.T <= 128) {
@@ -842,10 +853,18 @@ hipError_t launch_generations(const F &f, Params p, int cus, hipStream_t stream)
     constexpr int wg_per_cu = by_lds < 4 ? (by_lds > 0 ? by_lds : 1) : 4;
     const int wg_per_xcd = (cus / p.nxcd > 0 ? cus / p.nxcd : 1) * wg_per_cu;
     p.gen_step = wg_per_xcd * WAVES;
+    p.wg_per_gen = wg_per_xcd * p.nxcd;
     const int gens = (p.per_xcd + p.gen_step - 1) / p.gen_step;
-    for (int g = 0; g < gens; ++g) {
+    // One launch per generation keeps the wavefronts resident on an XCD
+    // sweeping one group's K/V together, which is what its L2 hits come
+    // from.  When one (b, g)'s K and V fit an XCD's L2 that sweep buys
+    // nothing, and a single launch carrying every generation lets the next
+    // generation's workgroups fill the tail of the previous one.
+    const bool one_launch = (int64_t)p.N * D * 2 * 2 <= (int64_t)p.l2_bytes;
+    const int per_launch = one_launch ? gens : 1;
+    for (int g = 0; g < gens; g += per_launch) {
         p.gen = g;
-        f.template launch<BS, SPLIT, D, PACK, MODE>(dim3(wg_per_xcd * p.nxcd), dim3(kWaveSize * WAVES), stream,
+        f.template launch<BS, SPLIT, D, PACK, MODE>(dim3(p.wg_per_gen * per_launch), dim3(kWaveSize * WAVES), stream,
                                                     p);
     }
     return hipGetLastError();
