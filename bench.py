@@ -1,7 +1,9 @@
-"""Benchmark of the NSA selection-attention forward (nsa_sel_fwd) on one MI355X.
+"""Benchmark of the NSA selection-attention forward (nsa_sel_fwd_ws) on one MI355X.
 
-One step is one nsa_sel_fwd launch over the whole workload (all (b, m, g)
-units of the config) with inputs already resident in HBM.  Prints ONE JSON
+One step is one nsa_sel_fwd_ws call over the whole workload (all (b, m, g)
+units of the config) with inputs and its workspace already resident in HBM;
+the same forward queued as one dispatch per generation (nsa_sel_fwd, no
+workspace) is timed beside it.  Prints ONE JSON
 line: effective TFLOP/s as ``value``, plus ms per step, gathered-KV GB/s, the
 roofline of the kernel (the larger of compulsory bytes at the HBM peak and
 effective flops at the fp16 MFMA peak), cold-cache timings, the
@@ -126,20 +128,29 @@ def _counter_sums(csv_path: str, counter: str):
 def summarize_pmc(fetch_csv: str, write_csv: str, calls: int, copy_mib: int, out_path: str, l2_csv=None):
     """Turns two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
     dispatch) of `bench.py --copy-probe-mib N --steps S --warmup W --no-dense
-    --no-cpu-baseline` into HBM bytes per nsa_sel_fwd call.  Each counter is
+    --no-cpu-baseline --no-graph` into HBM bytes per nsa_sel_fwd_ws call.  Each counter is
     scaled by what it reads for the plain N MiB device copy in the same run.
     l2_csv: an optional third run with TCC_HIT_sum and TCC_MISS_sum, giving the
     L2 hit rate of the forward's requests."""
     res = {"kernel_sha256": _kernel_sha(), "calls": calls, "copy_probe_mib": copy_mib}
+
+    def forward(sums):
+        # The dispatches of the timed forward calls: the persistent kernel and
+        # its schedule clearing, or the generation kernels where the call
+        # queues those.
+        names = ("nsa_sel_fwd_persistent_kernel", "sched_clear_kernel")
+        picked = [v for (n, v) in sums.values() if any(k in n for k in names)]
+        return picked or [v for (n, v) in sums.values() if "nsa_sel_fwd_kernel" in n]
+
     if l2_csv:
-        hit = sum(v for (n, v) in _counter_sums(l2_csv, "TCC_HIT_sum").values() if "nsa_sel_fwd_kernel" in n)
-        miss = sum(v for (n, v) in _counter_sums(l2_csv, "TCC_MISS_sum").values() if "nsa_sel_fwd_kernel" in n)
+        hit = sum(forward(_counter_sums(l2_csv, "TCC_HIT_sum")))
+        miss = sum(forward(_counter_sums(l2_csv, "TCC_MISS_sum")))
         res["l2_requests_per_call"] = (hit + miss) / calls
         res["l2_hit"] = hit / (hit + miss) if hit + miss > 0 else None
     for tag, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"), ("write", write_csv, "WRITE_SIZE")):
         sums = _counter_sums(path, counter)
         copy = [v for (n, v) in sums.values() if "copyBuffer" in n and v > 1000]
-        kern = [v for (n, v) in sums.values() if "nsa_sel_fwd_kernel" in n]
+        kern = forward(sums)
         scale = (copy_mib * 1024.0) / copy[0]
         res[f"{tag}_kib_raw_per_call"] = sum(kern) / calls
         res[f"{tag}_copy_scale"] = scale
@@ -306,7 +317,7 @@ def main():
         sys.exit(2)
 
     import torch
-    from block_sparse_attention_sel_amd.binding import nsa_sel_fwd
+    from block_sparse_attention_sel_amd.binding import nsa_sel_fwd, nsa_sel_fwd_workspace_size, nsa_sel_fwd_ws
 
     cfg = CONFIGS[args.config]
     print(f"[bench] generating {cfg}", file=sys.stderr, flush=True)
@@ -317,9 +328,24 @@ def main():
     L = torch.empty((cfg.B, cfg.H, cfg.M), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    workspaces = {}
+
+    def workspace(T):
+        if T not in workspaces:
+            n = nsa_sel_fwd_workspace_size(cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, T)
+            workspaces[T] = torch.empty(n, dtype=torch.uint8, device=dev)
+        return workspaces[T]
+
     def launch(ti_=ti, T=cfg.T):
-        nsa_sel_fwd(tq, tk, tv, ti_, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, T,
+        ws = workspace(T)
+        nsa_sel_fwd_ws(tq, tk, tv, ti_, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, T, ws,
+                       ws.numel(), stream.cuda_stream)
+
+    def launch_generations():
+        nsa_sel_fwd(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
                     stream.cuda_stream)
+
+    workspace(cfg.T)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
@@ -353,11 +379,12 @@ def main():
         "vs_baseline": None,
         "dtype": "fp16",
         "data": "synthetic",
-        "config": {"workload": f"nsa_sel_fwd {cfg.name}", "B": cfg.B, "M": cfg.M, "N": cfg.N, "H": cfg.H,
+        "config": {"workload": f"nsa_sel_fwd_ws {cfg.name}", "B": cfg.B, "M": cfg.M, "N": cfg.N, "H": cfg.H,
                    "G": cfg.G, "D": cfg.D, "block_size": cfg.block_size, "T": cfg.T,
                    "index_rule": cfg.rule, "seed": cfg.seed},
         "kernel_ms": round(ev_ms, 4),
         "kernel_ms_min": round(ev_min, 4),
+        "workspace_bytes": workspace(cfg.T).numel(),
         "gathered_GBps": round(gbps, 1),
         "eff_TFLOPs": round(flops / (ev_ms * 1e-3) / 1e12, 3),
         "work": {"counted_blocks": blocks, "visible_keys": keys, "gathered_bytes": gathered,
@@ -391,21 +418,28 @@ def main():
         detail["frac_cold_median"] = roofline(flops, compulsory, c_med)["frac"]
     out["roofline_detail"] = detail
 
+    # The same forward as one dispatch per generation (no workspace).
+    print("[bench] generation launches (nsa_sel_fwd)", file=sys.stderr, flush=True)
+    _, gl_ev, gl_min = time_launches(torch, launch_generations, args.steps, args.warmup)
+    out["generation_launches"] = {"kernel": "nsa_sel_fwd", "ms": round(gl_ev, 4), "ms_min": round(gl_min, 4),
+                                  "over_workspace_call": round(gl_ev / ev_ms, 4)}
+
     if not args.no_graph:
-        # One forward call (its 64 dispatches) captured in a HIP graph and
-        # replayed: the launch cost a caller that captures the call avoids.
+        # One forward call captured in a HIP graph and replayed: the launch
+        # cost a caller that captures the call avoids.
         print("[bench] HIP graph replay", file=sys.stderr, flush=True)
+        ws = workspace(cfg.T)
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            nsa_sel_fwd(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
-                        side.cuda_stream)
+            nsa_sel_fwd_ws(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
+                           ws, ws.numel(), side.cuda_stream)
         stream.wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            nsa_sel_fwd(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
-                        torch.cuda.current_stream(dev).cuda_stream)
+            nsa_sel_fwd_ws(tq, tk, tv, ti, O, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
+                           ws, ws.numel(), torch.cuda.current_stream(dev).cuda_stream)
         _, g_ev, g_min = time_launches(torch, graph.replay, args.steps, args.warmup)
         assert torch.isfinite(L).all().item(), "non-finite LSE after graph replay"
         out["graph"] = {"ms": round(g_ev, 4), "ms_min": round(g_min, 4),
@@ -425,14 +459,15 @@ def main():
         from block_sparse_attention_sel_amd.binding import nsa_gather_probe
         print("[bench] gather-ceiling probe", file=sys.stderr, flush=True)
         staged = torch.zeros(1, dtype=torch.int64, device=dev)
+        ws = workspace(cfg.T)
         qps = nsa_gather_probe(tk, tv, ti, staged, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size,
-                               cfg.T, stream.cuda_stream)
+                               cfg.T, stream.cuda_stream, ws, ws.numel())
         torch.cuda.synchronize()
         n_staged = int(staged.item())
 
         def probe():
             nsa_gather_probe(tk, tv, ti, staged, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size,
-                             cfg.T, stream.cuda_stream)
+                             cfg.T, stream.cuda_stream, ws, ws.numel())
 
         _, p_ev, p_min = time_launches(torch, probe, args.steps, args.warmup)
         staged_bytes = n_staged * cfg.block_size * cfg.D * 4
@@ -501,19 +536,21 @@ def main():
     if not args.no_bf16:
         # The selection forward with bf16 Q, K, V, O (same draws, rounded to bf16).
         import torch as _t
-        from block_sparse_attention_sel_amd.binding import nsa_sel_fwd_bf16
+        from block_sparse_attention_sel_amd.binding import nsa_sel_fwd_bf16_ws
         print("[bench] bf16 selection forward", file=sys.stderr, flush=True)
         qb, kb, vb, _ = make_inputs_bf16(cfg)
         bq, bk, bv = (_t.from_numpy(a.view(np.int16)).view(_t.bfloat16).to(dev) for a in (qb, kb, vb))
         del qb, kb, vb
         Ob = torch.empty((cfg.B, cfg.M, cfg.H, cfg.D), dtype=torch.bfloat16, device=dev)
 
+        wsb = workspace(cfg.T)
+
         def sel_bf16():
-            nsa_sel_fwd_bf16(bq, bk, bv, ti, Ob, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size, cfg.T,
-                             stream.cuda_stream)
+            nsa_sel_fwd_bf16_ws(bq, bk, bv, ti, Ob, L, cfg.B, cfg.M, cfg.N, cfg.H, cfg.G, cfg.D, cfg.block_size,
+                                cfg.T, wsb, wsb.numel(), stream.cuda_stream)
 
         _, s_ev, s_min = time_launches(torch, sel_bf16, args.steps, args.warmup)
-        out["bf16"] = {"kernel": "nsa_sel_fwd_bf16", "ms": round(s_ev, 4), "ms_min": round(s_min, 4),
+        out["bf16"] = {"kernel": "nsa_sel_fwd_bf16_ws", "ms": round(s_ev, 4), "ms_min": round(s_min, 4),
                        "eff_TFLOPs": round(flops / (s_ev * 1e-3) / 1e12, 3),
                        "ratio_bf16_over_fp16": round(s_ev / ev_ms, 3)}
         if args.no_window:

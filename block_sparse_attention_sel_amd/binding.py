@@ -1,7 +1,7 @@
 """Thin ctypes binding of libnsa_sel.so and libnsa_gather_probe.so.
 
-``nsa_sel_fwd``, ``nsa_sel_fwd_bf16``, ``nsa_sel_bwd``,
-``nsa_sel_bwd_workspace_size``, ``nsa_sel_bwd_noalloc``, ``nsa_dense_fwd``, ``nsa_window_fwd``,
+``nsa_sel_fwd``, ``nsa_sel_fwd_bf16``, ``nsa_sel_fwd_ws``, ``nsa_sel_fwd_bf16_ws``,
+``nsa_sel_fwd_workspace_size``, ``nsa_sel_bwd``, ``nsa_sel_bwd_workspace_size``, ``nsa_sel_bwd_noalloc``, ``nsa_dense_fwd``, ``nsa_window_fwd``,
 ``nsa_window_fwd_bf16``, ``nsa_topk_blocks`` and ``nsa_sel_status_string``
 mirror the C entry points one to one (pointers may be given as ints or as torch tensors);
 ``sel_attn_fwd``, ``sel_attn_bwd``, ``dense_attn_fwd``, ``window_attn_fwd`` and
@@ -35,7 +35,8 @@ NSA_SEL_ERR_HIP = 7
 NSA_SEL_ERR_WORKSPACE = 8
 NSA_SEL_ERR_SCRATCH = 9
 
-EXPORTED = ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_fwd_unpipelined", "nsa_sel_status_string")
+EXPORTED = ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_fwd_unpipelined", "nsa_sel_fwd_workspace_size",
+            "nsa_sel_fwd_ws", "nsa_sel_fwd_bf16_ws", "nsa_sel_status_string")
 DENSE_EXPORTED = ("nsa_dense_fwd", "nsa_window_fwd", "nsa_window_fwd_bf16")
 BWD_EXPORTED = ("nsa_sel_bwd", "nsa_sel_bwd_workspace_size", "nsa_sel_bwd_noalloc")
 TOPK_EXPORTED = ("nsa_topk_blocks",)
@@ -62,6 +63,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("nsa_sel_fwd", "nsa_sel_fwd_bf16", "nsa_sel_fwd_unpipelined"):
         getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp]
         getattr(lib, name).restype = ci
+    for name in ("nsa_sel_fwd_ws", "nsa_sel_fwd_bf16_ws"):
+        getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, vp] + [ci] * 8 + [vp, ctypes.c_size_t, vp]
+        getattr(lib, name).restype = ci
+    lib.nsa_sel_fwd_workspace_size.argtypes = [ci] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.nsa_sel_fwd_workspace_size.restype = ci
     lib.nsa_sel_status_string.argtypes = [ci]
     lib.nsa_sel_status_string.restype = ctypes.c_char_p
     lib.nsa_dense_fwd.argtypes = [vp, vp, vp, vp, vp] + [ci] * 6 + [vp]
@@ -163,10 +169,59 @@ def nsa_sel_fwd_bf16(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_siz
         raise NsaSelError(rc)
 
 
-def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, stream=None):
+def nsa_sel_fwd_workspace_size_raw(B, M, N, H, G, D, block_size, T):
+    """Calls the C entry point; returns (status, bytes)."""
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    rc = lib.nsa_sel_fwd_workspace_size(int(B), int(M), int(N), int(H), int(G), int(D), int(block_size), int(T),
+                                        ctypes.byref(n))
+    return rc, n.value
+
+
+def nsa_sel_fwd_workspace_size(B, M, N, H, G, D, block_size, T) -> int:
+    """Workspace bytes of nsa_sel_fwd_ws; raises NsaSelError on a nonzero status."""
+    rc, n = nsa_sel_fwd_workspace_size_raw(B, M, N, H, G, D, block_size, T)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+    return n
+
+
+def nsa_sel_fwd_ws_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, workspace,
+                       workspace_bytes, stream=0, bf16: bool = False) -> int:
+    """Calls the C entry point (nsa_sel_fwd_ws, or nsa_sel_fwd_bf16_ws when
+    bf16) and returns its status code unchanged."""
+    lib = load_library()
+    fn = lib.nsa_sel_fwd_bf16_ws if bf16 else lib.nsa_sel_fwd_ws
+    return fn(_addr(Q), _addr(K), _addr(V), _addr(block_indices), _addr(O), _addr(LSE),
+              int(B), int(M), int(N), int(H), int(G), int(D), int(block_size), int(T),
+              ctypes.c_void_p(_addr(workspace)), int(workspace_bytes), ctypes.c_void_p(_addr(stream)))
+
+
+def nsa_sel_fwd_ws(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, workspace, workspace_bytes,
+                   stream=0) -> None:
+    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
+    rc = nsa_sel_fwd_ws_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, workspace,
+                            workspace_bytes, stream)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def nsa_sel_fwd_bf16_ws(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, workspace,
+                        workspace_bytes, stream=0) -> None:
+    """Same arguments as the C entry point; raises NsaSelError on a nonzero status."""
+    rc = nsa_sel_fwd_ws_raw(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, workspace,
+                            workspace_bytes, stream, bf16=True)
+    if rc != NSA_SEL_OK:
+        raise NsaSelError(rc)
+
+
+def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, stream=None, workspace=None):
     """q [B,M,H,D], k/v [B,N,G,D] (all fp16 or all bf16), block_indices
     [B,M,G,T] int32, all contiguous CUDA tensors.  Returns (O [B,M,H,D] in the
-    input dtype, LSE [B,H,M] fp32)."""
+    input dtype, LSE [B,H,M] fp32).  Runs nsa_sel_fwd_ws (nsa_sel_fwd_bf16_ws)
+    with `workspace` (a uint8 CUDA tensor of at least
+    nsa_sel_fwd_workspace_size bytes), or with one allocated per call from
+    torch's caching allocator."""
     import torch
 
     et = q.dtype if isinstance(q, torch.Tensor) and q.dtype in (torch.float16, torch.bfloat16) else torch.float16
@@ -191,10 +246,18 @@ def sel_attn_fwd(q, k, v, block_indices, block_size: int, out=None, lse=None, st
         lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws_bytes = nsa_sel_fwd_workspace_size(B, M, N, H, G, D, block_size, T)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    elif not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or \
+            workspace.device != q.device or not workspace.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor on the inputs' device")
     if et == torch.bfloat16:
-        nsa_sel_fwd_bf16(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
+        nsa_sel_fwd_bf16_ws(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, workspace,
+                            workspace.numel(), stream)
     else:
-        nsa_sel_fwd(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, stream)
+        nsa_sel_fwd_ws(q, k, v, block_indices, out, lse, B, M, N, H, G, D, block_size, T, workspace,
+                       workspace.numel(), stream)
     return out, lse
 
 
@@ -468,27 +531,33 @@ def load_probe_library(path: str = PROBE_LIB_PATH) -> ctypes.CDLL:
         raise RuntimeError(f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
     lib = ctypes.CDLL(path)
     vp, ci = ctypes.c_void_p, ctypes.c_int
-    lib.nsa_gather_probe.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [ctypes.POINTER(ci), vp]
+    lib.nsa_gather_probe.argtypes = [vp, vp, vp, vp] + [ci] * 8 + [vp, ctypes.c_size_t, ctypes.POINTER(ci), vp]
     lib.nsa_gather_probe.restype = ci
     if path == PROBE_LIB_PATH:
         _probe_lib = lib
     return lib
 
 
-def nsa_gather_probe_raw(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream=0):
-    """Calls the probe's C entry point; returns (status, queries per slot)."""
+def nsa_gather_probe_raw(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream=0, workspace=None,
+                         workspace_bytes=0):
+    """Calls the probe's C entry point; returns (status, queries per slot).
+    workspace None: the launches of nsa_sel_fwd; a workspace: those of
+    nsa_sel_fwd_ws."""
     lib = load_probe_library()
     qps = ctypes.c_int(0)
     rc = lib.nsa_gather_probe(_addr(K), _addr(V), _addr(block_indices), _addr(staged), int(B), int(M), int(N),
-                              int(H), int(G), int(D), int(block_size), int(T), ctypes.byref(qps),
-                              ctypes.c_void_p(_addr(stream)))
+                              int(H), int(G), int(D), int(block_size), int(T),
+                              ctypes.c_void_p(_addr(workspace) if workspace is not None else None),
+                              int(workspace_bytes), ctypes.byref(qps), ctypes.c_void_p(_addr(stream)))
     return rc, qps.value
 
 
-def nsa_gather_probe(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream=0) -> int:
+def nsa_gather_probe(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream=0, workspace=None,
+                     workspace_bytes=0) -> int:
     """Queues the probe; raises NsaSelError on a nonzero status and returns the
     number of consecutive queries each wavefront slot carries."""
-    rc, qps = nsa_gather_probe_raw(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream)
+    rc, qps = nsa_gather_probe_raw(K, V, block_indices, staged, B, M, N, H, G, D, block_size, T, stream, workspace,
+                                   workspace_bytes)
     if rc != NSA_SEL_OK:
         raise NsaSelError(rc)
     return qps

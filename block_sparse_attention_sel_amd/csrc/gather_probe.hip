@@ -88,19 +88,54 @@ __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_gath
     if (lane == 0) atomicAdd((unsigned long long *)staged, (unsigned long long)n);
 }
 
+// The same slots run by the persistent schedule, as nsa_sel_fwd_ws runs them.
+template <int BS, int SPLIT, int D, int PACK, int MODE>
+__global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_gather_probe_persistent_kernel(
+    Params p, uint64_t *staged) {
+    constexpr int SBS = BS / SPLIT;
+    constexpr int WAVES = waves_per_wg(SBS);
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) unsigned char mbuf_all[MODE == 0 ? WAVES : 1][MODE == 0 ? kMapBlocks : 16];
+    int n = 0;
+    run_persistent<WAVES>(p, wave, lane, [&](int ws) {
+        if constexpr (MODE == 0)
+            n += probe_slot<BS, SPLIT, D, PACK, 1, MapMerger<PACK, BS>>(p, ws, lane, kbuf_all[wave], vbuf_all[wave],
+                                                                      mbuf_all[wave]);
+        else
+            n += probe_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, ws, lane, kbuf_all[wave],
+                                                                                  vbuf_all[wave], nullptr);
+    });
+    if (lane == 0 && n > 0) atomicAdd((unsigned long long *)staged, (unsigned long long)n);
+}
+
 struct ProbeKernel {
+    static constexpr bool kPersistent = true;
     uint64_t *staged;
     template <int BS, int SPLIT, int D, int PACK, int MODE>
     void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
         hipLaunchKernelGGL((nsa_gather_probe_kernel<BS, SPLIT, D, PACK, MODE>), grid, block, 0, stream, p, staged);
+    }
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    void launch_persist(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
+        hipLaunchKernelGGL((nsa_gather_probe_persistent_kernel<BS, SPLIT, D, PACK, MODE>), grid, block, 0, stream, p,
+                           staged);
+    }
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    int resident() const {
+        static std::atomic<int> cache[64];
+        return resident_workgroups(cache, (const void *)nsa_gather_probe_persistent_kernel<BS, SPLIT, D, PACK, MODE>,
+                                   kWaveSize * waves_per_wg(BS / SPLIT));
     }
 };
 
 }  // namespace
 
 extern "C" int nsa_gather_probe(const void *K, const void *V, const int32_t *block_indices, uint64_t *staged,
-                                int B, int M, int N, int H, int G, int D, int block_size, int T,
-                                int *queries_per_slot, hipStream_t stream) {
+                                int B, int M, int N, int H, int G, int D, int block_size, int T, void *workspace,
+                                size_t workspace_bytes, int *queries_per_slot, hipStream_t stream) {
     if (!K || !V || !block_indices || !staged) return NSA_SEL_ERR_NULL;
     Params p;
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
@@ -111,6 +146,13 @@ extern "C" int nsa_gather_probe(const void *K, const void *V, const int32_t *blo
     const Topology tp = device_topology();
     const int cus = tp.cus;
     plan_slots(p, tp);
+    if (workspace) {
+        const int64_t words = sched_words_bound(p, cus);
+        if (words > INT_MAX) return NSA_SEL_ERR_RANGE;
+        if (((uintptr_t)workspace & 255) || workspace_bytes < (size_t)words * 4) return NSA_SEL_ERR_WORKSPACE;
+        p.sched = (unsigned *)workspace;
+        p.sched_cap = (int)words;
+    }
     if (queries_per_slot) *queries_per_slot = slot_queries(p);
     p.Q = nullptr;
     p.K = (const _Float16 *)K;

@@ -226,11 +226,44 @@ __global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_
                                                                                vbuf_all[wave], nullptr);
 }
 
+// The same slots as nsa_sel_fwd_kernel, run by the persistent schedule.
+template <int BS, int SPLIT, int D, int PACK, int MODE, bool BF16, bool PIPE>
+__global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) void nsa_sel_fwd_persistent_kernel(Params p) {
+    constexpr int SBS = BS / SPLIT;
+    constexpr int WAVES = waves_per_wg(SBS);
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) unsigned char mbuf_all[MODE == 0 ? WAVES : 1][MODE == 0 ? kMapBlocks : 16];
+    run_persistent<WAVES>(p, wave, lane, [&](int ws) {
+        if constexpr (MODE == 0)
+            run_slot<BS, SPLIT, D, PACK, 1, MapMerger<PACK, BS>, BF16, PIPE>(p, ws, lane, kbuf_all[wave],
+                                                                     vbuf_all[wave], mbuf_all[wave]);
+        else
+            run_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>, BF16, PIPE>(p, ws, lane, kbuf_all[wave],
+                                                                                   vbuf_all[wave], nullptr);
+    });
+}
+
 template <bool BF16, bool PIPE = true>
 struct FwdKernel {
+    static constexpr bool kPersistent = true;
     template <int BS, int SPLIT, int D, int PACK, int MODE>
     void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
         hipLaunchKernelGGL((nsa_sel_fwd_kernel<BS, SPLIT, D, PACK, MODE, BF16, PIPE>), grid, block, 0, stream, p);
+    }
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    void launch_persist(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
+        hipLaunchKernelGGL((nsa_sel_fwd_persistent_kernel<BS, SPLIT, D, PACK, MODE, BF16, PIPE>), grid, block, 0,
+                           stream, p);
+    }
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    int resident() const {
+        static std::atomic<int> cache[64];
+        return resident_workgroups(cache,
+                                   (const void *)nsa_sel_fwd_persistent_kernel<BS, SPLIT, D, PACK, MODE, BF16, PIPE>,
+                                   kWaveSize * waves_per_wg(BS / SPLIT));
     }
 };
 
@@ -249,7 +282,7 @@ extern "C" const char *nsa_sel_status_string(int status) {
         case NSA_SEL_ERR_ALIAS: return "nsa_sel: an output buffer overlaps an input or the other output";
         case NSA_SEL_ERR_HIP: return "nsa_sel: the HIP runtime reported an error at kernel launch";
         case NSA_SEL_ERR_WORKSPACE:
-            return "nsa_sel: the backward workspace is NULL, not 256-byte aligned or smaller than required";
+            return "nsa_sel: the workspace is NULL, not 256-byte aligned or smaller than required";
         case NSA_SEL_ERR_SCRATCH:
             return "nsa_sel: these sizes need more workspace than the 64 MiB scratch of nsa_sel_bwd_noalloc; "
                    "call nsa_sel_bwd with a workspace";
@@ -259,9 +292,18 @@ extern "C" const char *nsa_sel_status_string(int status) {
 
 namespace {
 
+// Workspace bytes of the persistent schedule for checked sizes p on a device
+// of topology tp (p is planned in place).
+size_t fwd_workspace_bytes(Params &p, const Topology &tp) {
+    plan_slots(p, tp);
+    return (size_t)sched_words_bound(p, tp.cus) * 4;
+}
+
+// with_ws: the workspace entry points (workspace, workspace_bytes checked);
+// otherwise generation launches only.
 int sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_indices, void *O, float *LSE, int B,
             int M, int N, int H, int G, int D, int block_size, int T, hipStream_t stream, bool bf16,
-            bool pipelined = true) {
+            bool pipelined = true, bool with_ws = false, void *workspace = nullptr, size_t workspace_bytes = 0) {
     if (!Q || !K || !V || !block_indices || !O || !LSE) return NSA_SEL_ERR_NULL;
     Params p;
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
@@ -282,7 +324,19 @@ int sel_fwd(const void *Q, const void *K, const void *V, const int32_t *block_in
 
     const Topology tp = device_topology();
     const int cus = tp.cus;
-    plan_slots(p, tp);
+    if (with_ws) {
+        const size_t need = fwd_workspace_bytes(p, tp);
+        if (need / 4 > (size_t)INT_MAX) return NSA_SEL_ERR_RANGE;
+        if (!workspace || ((uintptr_t)workspace & 255) || workspace_bytes < need) return NSA_SEL_ERR_WORKSPACE;
+        for (int i = 0; i < 4; ++i)
+            if (ranges_overlap(workspace, need, ins[i], in_bytes[i])) return NSA_SEL_ERR_ALIAS;
+        if (ranges_overlap(workspace, need, O, q_bytes) || ranges_overlap(workspace, need, LSE, lse_bytes))
+            return NSA_SEL_ERR_ALIAS;
+        p.sched = (unsigned *)workspace;
+        p.sched_cap = (int)(need / 4);
+    } else {
+        plan_slots(p, tp);
+    }
     p.Q = (const _Float16 *)Q;
     p.K = (const _Float16 *)K;
     p.V = (const _Float16 *)V;
@@ -307,6 +361,32 @@ extern "C" int nsa_sel_fwd_bf16(const void *Q, const void *K, const void *V, con
                                 void *O, float *LSE, int B, int M, int N, int H, int G, int D,
                                 int block_size, int T, hipStream_t stream) {
     return sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, true);
+}
+
+extern "C" int nsa_sel_fwd_workspace_size(int B, int M, int N, int H, int G, int D, int block_size, int T,
+                                          size_t *bytes) {
+    if (!bytes) return NSA_SEL_ERR_NULL;
+    Params p;
+    const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
+    if (st != NSA_SEL_OK) return st;
+    const size_t b = fwd_workspace_bytes(p, device_topology());
+    if (b / 4 > (size_t)INT_MAX) return NSA_SEL_ERR_RANGE;
+    *bytes = b;
+    return NSA_SEL_OK;
+}
+
+extern "C" int nsa_sel_fwd_ws(const void *Q, const void *K, const void *V, const int32_t *block_indices, void *O,
+                              float *LSE, int B, int M, int N, int H, int G, int D, int block_size, int T,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, false, true, true,
+                   workspace, workspace_bytes);
+}
+
+extern "C" int nsa_sel_fwd_bf16_ws(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                                   void *O, float *LSE, int B, int M, int N, int H, int G, int D, int block_size,
+                                   int T, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return sel_fwd(Q, K, V, block_indices, O, LSE, B, M, N, H, G, D, block_size, T, stream, true, true, true,
+                   workspace, workspace_bytes);
 }
 
 extern "C" int nsa_sel_fwd_unpipelined(const void *Q, const void *K, const void *V, const int32_t *block_indices,

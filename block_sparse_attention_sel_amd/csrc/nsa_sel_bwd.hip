@@ -280,6 +280,7 @@ void nsa_sel_bwd_dq_kernel(Params p, DqArgs x) {
 }
 
 struct DqKernel {
+    static constexpr bool kPersistent = false;
     DqArgs x;
     template <int BS, int SPLIT, int D, int PACK, int MODE>
     void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {

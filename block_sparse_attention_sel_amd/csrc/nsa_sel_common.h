@@ -57,6 +57,10 @@ struct Params {
     int wg_per_gen;     // workgroups of one generation (a launch carries one or all generations)
     int nxcd;           // XCDs workgroups are dealt to (w % nxcd); 1 = one contiguous range
     int l2_bytes;       // L2 of one XCD
+    unsigned *sched;    // persistent schedule words (device), or nullptr: generation launches only
+    int sched_cap;      // 32-bit words available at sched
+    int gens;           // generations of one XCD's range (persistent launch)
+    int steps_max;      // steps of the persistent loop: nxcd * gens + 1
     float scale_log2;   // log2(e) / sqrt(D)
 };
 
@@ -724,6 +728,108 @@ __device__ __forceinline__ int wave_slot(const Params &p, int wave) {
     return (loc >= p.per_xcd || ws >= p.wslots) ? -1 : ws;
 }
 
+// Persistent launch.  One workgroup per workgroup slot of the device instead
+// of one launch per generation: the workgroups of XCD x (w % nxcd == x, as
+// the dispatcher deals them) run one generation of slots per step.  At every
+// step they meet at a barrier of their XCD, so that its wavefronts start
+// together and sweep key space in step, as a generation launch makes them;
+// the last workgroup to arrive claims the step's generation -- the next one
+// of the XCD's own range or, once that range is used up, the next one of
+// another range -- and publishes it.  XCDs then advance independently, and
+// one whose range runs fast takes generations over from slow ones, where a
+// generation launch makes every XCD wait for the slowest.
+//
+// 32-bit words at p.sched, cleared by sched_clear_kernel before the launch:
+//   taken[r]      word 32 * r: generations of range r claimed so far
+//   arrive[x][s]  word 32 * nxcd + x * steps_max + s: workgroups of XCD x that
+//                 reached step s
+//   claim[x][s]   word 32 * nxcd + (nxcd + x) * steps_max + s: the generation
+//                 of step s (kSchedValid | r << 20 | j), kSchedFinished, or
+//                 kSchedEmpty / kSchedClaiming while it is not yet known
+// Every wait is bounded.  A workgroup that waits at the barrier for more than
+// kAlignSpin polls claims the step itself; whoever claims a step, each of its
+// slots runs once, with the same code, so workgroups that are not all
+// resident at once cost time, never correctness.  The atomics are
+// device-scope: the ranges are claimed across XCDs.
+constexpr unsigned kSchedEmpty = 0, kSchedClaiming = 1, kSchedFinished = 2, kSchedValid = 0x80000000u;
+constexpr int kAlignSpin = 400;     // about 0.5 ms of polls
+constexpr int kClaimSpin = 1 << 20;  // a claim in progress ends after at most nxcd atomics
+
+__device__ __forceinline__ unsigned sched_add(unsigned *a) {
+    return __hip_atomic_fetch_add(a, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned sched_load(unsigned *a) {
+    return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The generation of step s for XCD x, as seen by one lane (lane 0 of
+// wavefront 0 of a workgroup: the code runs with that lane alone active).
+// Returns kSchedFinished or kSchedValid | r << 20 | j.
+__device__ __forceinline__ unsigned sched_step(const Params &p, int x, int s) {
+    unsigned *arrive = p.sched + 32 * p.nxcd + x * p.steps_max + s;
+    unsigned *claim = p.sched + 32 * p.nxcd + (p.nxcd + x) * p.steps_max + s;
+    const unsigned wgs = (unsigned)(p.wg_per_gen / p.nxcd);
+    if (sched_add(arrive) + 1 < wgs) {  // not the last to arrive: wait for the claim
+#pragma unroll 1
+        for (int it = 0; it < kAlignSpin; ++it) {
+            const unsigned v = sched_load(claim);
+            if (v >= kSchedFinished) return v;
+            __builtin_amdgcn_s_sleep(8);
+        }
+    }
+    unsigned prev = kSchedEmpty;
+    __hip_atomic_compare_exchange_strong(claim, &prev, kSchedClaiming, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == kSchedEmpty) {  // this workgroup claims the step
+        unsigned res = kSchedFinished;
+#pragma unroll 1
+        for (int d = 0; d < p.nxcd; ++d) {
+            const int r = (x + d) % p.nxcd;
+            const unsigned j = sched_add(p.sched + 32 * r);
+            if (j < (unsigned)p.gens) {
+                res = kSchedValid | ((unsigned)r << 20) | j;
+                break;
+            }
+        }
+        __hip_atomic_store(claim, res, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return res;
+    }
+    if (prev >= kSchedFinished) return prev;
+#pragma unroll 1
+    for (int it = 0; it < kClaimSpin; ++it) {  // another workgroup is claiming
+        const unsigned v = sched_load(claim);
+        if (v >= kSchedFinished) return v;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return kSchedFinished;  // not reached: the claimer stores after at most nxcd atomics
+}
+
+// The persistent loop of one workgroup: run(ws) for its wavefront's slot of
+// each generation the XCD is given.  One lane of the workgroup takes part in
+// the schedule; the wavefronts wait for it at the workgroup barrier.
+template <int WAVES, class Run>
+__device__ __forceinline__ void run_persistent(const Params &p, int wave, int lane, Run &&run) {
+    __shared__ unsigned step_claim;
+    const int x = (int)blockIdx.x % p.nxcd;
+    const int i = ((int)blockIdx.x / p.nxcd) * WAVES + wave;
+    for (int s = 0; s < p.steps_max; ++s) {
+        __syncthreads();  // every wavefront of the workgroup is done with step s - 1
+        if (wave == 0 && lane == 0) step_claim = sched_step(p, x, s);
+        __syncthreads();
+        const unsigned v = __builtin_amdgcn_readfirstlane(step_claim);
+        if (v == kSchedFinished) return;
+        const int r = (int)((v >> 20) & 0x7ffu), j = (int)(v & 0xfffffu);
+        const int loc = j * p.gen_step + i;
+        const int ws = r * p.per_xcd + loc;
+        if (r < p.nxcd && loc < p.per_xcd && ws < p.wslots) run(ws);
+    }
+}
+
+__global__ void sched_clear_kernel(unsigned *w, int n) {
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) w[i] = 0u;
+}
+
 // Buffer descriptors of K and V for (b, g): the range runs from the group's
 // first row to the end of the tensor.  b and g are wave-uniform; reading them
 // through readfirstlane keeps the descriptors in scalar registers (without
@@ -802,6 +908,10 @@ int check_sizes(int B, int M, int N, int H, int G, int D, int block_size, int T,
     p.wg_per_gen = 1;
     p.nxcd = 1;
     p.l2_bytes = 0;
+    p.sched = nullptr;
+    p.sched_cap = 0;
+    p.gens = 0;
+    p.steps_max = 0;
     return NSA_SEL_OK;
 }
 
@@ -836,12 +946,42 @@ void plan_slots(Params &p, const Topology &tp, int max_mode = 2) {
 // Queries per wavefront slot of a planned launch.
 int slot_queries(const Params &p) { return p.pack * (p.mode > 0 ? p.mode : 1); }
 
+// Schedule words of a persistent launch planned in p.
+int64_t sched_words(const Params &p) { return 32 * (int64_t)p.nxcd + 2 * (int64_t)p.nxcd * p.steps_max; }
+
+// Upper bound of sched_words for p after plan_slots on a device with `cus`
+// compute units, whatever the kernel's occupancy: a generation holds at
+// least one wavefront per CU.
+int64_t sched_words_bound(const Params &p, int cus) {
+    const int64_t per_gen = cus / p.nxcd > 0 ? cus / p.nxcd : 1;
+    const int64_t gens = (p.per_xcd + per_gen - 1) / per_gen;
+    return 32 * (int64_t)p.nxcd + 2 * (int64_t)p.nxcd * (p.nxcd * gens + 1);
+}
+
+// Workgroups of `kernel` (`threads` threads, static LDS only) that one CU holds
+// at once, from the HIP occupancy calculator, cached per device in `cache`;
+// 0 when unknown.
+int resident_workgroups(std::atomic<int> (&cache)[64], const void *kernel, int threads) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 // Launch chain, generic over a kernel family: f.launch<BS, SPLIT, D, PACK,
-// MODE>(grid, block, stream, params) queues one generation.
+// MODE>(grid, block, stream, params) queues one generation (or, from
+// p.gen, as many as the grid holds), f.launch_persist<...>(...) the
+// persistent kernel, and f.resident<...>() gives how many of the persistent
+// kernel's workgroups one CU holds (0: unknown).
 //
 // Generations are queued in order on the stream.  Every generation starts all
 // its workgroups together and ends before the next starts, so the slots
-// resident on an XCD sweep key space in step and share its L2.
+// resident on an XCD sweep key space in step and share its L2.  With a
+// schedule buffer (p.sched) the persistent kernel keeps that step per XCD
+// instead (see run_persistent).
 template <class F, int BS, int SPLIT, int D, int PACK, int MODE>
 hipError_t launch_generations(const F &f, Params p, int cus, hipStream_t stream) {
     // One generation fills every workgroup slot of every CU: the staging
@@ -861,6 +1001,28 @@ hipError_t launch_generations(const F &f, Params p, int cus, hipStream_t stream)
     // nothing, and a single launch carrying every generation lets the next
     // generation's workgroups fill the tail of the previous one.
     const bool one_launch = (int64_t)p.N * D * 2 * 2 <= (int64_t)p.l2_bytes;
+    if constexpr (F::kPersistent) {
+    if (p.sched && !one_launch) {
+        // One workgroup per slot that is resident at once: a barrier of the
+        // XCD waits for all of them.
+        const int occ = f.template resident<BS, SPLIT, D, PACK, MODE>();
+        const int per_cu = occ > 0 && occ < wg_per_cu ? occ : wg_per_cu;
+        Params q = p;
+        const int wxcd = (cus / q.nxcd > 0 ? cus / q.nxcd : 1) * per_cu;
+        q.gen_step = wxcd * WAVES;
+        q.wg_per_gen = wxcd * q.nxcd;
+        q.gens = (q.per_xcd + q.gen_step - 1) / q.gen_step;
+        q.steps_max = q.nxcd * q.gens + 1;
+        q.gen = 0;
+        if (q.gens < (1 << 20) && sched_words(q) <= q.sched_cap) {
+            const int n = (int)sched_words(q);
+            hipLaunchKernelGGL(sched_clear_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, q.sched, n);
+            f.template launch_persist<BS, SPLIT, D, PACK, MODE>(dim3(q.wg_per_gen), dim3(kWaveSize * WAVES), stream,
+                                                                q);
+            return hipGetLastError();
+        }
+    }
+    }
     const int per_launch = one_launch ? gens : 1;
     for (int g = 0; g < gens; g += per_launch) {
         p.gen = g;

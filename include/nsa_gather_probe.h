@@ -40,6 +40,10 @@ extern "C" {
  *                 to it.  The caller zeroes it first.
  *   B, M, N, H, G, D, block_size, T   as for nsa_sel_fwd (H sets how many
  *                 queries share a wavefront slot, as it does there)
+ *   workspace, workspace_bytes  NULL and 0: the launches of nsa_sel_fwd;
+ *                 otherwise a workspace as nsa_sel_fwd_ws takes (at least
+ *                 nsa_sel_fwd_workspace_size() bytes, 256-byte aligned): the
+ *                 launches of nsa_sel_fwd_ws
  *   queries_per_slot  host pointer or NULL; receives the number of
  *                 consecutive queries of one (b, g) that each wavefront slot
  *                 carries (slots start at m = 0, that many apart)
@@ -47,14 +51,15 @@ extern "C" {
  *
  * Behaviour: the checks of nsa_sel_fwd apply (NULL pointers, sizes,
  * supported D / block_size / H/G, alignment: K and V 16 bytes, block_indices
- * 4 bytes, staged 8 bytes), all on the host before any HIP call, with the
+ * 4 bytes, staged 8 bytes; a misaligned or short workspace is
+ * NSA_SEL_ERR_WORKSPACE), all on the host before any HIP call, with the
  * same status codes.  On success the work is queued on `stream` and
  * NSA_SEL_OK is returned; nothing is allocated and nothing synchronises.
  * Inputs are only read.
  */
 int nsa_gather_probe(const void *K, const void *V, const int32_t *block_indices, uint64_t *staged, int B,
-                     int M, int N, int H, int G, int D, int block_size, int T, int *queries_per_slot,
-                     hipStream_t stream);
+                     int M, int N, int H, int G, int D, int block_size, int T, void *workspace,
+                     size_t workspace_bytes, int *queries_per_slot, hipStream_t stream);
 
 #ifdef __cplusplus
 }

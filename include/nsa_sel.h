@@ -41,7 +41,7 @@ enum {
     NSA_SEL_ERR_RANGE = 5,       /* B*M*G units or a tensor size beyond the limits  */
     NSA_SEL_ERR_ALIAS = 6,       /* an output buffer overlaps an input or the other */
     NSA_SEL_ERR_HIP = 7,         /* the HIP runtime reported an error at launch     */
-    NSA_SEL_ERR_WORKSPACE = 8,   /* workspace NULL, misaligned or too small (bwd)   */
+    NSA_SEL_ERR_WORKSPACE = 8,   /* workspace NULL, misaligned or too small         */
     NSA_SEL_ERR_SCRATCH = 9      /* sizes need more than the fixed scratch (bwd)    */
 };
 
@@ -86,6 +86,54 @@ int nsa_sel_fwd(const void *Q, const void *K, const void *V, const int32_t *bloc
 int nsa_sel_fwd_bf16(const void *Q, const void *K, const void *V, const int32_t *block_indices,
                      void *O, float *LSE, int B, int M, int N, int H, int G, int D,
                      int block_size, int T, hipStream_t stream);
+
+/*
+ * nsa_sel_fwd_workspace_size -- bytes of device workspace nsa_sel_fwd_ws and
+ * nsa_sel_fwd_bf16_ws need for these sizes on the current device: an upper
+ * bound that does not depend on the index values (on MI355X about 260 KiB
+ * for one batch of 65536 queries in 8 groups, 520 KiB for 131072).
+ * Sizes are checked as for nsa_sel_fwd; returns NSA_SEL_OK and stores the
+ * size in *bytes, or an error code (NSA_SEL_ERR_NULL when bytes is NULL).
+ * Reads the current device's compute-unit and XCD counts and L2 size (HIP
+ * device attributes, cached per device); queues nothing.
+ */
+int nsa_sel_fwd_workspace_size(int B, int M, int N, int H, int G, int D, int block_size, int T, size_t *bytes);
+
+/*
+ * nsa_sel_fwd_ws, nsa_sel_fwd_bf16_ws -- nsa_sel_fwd and nsa_sel_fwd_bf16
+ * with a workspace, which lets them run as one persistent dispatch.
+ *
+ * Same operation, arguments, checks and results (bitwise) as nsa_sel_fwd and
+ * nsa_sel_fwd_bf16, plus:
+ *   workspace, workspace_bytes  device memory of at least
+ *         nsa_sel_fwd_workspace_size() bytes, 256-byte aligned, overlapping
+ *         no input or output; its contents on entry do not matter (the call
+ *         clears what it uses, on `stream`, with a kernel, not a memset) and
+ *         are unspecified on return.
+ *
+ * Where one (b, g)'s K and V exceed one XCD's L2 (N * D * 4 bytes), the call
+ * queues that clearing kernel and one persistent dispatch in place of one
+ * dispatch per generation: the workgroups of each XCD still run one
+ * generation of wavefront slots at a time, all starting together, but they
+ * wait only for each other, and an XCD whose own share is done takes over
+ * generations of the others.  A share that runs slower (K/V rows at some
+ * address offsets are fetched more slowly) then no longer holds every XCD
+ * back.  For other sizes the call does what nsa_sel_fwd does.
+ *
+ * NSA_SEL_ERR_WORKSPACE for a NULL, misaligned or short workspace,
+ * NSA_SEL_ERR_ALIAS when it overlaps an input or an output.  Two calls that
+ * share a workspace must be ordered (same stream, or synchronised).  The
+ * dispatch expects its workgroups to be resident together (it launches one
+ * per workgroup slot of the device): work of other streams on the same GPU
+ * slows it, since its waits end only after about 0.5 ms, but does not change
+ * its results.
+ */
+int nsa_sel_fwd_ws(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                   void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                   int block_size, int T, void *workspace, size_t workspace_bytes, hipStream_t stream);
+int nsa_sel_fwd_bf16_ws(const void *Q, const void *K, const void *V, const int32_t *block_indices,
+                        void *O, float *LSE, int B, int M, int N, int H, int G, int D,
+                        int block_size, int T, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * nsa_sel_fwd_unpipelined -- verification aid: nsa_sel_fwd (fp16) with the

@@ -55,6 +55,42 @@ int main() {
         rc = f(A(0), A(1), A(2), I, A(4), (float *)A(4), 1, 64, 64, 8, 2, 64, 32, 4, 0);
         expect(rc == NSA_SEL_ERR_ALIAS, "fwd alias outputs", rc);
     }
+    // the workspace forward: size sweep, then rejected calls
+    {
+        size_t n = 0, prev = 0;
+        for (int M = 32; M <= 1 << 17; M *= 2) {
+            int rc = nsa_sel_fwd_workspace_size(1, M, M, 64, 8, 128, 64, 16, &n);
+            expect(rc == NSA_SEL_OK && n >= prev && n % 4 == 0, "fwd workspace grows", rc);
+            prev = n;
+            rc = nsa_sel_fwd_workspace_size(2, M, M + 17, 48, 4, 64, 32, 70, &n);
+            expect(rc == NSA_SEL_OK && n > 0, "fwd workspace ragged", rc);
+        }
+        int rc = nsa_sel_fwd_workspace_size(1, 64, 64, 8, 2, 64, 32, 4, nullptr);
+        expect(rc == NSA_SEL_ERR_NULL, "fwd workspace null", rc);
+        rc = nsa_sel_fwd_workspace_size(1, 64, 64, 8, 3, 64, 32, 4, &n);
+        expect(rc == NSA_SEL_ERR_SHAPE, "fwd workspace shape", rc);
+        const int32_t *I = (const int32_t *)A(3);
+        float *L = (float *)A(5);
+        size_t need = 0;
+        nsa_sel_fwd_workspace_size(1, 64, 64, 8, 2, 64, 32, 4, &need);
+        typedef int (*FwdWs)(const void *, const void *, const void *, const int32_t *, void *, float *, int, int,
+                             int, int, int, int, int, int, void *, size_t, hipStream_t);
+        const FwdWs fws[2] = {nsa_sel_fwd_ws, nsa_sel_fwd_bf16_ws};
+        for (FwdWs f : fws) {
+            rc = f(A(0), A(1), A(2), I, A(4), L, 1, 64, 64, 8, 2, 64, 32, 4, nullptr, need, 0);
+            expect(rc == NSA_SEL_ERR_WORKSPACE, "fwd_ws null workspace", rc);
+            rc = f(A(0), A(1), A(2), I, A(4), L, 1, 64, 64, 8, 2, 64, 32, 4, A(6), need - 1, 0);
+            expect(rc == NSA_SEL_ERR_WORKSPACE, "fwd_ws short workspace", rc);
+            rc = f(A(0), A(1), A(2), I, A(4), L, 1, 64, 64, 8, 2, 64, 32, 4, (char *)A(6) + 16, need, 0);
+            expect(rc == NSA_SEL_ERR_WORKSPACE, "fwd_ws misaligned workspace", rc);
+            rc = f(A(0), A(1), A(2), I, A(4), L, 1, 64, 64, 8, 2, 64, 32, 4, A(1), need, 0);
+            expect(rc == NSA_SEL_ERR_ALIAS, "fwd_ws workspace over K", rc);
+            rc = f(nullptr, A(1), A(2), I, A(4), L, 1, 64, 64, 8, 2, 64, 32, 4, A(6), need, 0);
+            expect(rc == NSA_SEL_ERR_NULL, "fwd_ws null", rc);
+            rc = f(A(0), A(1), A(2), I, A(4), L, 1, 64, 64, 8, 2, 96, 32, 4, A(6), need, 0);
+            expect(rc == NSA_SEL_ERR_UNSUPPORTED, "fwd_ws D", rc);
+        }
+    }
     // dense and window
     {
         int rc = nsa_dense_fwd(A(0), A(1), nullptr, A(4), (float *)A(5), 1, 64, 64, 8, 2, 64, 0);

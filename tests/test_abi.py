@@ -102,6 +102,54 @@ def test_alias(lib):
     assert _call(L=ADDR["O"] + 256) == binding.NSA_SEL_ERR_ALIAS
 
 
+# A fake 256-byte aligned workspace address, far from the tensors above.
+WS = 1 << 44
+
+
+def _call_ws(ws=WS, nbytes=1 << 30, **over):
+    args = dict(GOOD)
+    ptrs = dict(ADDR)
+    for k in list(over):
+        if k in ptrs:
+            ptrs[k] = over.pop(k)
+    args.update(over)
+    return binding.nsa_sel_fwd_ws_raw(ptrs["Q"], ptrs["K"], ptrs["V"], ptrs["I"], ptrs["O"], ptrs["L"],
+                                      args["B"], args["M"], args["N"], args["H"], args["G"], args["D"],
+                                      args["block_size"], args["T"], ws, nbytes, 0)
+
+
+@pytest.mark.parametrize("over", [dict(Q=0), dict(L=0), dict(M=0), dict(H=8, G=3), dict(D=96), dict(K=ADDR["K"] + 2),
+                                  dict(O=ADDR["Q"]), dict(B=1 << 12, M=1 << 20, G=1, H=1)])
+def test_workspace_forward_checks_like_the_forward(lib, over):
+    # The argument checks of nsa_sel_fwd come first, with the same codes.
+    assert _call_ws(**dict(over)) == _call(**dict(over)) != binding.NSA_SEL_OK
+
+
+def test_fwd_workspace_size(lib):
+    rc, n = binding.nsa_sel_fwd_workspace_size_raw(*GOOD.values())
+    assert rc == binding.NSA_SEL_OK and n > 0 and n % 4 == 0
+    rc, n2 = binding.nsa_sel_fwd_workspace_size_raw(*dict(GOOD, M=65536, N=65536).values())
+    assert rc == binding.NSA_SEL_OK and n2 > n
+    assert binding.nsa_sel_fwd_workspace_size_raw(*dict(GOOD, M=0).values())[0] == binding.NSA_SEL_ERR_SHAPE
+    assert binding.nsa_sel_fwd_workspace_size_raw(*dict(GOOD, D=96).values())[0] == binding.NSA_SEL_ERR_UNSUPPORTED
+    assert lib.nsa_sel_fwd_workspace_size(*GOOD.values(), None) == binding.NSA_SEL_ERR_NULL
+
+
+def test_workspace_forward_rejects_bad_workspaces(lib):
+    need = binding.nsa_sel_fwd_workspace_size(*GOOD.values())
+    assert _call_ws(ws=0) == binding.NSA_SEL_ERR_WORKSPACE
+    assert _call_ws(ws=WS + 128) == binding.NSA_SEL_ERR_WORKSPACE
+    assert _call_ws(nbytes=need - 1) == binding.NSA_SEL_ERR_WORKSPACE
+    assert _call_ws(nbytes=0) == binding.NSA_SEL_ERR_WORKSPACE
+    for name in ("Q", "K", "V", "I", "O", "L"):
+        assert _call_ws(ws=ADDR[name]) == binding.NSA_SEL_ERR_ALIAS, name
+    o_bytes = GOOD["B"] * GOOD["M"] * GOOD["H"] * GOOD["D"] * 2
+    assert _call_ws(ws=ADDR["O"] + o_bytes - 256) == binding.NSA_SEL_ERR_ALIAS  # O's last 256 bytes
+    with pytest.raises(binding.NsaSelError) as ei:
+        binding.nsa_sel_fwd_ws(*[ADDR[n] for n in ("Q", "K", "V", "I", "O", "L")], *GOOD.values(), 0, 0)
+    assert ei.value.status == binding.NSA_SEL_ERR_WORKSPACE and "workspace" in str(ei.value)
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(binding.NsaSelError) as ei:
         binding.nsa_sel_fwd(0, 1, 2, 3, 4, 5, 1, 1, 1, 1, 1, 64, 32, 1, 0)
@@ -173,6 +221,13 @@ def test_probe_bad_sizes(probe_lib, over, code):
 @pytest.mark.parametrize("which,off", [("K", 8), ("V", 2), ("I", 2), ("S", 4)])
 def test_probe_misaligned(probe_lib, which, off):
     assert _probe_call(**{which: PADDR[which] + off}) == binding.NSA_SEL_ERR_ALIGN
+
+
+def test_probe_rejects_bad_workspaces(probe_lib, lib):
+    need = binding.nsa_sel_fwd_workspace_size(*GOOD.values())
+    args = [PADDR["K"], PADDR["V"], PADDR["I"], PADDR["S"], *GOOD.values(), 0]
+    assert binding.nsa_gather_probe_raw(*args, WS + 64, need)[0] == binding.NSA_SEL_ERR_WORKSPACE
+    assert binding.nsa_gather_probe_raw(*args, WS, need - 4)[0] == binding.NSA_SEL_ERR_WORKSPACE
 
 
 # --- dense causal attention (include/nsa_dense.h) ----------------------------
