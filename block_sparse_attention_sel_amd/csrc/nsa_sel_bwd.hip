@@ -279,12 +279,48 @@ void nsa_sel_bwd_dq_kernel(Params p, DqArgs x) {
                                                                         vbuf_all[wave], nullptr);
 }
 
+// The same slots run by the persistent schedule of the forward (run_persistent):
+// one workgroup per workgroup slot of the device, the workgroups of each XCD
+// taking one generation per step and, once their own range is done,
+// generations of other XCDs.  Each slot runs once with the same code, so dQ
+// and the row statistics are bitwise those of the generation launches.
+template <int BS, int SPLIT, int D, int PACK, int MODE>
+__global__ __launch_bounds__(kWaveSize * waves_per_wg(BS / SPLIT)) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void nsa_sel_bwd_dq_persistent_kernel(Params p, DqArgs x) {
+    constexpr int SBS = BS / SPLIT;
+    constexpr int WAVES = waves_per_wg(SBS);
+    const int lane = threadIdx.x & (kWaveSize - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ __attribute__((aligned(16))) _Float16 kbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) _Float16 vbuf_all[WAVES][Stage<SBS, D>::HALVES];
+    __shared__ __attribute__((aligned(16))) unsigned char mbuf_all[MODE == 0 ? WAVES : 1][MODE == 0 ? kMapBlocks : 16];
+    run_persistent<WAVES>(p, wave, lane, [&](int ws) {
+        if constexpr (MODE == 0)
+            dq_slot<BS, SPLIT, D, PACK, 1, MapMerger<PACK, BS>>(p, x, ws, lane, kbuf_all[wave], vbuf_all[wave],
+                                                                 mbuf_all[wave]);
+        else
+            dq_slot<BS, SPLIT, D, PACK, MODE, RegMerger<PACK * MODE, BS>>(p, x, ws, lane, kbuf_all[wave],
+                                                                            vbuf_all[wave], nullptr);
+    });
+}
+
 struct DqKernel {
-    static constexpr bool kPersistent = false;
+    static constexpr bool kPersistent = true;
     DqArgs x;
     template <int BS, int SPLIT, int D, int PACK, int MODE>
     void launch(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
         hipLaunchKernelGGL((nsa_sel_bwd_dq_kernel<BS, SPLIT, D, PACK, MODE>), grid, block, 0, stream, p, x);
+    }
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    void launch_persist(dim3 grid, dim3 block, hipStream_t stream, const Params &p) const {
+        hipLaunchKernelGGL((nsa_sel_bwd_dq_persistent_kernel<BS, SPLIT, D, PACK, MODE>), grid, block, 0, stream, p,
+                           x);
+    }
+    template <int BS, int SPLIT, int D, int PACK, int MODE>
+    int resident() const {
+        static std::atomic<int> cache[64];
+        return resident_workgroups(cache, (const void *)nsa_sel_bwd_dq_persistent_kernel<BS, SPLIT, D, PACK, MODE>,
+                                   kWaveSize * waves_per_wg(BS / SPLIT));
     }
 };
 
@@ -910,14 +946,20 @@ struct BwdPlan {
     int NB, MW, R, qc, kmax, qpt;
     int64_t cap, pcap;
     size_t off_rowstat, off_bits, off_row_items, off_row_first, off_row_part, off_starts, off_items, off_nitems,
-        off_part, total;
+        off_part, off_sched, total;
+    int64_t sched_words;  // schedule of the persistent dQ pass
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Sizes of the workspace for (B, M, N, H, G, D, bs, T); p must hold the
-// checked sizes.  Returns NSA_SEL_OK or NSA_SEL_ERR_RANGE.
-int bwd_plan(const Params &p, int D, int bs, BwdPlan &pl) {
+// Sizes of the workspace for (B, M, N, H, G, D, bs, T) on a device of
+// topology tp; p must hold the checked sizes and is planned in place
+// (plan_slots: the dQ pass's slots, whose persistent schedule the workspace
+// holds).  Returns NSA_SEL_OK or NSA_SEL_ERR_RANGE.
+int bwd_plan(Params &p, const Topology &tp, int D, int bs, BwdPlan &pl) {
+    plan_slots(p, tp);
+    pl.sched_words = sched_words_bound(p, tp.cus);
+    if (pl.sched_words > INT_MAX) return NSA_SEL_ERR_RANGE;
     pl.NB = p.NB;
     pl.MW = (p.M + 31) / 32;
     const int64_t R = (int64_t)p.B * p.G * p.NB;
@@ -961,6 +1003,8 @@ int bwd_plan(const Params &p, int D, int bs, BwdPlan &pl) {
     o = align256(o + (size_t)pl.cap * 8);
     pl.off_part = o;
     o = align256(o + (size_t)pl.pcap * 2 * bs * D * 4);
+    pl.off_sched = o;
+    o = align256(o + (size_t)pl.sched_words * 4);
     pl.total = o;
     return NSA_SEL_OK;
 }
@@ -987,7 +1031,7 @@ extern "C" int nsa_sel_bwd_workspace_size(int B, int M, int N, int H, int G, int
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
     if (st != NSA_SEL_OK) return st;
     BwdPlan pl;
-    const int st2 = bwd_plan(p, D, block_size, pl);
+    const int st2 = bwd_plan(p, device_topology(), D, block_size, pl);
     if (st2 != NSA_SEL_OK) return st2;
     *bytes = pl.total;
     return NSA_SEL_OK;
@@ -1007,8 +1051,9 @@ int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_in
     Params p;
     const int st = check_sizes(B, M, N, H, G, D, block_size, T, p);
     if (st != NSA_SEL_OK) return st;
+    const Topology tp = device_topology();
     BwdPlan pl;
-    const int st2 = bwd_plan(p, D, block_size, pl);
+    const int st2 = bwd_plan(p, tp, D, block_size, pl);
     if (st2 != NSA_SEL_OK) return st2;
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O | (uintptr_t)dO | (uintptr_t)dQ |
          (uintptr_t)dK | (uintptr_t)dV) & 15)
@@ -1034,9 +1079,7 @@ int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_in
             if (ranges_overlap(outs[o], out_bytes[o], outs[o2], out_bytes[o2])) return NSA_SEL_ERR_ALIAS;
     }
 
-    const Topology tp = device_topology();
     const int cus = tp.cus;
-    plan_slots(p, tp);
     p.Q = (const _Float16 *)Q;
     p.K = (const _Float16 *)K;
     p.V = (const _Float16 *)V;
@@ -1044,6 +1087,8 @@ int sel_bwd(const void *Q, const void *K, const void *V, const int32_t *block_in
     p.O = nullptr;
     p.LSE = nullptr;
     char *ws = (char *)workspace;
+    p.sched = (unsigned *)(ws + pl.off_sched);
+    p.sched_cap = (int)pl.sched_words;
     float2 *rowstat = (float2 *)(ws + pl.off_rowstat);
     DqKernel f;
     f.x.O = (const _Float16 *)O;

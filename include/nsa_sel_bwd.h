@@ -38,10 +38,15 @@ extern "C" {
 
 /*
  * nsa_sel_bwd_workspace_size -- bytes of device workspace nsa_sel_bwd needs
- * for these sizes (an upper bound that does not depend on the index values).
- * Sizes are checked as for nsa_sel_fwd; returns NSA_SEL_OK and stores the
- * size in *bytes, or an error code (NSA_SEL_ERR_NULL when bytes is NULL).
- * Makes no HIP call.
+ * for these sizes on the current device (an upper bound that does not depend
+ * on the index values).  It holds the inverted index and partial sums of the
+ * key-major pass and the schedule of the query-major dQ pass, which runs as
+ * one persistent dispatch (as nsa_sel_fwd_ws does) when one group's K and V
+ * exceed the L2 of one XCD.  Sizes are checked as for nsa_sel_fwd; returns
+ * NSA_SEL_OK and stores the size in *bytes, or an error code
+ * (NSA_SEL_ERR_NULL when bytes is NULL).  Reads the current device's
+ * compute-unit and XCD counts and L2 size (HIP device attributes, cached per
+ * device); queues nothing.
  */
 int nsa_sel_bwd_workspace_size(int B, int M, int N, int H, int G, int D, int block_size, int T, size_t *bytes);
 
@@ -67,7 +72,7 @@ int nsa_sel_bwd_workspace_size(int B, int M, int N, int H, int G, int D, int blo
  *         workspace is unspecified on return
  *   B, M, N, H, G, D, block_size, T, stream   as for nsa_sel_fwd
  *
- * Behaviour: every argument is checked on the host before any HIP call, with
+ * Behaviour: every argument is checked on the host before any work is queued, with
  * the forward's status codes (Q/K/V/O/dO and dQ/dK/dV must be 16-byte
  * aligned, block_indices and LSE 4-byte aligned; outputs and workspace may
  * not overlap the inputs or each other; NSA_SEL_ERR_WORKSPACE for a NULL,
@@ -92,7 +97,7 @@ int nsa_sel_bwd(const void *Q, const void *K, const void *V, const int32_t *bloc
  * first call on that GPU until the process ends; the call allocates nothing
  * and calls no allocating routine.  Sizes whose workspace
  * (nsa_sel_bwd_workspace_size) exceeds 64 MiB return NSA_SEL_ERR_SCRATCH
- * before any HIP call (for example the 8192-query shape with 32 heads in 2
+ * before any work is queued (for example the 8192-query shape with 32 heads in 2
  * groups, D = 128, block_size 64, T = 16 fits; a 64k-query shape does not).
  * Every call on a GPU shares that GPU's array and leaves its last contents
  * there: calls that may overlap on one GPU (different streams, or threads
