@@ -78,11 +78,27 @@ __device__ __forceinline__ void dq_scores(const half8 (&kf)[SBS / 16][D / 32], c
     }
 }
 
+// The lane id, recomputed where it is used.  The dQ step holds nearly 256
+// live registers, and a per-lane value kept across the sub-block loop gets
+// spilled; its reload waits for every copy in flight (vmcnt(0)), which
+// exposes the next sub-block's copy latency.  Two VALU instructions instead.
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// Query of the tile (0 .. 15) that column r (0 .. 15) belongs to, r / gs,
+// as (r * ceil(2^16 / gs)) >> 16, which is exact for r < 16 and gs <= 16.
+__device__ __forceinline__ int col_query(int r, unsigned gs_magic) { return (int)(__umul24((unsigned)r, gs_magic) >> 16); }
+
+//   tbits: bit q set when query q of the tile selected the block and is live
+//   first_m: the tile's first query; lim = min(first_m + (l%16) / gs, N - 1)
 template <int SBS, int D>
 __device__ __forceinline__ void dq_grad(const half8 (&vf)[SBS / 16][D / 32], const half4 (&kt)[SBS / 32][D / 32][2][2],
-                                        const half8 (&df)[D / 32], const float4v (&s)[SBS / 16], int key0,
-                                        bool causal, bool col_on, int lim, float scale_log2, float lse2, float delta,
-                                        float4v (&acc)[D / 32][2], int q4) {
+                                        const half8 (&df)[D / 32], float4v (&s)[SBS / 16], int key0,
+                                        bool causal, unsigned tbits, int first_m, int n_keys, unsigned gs_magic,
+                                        float scale_log2, float lse2, float delta, float4v (&acc)[D / 32][2]) {
     constexpr int KT = SBS / 16;
     constexpr int DC = D / 32;
     float4v dp[KT];
@@ -92,16 +108,28 @@ __device__ __forceinline__ void dq_grad(const half8 (&vf)[SBS / 16][D / 32], con
 #pragma unroll
         for (int c = 0; c < DC; ++c) dp[k] = mfma_16x16x32(vf[k][c], df[c], dp[k]);
     }
-    // A column that did not select the block gets P = exp2(-inf) = 0.
+    // A column whose query did not select the block gets P = exp2(-inf) = 0,
+    // and so does a key past the column's last visible one (masked under a
+    // wave-uniform branch: only the sub-blocks on the diagonal take it).
+    const int cq = col_query(fresh_lane() & 15, gs_magic);
+    const bool col_on = (tbits >> cq) & 1u;
     const float m_exp = (col_on && lse2 != -INFINITY) ? lse2 : INFINITY;
+    if (causal) {
+        const int l = fresh_lane();
+        const int lim = min(first_m + col_query(l & 15, gs_magic), n_keys - 1) - key0 - 4 * (l >> 4);
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (k * 16 + i > lim) s[k][i] = -INFINITY;
+    }
     half4 dsf[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
         float4v ds;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float pv = fast_exp2(__builtin_fmaf(s[k][i], scale_log2, -m_exp));
-            if (causal && key0 + k * 16 + q4 * 4 + i > lim) pv = 0.f;
+            const float pv = fast_exp2(__builtin_fmaf(s[k][i], scale_log2, -m_exp));
             ds[i] = pv * (dp[k][i] - delta);
         }
         dsf[k] = to_half4(ds);
@@ -184,6 +212,14 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
 
     constexpr int NI = Stage<SBS, D>::NI;
     const unsigned tile_bits = (1u << PACK) - 1u;
+    // Live queries of each tile (a query past the end of the rows is not).
+    const unsigned gs_magic = (65536u + (unsigned)p.gs - 1u) / (unsigned)p.gs;
+    unsigned live_bits[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n_live = min(max(nq - nt * PACK, 0), PACK);
+        live_bits[nt] = (1u << n_live) - 1u;
+    }
 
     // Same pipeline as the forward: K(s1) is issued once K(s0)'s row and
     // transposed fragments are in registers, V(s1) once V(s0)'s are.
@@ -231,9 +267,8 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
             if (tb == 0) continue;
             const int first_m = m0 + nt * PACK;
             const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
-            const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
-            dq_grad<SBS, D>(vf, kt, df[nt], sc[nt], key0, causal, col_on, min(my_m[nt], p.N - 1), p.scale_log2,
-                            lse2[nt], delta[nt], acc[nt], q4);
+            dq_grad<SBS, D>(vf, kt, df[nt], sc[nt], key0, causal, tb & live_bits[nt], first_m, p.N, gs_magic,
+                            p.scale_log2, lse2[nt], delta[nt], acc[nt]);
         }
         __builtin_amdgcn_s_setprio(0);
         s0 = s1;
