@@ -157,7 +157,7 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             const int first_m = m0 + nt * PACK;
             const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
             const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
-            score_block<SBS, D, BF16>(kf, qf[nt], key0, causal, true, col_on, INT_MIN, min(my_m[nt], p.N - 1),
+            score_block<SBS, D, BF16, false>(kf, qf[nt], key0, causal, true, col_on, INT_MIN, min(my_m[nt], p.N - 1),
                                       p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
         }
         __builtin_amdgcn_s_setprio(0);

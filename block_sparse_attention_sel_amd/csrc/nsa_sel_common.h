@@ -593,18 +593,30 @@ __device__ __forceinline__ void qk_tile(const half8 (&kf)[SBS / 16][D / 32], con
 // give the same P wherever the running max is kept.
 constexpr float kLazyMax = 8.0f;
 
-template <int KT, bool BF16 = false>
+// LO: keys below lo are masked too (a window's left edge); without it lo is
+// ignored and the test is against lim alone, relative to the lane's first
+// key, so that nothing per score is computed outside the masked branch.
+template <int KT, bool BF16 = false, bool LO = true>
 __device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool causal, bool col_mask, bool col_on,
                                              int lo, int lim, float scale_log2, float &m_run, float &l_run,
                                              float &alpha, half4 (&pf)[KT], int q4) {
     if (causal) {
+        if constexpr (LO) {
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = key0 + kt * 16 + q4 * 4 + i;
-                if (key > lim || key < lo) s[kt][i] = -INFINITY;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const int key = key0 + kt * 16 + q4 * 4 + i;
+                    if (key > lim || key < lo) s[kt][i] = -INFINITY;
+                }
+        } else {
+            const int hi_rel = lim - (key0 + q4 * 4);
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (kt * 16 + i > hi_rel) s[kt][i] = -INFINITY;
+        }
     }
     const bool off = col_mask && !col_on;
     {
@@ -663,14 +675,15 @@ __device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool ca
 }
 
 // qk_tile and softmax_tile in one step.
-template <int BS, int D, bool BF16 = false>
+template <int BS, int D, bool BF16 = false, bool LO = true>
 __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
                                             int key0, bool causal, bool col_mask, bool col_on, int lo, int lim,
                                             float scale_log2, float &m_run, float &l_run,
                                             float &alpha, half4 (&pf)[BS / 16], int q4) {
     float4v s[BS / 16];
     qk_tile<BS, D, BF16>(kf, qf, s);
-    softmax_tile<BS / 16, BF16>(s, key0, causal, col_mask, col_on, lo, lim, scale_log2, m_run, l_run, alpha, pf, q4);
+    softmax_tile<BS / 16, BF16, LO>(s, key0, causal, col_mask, col_on, lo, lim, scale_log2, m_run, l_run, alpha, pf,
+                                    q4);
 }
 
 // O^T = alpha * O^T + V^T * P^T over 32-key chunks.  acc[c][hh] holds O^T rows
