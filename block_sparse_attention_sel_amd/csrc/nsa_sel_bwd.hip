@@ -35,6 +35,7 @@
 #include "nsa_sel_bwd.h"
 
 #include <mutex>
+#include <type_traits>
 
 // Scratch of the allocation-free entry point (nsa_sel_bwd_noalloc): its
 // workspace lives in this file-scope device array, one copy per GPU, held for
@@ -92,13 +93,39 @@ __device__ __forceinline__ int fresh_lane() {
 // as (r * ceil(2^16 / gs)) >> 16, which is exact for r < 16 and gs <= 16.
 __device__ __forceinline__ int col_query(int r, unsigned gs_magic) { return (int)(__umul24((unsigned)r, gs_magic) >> 16); }
 
+// The lanes whose column belongs to a query set in tbits (bit q: query q of
+// the tile, columns q*gs .. q*gs+gs-1 of each 16-lane row), as a wave-wide
+// mask built on the scalar unit.
+template <int PACK>
+__device__ __forceinline__ uint64_t col_lanes(unsigned tbits, int gs) {
+    const unsigned g = (1u << gs) - 1u;
+    unsigned m16 = 0;
+#pragma unroll
+    for (int q = 0; q < PACK; ++q)
+        if ((tbits >> q) & 1u) m16 |= g << (q * gs);
+    const uint64_t m32 = (uint64_t)(m16 | (m16 << 16));
+    return m32 | (m32 << 32);
+}
+
+// Per lane: if1 where the lane's bit of mask is set, else if0 (one
+// v_cndmask with the mask in scalar registers).
+__device__ __forceinline__ float select_lanes(uint64_t mask, float if0, float if1) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if0), "v"(if1), "s"(mask));
+    return r;
+}
+
 //   tbits: bit q set when query q of the tile selected the block and is live
 //   first_m: the tile's first query; lim = min(first_m + (l%16) / gs, N - 1)
-template <int SBS, int D>
+//   lse2e: the column's LSE log2(e), or +inf for a row with no visible key
+//   SMASK: select the columns with a scalar lane mask (PACK <= 4; not with
+//   the block-map merger, whose state already fills the scalar registers)
+template <int SBS, int D, int PACK, bool SMASK>
 __device__ __forceinline__ void dq_grad(const half8 (&vf)[SBS / 16][D / 32], const half4 (&kt)[SBS / 32][D / 32][2][2],
                                         const half8 (&df)[D / 32], float4v (&s)[SBS / 16], int key0,
-                                        bool causal, unsigned tbits, int first_m, int n_keys, unsigned gs_magic,
-                                        float scale_log2, float lse2, float delta, float4v (&acc)[D / 32][2]) {
+                                        bool causal, unsigned tbits, int first_m, int n_keys, int gs,
+                                        unsigned gs_magic, float scale_log2, float lse2e, float delta,
+                                        float4v (&acc)[D / 32][2]) {
     constexpr int KT = SBS / 16;
     constexpr int DC = D / 32;
     float4v dp[KT];
@@ -111,9 +138,13 @@ __device__ __forceinline__ void dq_grad(const half8 (&vf)[SBS / 16][D / 32], con
     // A column whose query did not select the block gets P = exp2(-inf) = 0,
     // and so does a key past the column's last visible one (masked under a
     // wave-uniform branch: only the sub-blocks on the diagonal take it).
-    const int cq = col_query(fresh_lane() & 15, gs_magic);
-    const bool col_on = (tbits >> cq) & 1u;
-    const float m_exp = (col_on && lse2 != -INFINITY) ? lse2 : INFINITY;
+    float m_exp;
+    if constexpr (SMASK) {
+        m_exp = select_lanes(col_lanes<PACK>(tbits, gs), INFINITY, lse2e);
+    } else {
+        const int cq = col_query(fresh_lane() & 15, gs_magic);
+        m_exp = ((tbits >> cq) & 1u) ? lse2e : INFINITY;
+    }
     if (causal) {
         const int l = fresh_lane();
         const int lim = min(first_m + col_query(l & 15, gs_magic), n_keys - 1) - key0 - 4 * (l >> 4);
@@ -211,7 +242,11 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
         }
 
     constexpr int NI = Stage<SBS, D>::NI;
+    constexpr bool kScalarMask = PACK <= 4 && !std::is_same<Merger, MapMerger<PACK, BS>>::value;
     const unsigned tile_bits = (1u << PACK) - 1u;
+    float lse2e[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) lse2e[nt] = lse2[nt] == -INFINITY ? INFINITY : lse2[nt];
     // Live queries of each tile (a query past the end of the rows is not).
     const unsigned gs_magic = (65536u + (unsigned)p.gs - 1u) / (unsigned)p.gs;
     unsigned live_bits[NT];
@@ -267,8 +302,8 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
             if (tb == 0) continue;
             const int first_m = m0 + nt * PACK;
             const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
-            dq_grad<SBS, D>(vf, kt, df[nt], sc[nt], key0, causal, tb & live_bits[nt], first_m, p.N, gs_magic,
-                            p.scale_log2, lse2[nt], delta[nt], acc[nt]);
+            dq_grad<SBS, D, PACK, kScalarMask>(vf, kt, df[nt], sc[nt], key0, causal, tb & live_bits[nt], first_m, p.N, p.gs,
+                                  gs_magic, p.scale_log2, lse2e[nt], delta[nt], acc[nt]);
         }
         __builtin_amdgcn_s_setprio(0);
         s0 = s1;
