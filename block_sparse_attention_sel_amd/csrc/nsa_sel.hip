@@ -29,6 +29,8 @@
 //    in step and share its L2.
 #include "nsa_sel_common.h"
 
+#include <type_traits>
+
 namespace {
 
 // One wavefront slot: QW = PACK * NT consecutive queries m0 .. m0+nq-1 of one
@@ -111,6 +113,13 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
 
     constexpr int NI = Stage<SBS, D>::NI;
     const unsigned tile_bits = (1u << PACK) - 1u;
+    // The columns taking part in a block as a scalar lane mask, with up to
+    // four queries per tile (not with the block-map merger, whose state
+    // already fills the scalar registers).
+    constexpr bool kScalarMask = PACK <= 4 && !std::is_same<Merger, MapMerger<PACK, BS>>::value;
+    unsigned live_bits[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) live_bits[nt] = (1u << min(max(nq - nt * PACK, 0), PACK)) - 1u;
 
     // Pipeline over the merged sequence of sub-blocks (block t, part h): while
     // sub-block s0 is computed, the copies of the next one s1 into LDS are in
@@ -157,8 +166,10 @@ __device__ __forceinline__ void run_slot(const Params &p, int ws, int lane, _Flo
             const int first_m = m0 + nt * PACK;
             const bool causal = (key0 + SBS - 1 > first_m) || (key0 + SBS > p.N);
             const bool col_on = live[nt] && ((tb >> q_in_tile) & 1u);
-            score_block<SBS, D, BF16, false>(kf, qf[nt], key0, causal, true, col_on, INT_MIN, min(my_m[nt], p.N - 1),
-                                      p.scale_log2, m_run[nt], l_run[nt], alpha[nt], pf[nt], q4);
+            const uint64_t on_lanes = kScalarMask ? col_lanes<PACK>(tb & live_bits[nt], p.gs) : 0;
+            score_block<SBS, D, BF16, false, kScalarMask>(kf, qf[nt], key0, causal, true, col_on, INT_MIN,
+                                                          min(my_m[nt], p.N - 1), p.scale_log2, m_run[nt],
+                                                          l_run[nt], alpha[nt], pf[nt], q4, on_lanes);
         }
         __builtin_amdgcn_s_setprio(0);
         if (PIPE && has1)

@@ -93,28 +93,6 @@ __device__ __forceinline__ int fresh_lane() {
 // as (r * ceil(2^16 / gs)) >> 16, which is exact for r < 16 and gs <= 16.
 __device__ __forceinline__ int col_query(int r, unsigned gs_magic) { return (int)(__umul24((unsigned)r, gs_magic) >> 16); }
 
-// The lanes whose column belongs to a query set in tbits (bit q: query q of
-// the tile, columns q*gs .. q*gs+gs-1 of each 16-lane row), as a wave-wide
-// mask built on the scalar unit.
-template <int PACK>
-__device__ __forceinline__ uint64_t col_lanes(unsigned tbits, int gs) {
-    const unsigned g = (1u << gs) - 1u;
-    unsigned m16 = 0;
-#pragma unroll
-    for (int q = 0; q < PACK; ++q)
-        if ((tbits >> q) & 1u) m16 |= g << (q * gs);
-    const uint64_t m32 = (uint64_t)(m16 | (m16 << 16));
-    return m32 | (m32 << 32);
-}
-
-// Per lane: if1 where the lane's bit of mask is set, else if0 (one
-// v_cndmask with the mask in scalar registers).
-__device__ __forceinline__ float select_lanes(uint64_t mask, float if0, float if1) {
-    float r;
-    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if0), "v"(if1), "s"(mask));
-    return r;
-}
-
 //   tbits: bit q set when query q of the tile selected the block and is live
 //   first_m: the tile's first query; lim = min(first_m + (l%16) / gs, N - 1)
 //   lse2e: the column's LSE log2(e), or +inf for a row with no visible key

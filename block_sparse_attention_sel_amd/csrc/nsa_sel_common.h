@@ -593,13 +593,37 @@ __device__ __forceinline__ void qk_tile(const half8 (&kf)[SBS / 16][D / 32], con
 // give the same P wherever the running max is kept.
 constexpr float kLazyMax = 8.0f;
 
+// The lanes whose column belongs to a query set in tbits (bit q: query q of
+// a 16-column tile, columns q*gs .. q*gs+gs-1 of each 16-lane row), as a
+// wave-wide mask built on the scalar unit.
+template <int PACK>
+__device__ __forceinline__ uint64_t col_lanes(unsigned tbits, int gs) {
+    const unsigned g = (1u << gs) - 1u;
+    unsigned m16 = 0;
+#pragma unroll
+    for (int q = 0; q < PACK; ++q)
+        if ((tbits >> q) & 1u) m16 |= g << (q * gs);
+    const uint64_t m32 = (uint64_t)(m16 | (m16 << 16));
+    return m32 | (m32 << 32);
+}
+
+// Per lane: if1 where the lane's bit of mask is set, else if0 (one
+// v_cndmask with the mask in scalar registers).
+__device__ __forceinline__ float select_lanes(uint64_t mask, float if0, float if1) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(if0), "v"(if1), "s"(mask));
+    return r;
+}
+
 // LO: keys below lo are masked too (a window's left edge); without it lo is
 // ignored and the test is against lim alone, relative to the lane's first
 // key, so that nothing per score is computed outside the masked branch.
-template <int KT, bool BF16 = false, bool LO = true>
+// SMASK: the columns taking part are the lanes set in on_lanes (a scalar
+// mask) instead of those with col_on (col_mask and col_on are then unused).
+template <int KT, bool BF16 = false, bool LO = true, bool SMASK = false>
 __device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool causal, bool col_mask, bool col_on,
                                              int lo, int lim, float scale_log2, float &m_run, float &l_run,
-                                             float &alpha, half4 (&pf)[KT], int q4) {
+                                             float &alpha, half4 (&pf)[KT], int q4, uint64_t on_lanes = 0) {
     if (causal) {
         if constexpr (LO) {
 #pragma unroll
@@ -619,8 +643,15 @@ __device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool ca
         }
     }
     const bool off = col_mask && !col_on;
+    // if_off for a column left out of this block, else if_on.
+    auto pick = [&](float if_off, float if_on) -> float {
+        if constexpr (SMASK)
+            return select_lanes(on_lanes, if_off, if_on);
+        else
+            return off ? if_off : if_on;
+    };
     {
-        const float m_keep = off ? INFINITY : m_run;
+        const float m_keep = pick(INFINITY, m_run);
         float x[KT][4];
         float xmax = -INFINITY;
 #pragma unroll
@@ -629,15 +660,17 @@ __device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool ca
             for (int i = 0; i < 4; ++i) x[kt][i] = __builtin_fmaf(s[kt][i], scale_log2, -m_keep);
             xmax = fmaxf(xmax, fmaxf(fmaxf(x[kt][0], x[kt][1]), fmaxf(x[kt][2], x[kt][3])));
         }
-        if (!__builtin_amdgcn_ballot_w64(xmax > kLazyMax || m_keep == -INFINITY)) {
-            float psum = 0.f;
+        // Two ballots of plain compares (one of the combined condition makes
+        // the compiler round-trip it through a vector register).
+        if (!(__builtin_amdgcn_ballot_w64(xmax > kLazyMax) | __builtin_amdgcn_ballot_w64(m_keep == -INFINITY))) {
+            float psum;
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) {
                 float4v pv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     pv[i] = fast_exp2(x[kt][i]);
-                    psum += pv[i];
+                    psum = (kt == 0 && i == 0) ? pv[i] : psum + pv[i];
                 }
                 pf[kt] = pack4<BF16>(pv);
             }
@@ -653,21 +686,20 @@ __device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool ca
     for (int kt = 0; kt < KT; ++kt) mloc = fmaxf(mloc, fmaxf(fmaxf(s[kt][0], s[kt][1]), fmaxf(s[kt][2], s[kt][3])));
     mloc = col_max(mloc);
     const float m_blk = mloc * scale_log2;
-    float m_new = (m_blk > m_run + kLazyMax) ? m_blk : m_run;
-    if (off) m_new = m_run;
+    const float m_new = pick(m_run, (m_blk > m_run + kLazyMax) ? m_blk : m_run);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     alpha = (m_new == m_run) ? 1.f : fast_exp2(m_run - m_use);
     m_run = m_new;
     // A column left out of this block gets P = exp2(-inf) = 0.
-    const float m_exp = off ? INFINITY : m_use;
-    float psum = 0.f;
+    const float m_exp = pick(INFINITY, m_use);
+    float psum;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
         float4v pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             pv[i] = fast_exp2(__builtin_fmaf(s[kt][i], scale_log2, -m_exp));
-            psum += pv[i];
+            psum = (kt == 0 && i == 0) ? pv[i] : psum + pv[i];
         }
         pf[kt] = pack4<BF16>(pv);
     }
@@ -675,15 +707,15 @@ __device__ __forceinline__ void softmax_tile(float4v (&s)[KT], int key0, bool ca
 }
 
 // qk_tile and softmax_tile in one step.
-template <int BS, int D, bool BF16 = false, bool LO = true>
+template <int BS, int D, bool BF16 = false, bool LO = true, bool SMASK = false>
 __device__ __forceinline__ void score_block(const half8 (&kf)[BS / 16][D / 32], const half8 (&qf)[D / 32],
                                             int key0, bool causal, bool col_mask, bool col_on, int lo, int lim,
                                             float scale_log2, float &m_run, float &l_run,
-                                            float &alpha, half4 (&pf)[BS / 16], int q4) {
+                                            float &alpha, half4 (&pf)[BS / 16], int q4, uint64_t on_lanes = 0) {
     float4v s[BS / 16];
     qk_tile<BS, D, BF16>(kf, qf, s);
-    softmax_tile<BS / 16, BF16, LO>(s, key0, causal, col_mask, col_on, lo, lim, scale_log2, m_run, l_run, alpha, pf,
-                                    q4);
+    softmax_tile<BS / 16, BF16, LO, SMASK>(s, key0, causal, col_mask, col_on, lo, lim, scale_log2, m_run, l_run,
+                                           alpha, pf, q4, on_lanes);
 }
 
 // O^T = alpha * O^T + V^T * P^T over 32-key chunks.  acc[c][hh] holds O^T rows
