@@ -98,7 +98,10 @@ template <int NT, int KT, bool BF16>
 __device__ __forceinline__ void softmax_open_tiles(const float4v (&s)[NT][KT], float scale_log2, float (&m_run)[NT],
                                                    float (&l_run)[NT], float (&alpha)[NT], half4 (&pf)[NT][KT]) {
     float x[NT][KT][4];
-    bool raise = false;
+    // Ballots of plain compares, ORed on the scalar unit (one ballot of a
+    // combined condition makes the compiler move it through a vector
+    // register and back).
+    uint64_t raise = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         float xmax = -INFINITY;
@@ -108,9 +111,9 @@ __device__ __forceinline__ void softmax_open_tiles(const float4v (&s)[NT][KT], f
             for (int i = 0; i < 4; ++i) x[nt][kt][i] = __builtin_fmaf(s[nt][kt][i], scale_log2, -m_run[nt]);
             xmax = fmaxf(xmax, fmaxf(fmaxf(x[nt][kt][0], x[nt][kt][1]), fmaxf(x[nt][kt][2], x[nt][kt][3])));
         }
-        raise = raise || xmax > kLazyMax || m_run[nt] == -INFINITY;
+        raise |= __builtin_amdgcn_ballot_w64(xmax > kLazyMax) | __builtin_amdgcn_ballot_w64(m_run[nt] == -INFINITY);
     }
-    if (!__builtin_amdgcn_ballot_w64(raise)) {
+    if (!raise) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             float part[KT];
