@@ -303,7 +303,8 @@ __device__ __forceinline__ void dq_slot(const Params &p, const DqArgs &x, int ws
 }
 
 // Two wavefronts per SIMD even with two tiles per wavefront: the compiler then
-// spills about 23 VGPRs of the two-tile kernel (D = 128), which measured 10%
+// spills a few VGPRs of the two-tile kernel (D = 128; written before the
+// block loop and reloaded after it, never inside it), which measured 10%
 // faster over the whole backward than one tile per wavefront (189 VGPRs) and
 // than two tiles at one wavefront per SIMD (274 VGPRs).
 template <int BS, int SPLIT, int D, int PACK, int MODE>
